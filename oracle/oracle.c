@@ -1,0 +1,308 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.  Plain, slow, obviously-correct CPU
+ * reference for the block-quantized weight x bf16 activation product.
+ *
+ * Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may load
+ * this library.  The GPU library never links, includes or calls it, and it
+ * shares no header, table or helper with the GPU library.
+ *
+ * What it computes (all dequantized weights are fp32, all dot products fp64):
+ *
+ *   w[r,k]     = DEQ_fmt(packed, r, k)                 -- one fp32 value, exact rules below
+ *   y[m,n]     = sum_k (double)w[e*N+n, k] * (double)x[m,k]   (k ascending)
+ *   bound[m,n] = sum_k |(double)w[e*N+n, k] * (double)x[m,k]|
+ *   e          = ids[m] (or 0 when ids is NULL): row block e of the stacked
+ *                weight[E*N, K] tensor.
+ *
+ * Sources (the web pages the method is described on):
+ *  - Fused dequant-matvec: each packed block is read and dequantized, then
+ *    dotted with the activation; the dequantized weight never needs to exist
+ *    in memory ("A 320B MoE on a free Kaggle TPU", section "The kernel, and why
+ *    64 tok/s is not a bandwidth number").
+ *  - Block byte sizes: Q8_0 = 34 B and Q6_K = 210 B (they pad to 9 and 53 i32
+ *    words) -- vllm.cpp issue #3030 "BACKEND-TENSTORRENT-KEEPQUANT", issue body,
+ *    residency budget paragraph.
+ *  - Stacked experts weight[E*N, K], E = 1 being the dense case -- same issue,
+ *    sections "Second falsification" and issue-body scope item 2.
+ *  - NVFP4: E2M1 values with block scales and a per-site weight divisor/scale
+ *    -- "I Built a Custom Blackwell Kernel for Qwen3.8-27B", section "What the
+ *    custom path actually does".
+ *
+ * The pages fix the byte sizes but not the bit layout inside a block.  The
+ * reading taken here is the GGUF convention (the pages gate the K-quants
+ * against llama.cpp's dequantizer).  Parity with real GGUF files is
+ * UNPINNED (no GGUF bytes, gguf-py or llama.cpp are available); the layout is
+ * pinned only by encoder round trips written independently in the tests.
+ *
+ * Exactness: every DEQ below is evaluated in fp64, where it is exact (the
+ * operands carry at most 30 significant bits in total), and then rounded once
+ * to fp32 (round to nearest even, the C default).  Q8_0 and Q6_K products are
+ * already exact in fp32; Q4_K and NVFP4 round exactly once.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_Q8_0 = 1, ORC_Q4_K = 2, ORC_Q6_K = 3, ORC_NVFP4 = 4 };
+
+/* ---------- scalar decoders written from the number-format definitions ---------- */
+
+/* IEEE 754 binary16: sign, 5-bit exponent (bias 15), 10-bit fraction; subnormals honoured. */
+static double orc_fp16(uint16_t h) {
+    int s = h >> 15, e = (h >> 10) & 31, f = h & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)f, -24);
+    else if (e == 31) v = f ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + f), e - 25);
+    return s ? -v : v;
+}
+
+/* bfloat16: the top 16 bits of an IEEE binary32. */
+static double orc_bf16(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* FP8 E4M3 ("fn" variant): sign, 4-bit exponent (bias 7), 3-bit mantissa,
+ * subnormals m/8 * 2^-6, no infinities, S.1111.111 is NaN, max 448. */
+static double orc_e4m3(uint8_t b) {
+    int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);
+    else v = ldexp((double)(8 + m), e - 10);
+    return s ? -v : v;
+}
+
+/* FP4 E2M1: sign, 2-bit exponent (bias 1), 1-bit mantissa; exponent 0 is
+ * subnormal (m * 0.5).  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+static double orc_e2m1(unsigned c) {
+    int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+static uint16_t orc_le16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* ---------- sizes ---------- */
+
+long long orc_block_values(int fmt) {
+    switch (fmt) {
+    case ORC_Q8_0: return 32;
+    case ORC_Q4_K: return 256;
+    case ORC_Q6_K: return 256;
+    case ORC_NVFP4: return 16;
+    default: return 0;
+    }
+}
+
+/* Q8_0: fp16 d + 32 int8 = 34 B.  Q4_K: fp16 d + fp16 dmin + 12 scale bytes +
+ * 128 nibble bytes = 144 B.  Q6_K: 128 low-nibble bytes + 64 high-bit bytes +
+ * 16 int8 sub-scales + fp16 d = 210 B.  NVFP4: 8 code bytes + 1 E4M3 scale
+ * byte per 16 values (the 4-byte fp32 tensor scale is counted per tensor). */
+long long orc_block_bytes(int fmt) {
+    switch (fmt) {
+    case ORC_Q8_0: return 34;
+    case ORC_Q4_K: return 144;
+    case ORC_Q6_K: return 210;
+    case ORC_NVFP4: return 9;
+    default: return 0;
+    }
+}
+
+/* Bytes of a packed weight[E*N, K] tensor; 0 for a bad tag or K not a multiple of the block. */
+long long orc_packed_bytes(int fmt, long long E, long long N, long long K) {
+    long long qk = orc_block_values(fmt);
+    if (qk == 0 || E < 0 || N < 0 || K < 0 || K % qk) return 0;
+    long long rows = E * N, blocks = rows * (K / qk);
+    if (fmt == ORC_NVFP4) return blocks * 9 + 4 * E;
+    return blocks * orc_block_bytes(fmt);
+}
+
+/* ---------- dequantization of one packed row ---------- */
+
+/* Q8_0 block: bytes [0,2) d (fp16), bytes [2,34) q[0..31] (int8).  w_i = d * q_i. */
+static void orc_deq_q8_0(const uint8_t* blk, float* out) {
+    double d = orc_fp16(orc_le16(blk));
+    for (int i = 0; i < 32; ++i) out[i] = (float)(d * (double)(int8_t)blk[2 + i]);
+}
+
+/* Q4_K super-block of 256 values in 8 sub-blocks of 32:
+ *   [0,2) d fp16, [2,4) dmin fp16, [4,16) S[0..11] packed 6-bit scales/mins,
+ *   [16,144) Q[0..127] nibbles.
+ * Sub-block j: scale sc_j and min m_j (6 bits each):
+ *   j < 4 : sc_j = S[j] & 63,                       m_j = S[j+4] & 63
+ *   j >= 4: sc_j = (S[j+4] & 15) | ((S[j-4] >> 6) << 4),
+ *           m_j  = (S[j+4] >> 4) | ((S[j]   >> 6) << 4)
+ * Value 64g+l (g in 0..3, l in 0..31) is the low nibble of Q[32g+l]; value
+ * 64g+32+l is the high nibble of the same byte.
+ * w = d*sc_j*q - dmin*m_j, rounded once to fp32. */
+static void orc_deq_q4_k(const uint8_t* blk, float* out) {
+    double d = orc_fp16(orc_le16(blk)), dmin = orc_fp16(orc_le16(blk + 2));
+    const uint8_t* S = blk + 4;
+    const uint8_t* Q = blk + 16;
+    for (int j = 0; j < 8; ++j) {
+        int sc, m;
+        if (j < 4) {
+            sc = S[j] & 63;
+            m = S[j + 4] & 63;
+        } else {
+            sc = (S[j + 4] & 15) | ((S[j - 4] >> 6) << 4);
+            m = (S[j + 4] >> 4) | ((S[j] >> 6) << 4);
+        }
+        int g = j / 2, hi = j % 2;
+        for (int l = 0; l < 32; ++l) {
+            uint8_t byte = Q[32 * g + l];
+            int q = hi ? (byte >> 4) : (byte & 15);
+            out[32 * j + l] = (float)(d * sc * q - dmin * m);
+        }
+    }
+}
+
+/* Q6_K super-block of 256 values in 16 sub-blocks of 16:
+ *   [0,128) ql (low 4 bits), [128,192) qh (high 2 bits), [192,208) s[0..15]
+ *   int8 sub-scales, [208,210) d fp16.
+ * For half h in {0,1}, l in 0..31, L = ql + 64h, H = qh + 32h, base 128h:
+ *   q[base+l]    = (L[l]    & 15) | (((H[l] >> 0) & 3) << 4)
+ *   q[base+32+l] = (L[l+32] & 15) | (((H[l] >> 2) & 3) << 4)
+ *   q[base+64+l] = (L[l]    >> 4) | (((H[l] >> 4) & 3) << 4)
+ *   q[base+96+l] = (L[l+32] >> 4) | (((H[l] >> 6) & 3) << 4)
+ * Value v uses s[v/16].  w = d * s * (q - 32). */
+static void orc_deq_q6_k(const uint8_t* blk, float* out) {
+    const uint8_t* ql = blk;
+    const uint8_t* qh = blk + 128;
+    const int8_t* s = (const int8_t*)(blk + 192);
+    double d = orc_fp16(orc_le16(blk + 208));
+    for (int h = 0; h < 2; ++h) {
+        const uint8_t* L = ql + 64 * h;
+        const uint8_t* H = qh + 32 * h;
+        int base = 128 * h;
+        for (int l = 0; l < 32; ++l) {
+            int q[4];
+            q[0] = (L[l] & 15) | (((H[l] >> 0) & 3) << 4);
+            q[1] = (L[l + 32] & 15) | (((H[l] >> 2) & 3) << 4);
+            q[2] = (L[l] >> 4) | (((H[l] >> 4) & 3) << 4);
+            q[3] = (L[l + 32] >> 4) | (((H[l] >> 6) & 3) << 4);
+            for (int t = 0; t < 4; ++t) {
+                int v = base + 32 * t + l;
+                out[v] = (float)(d * (double)s[v / 16] * (double)(q[t] - 32));
+            }
+        }
+    }
+}
+
+/* NVFP4 tensor of R = E*N rows: three planes,
+ *   codes  [R][K/2]  : value k is the low nibble of byte k/2 when k is even, the high nibble when odd
+ *   scales [R][K/16] : one E4M3 scale per 16 consecutive values
+ *   gscale [E]       : one fp32 tensor scale per stacked matrix (little endian)
+ * w = (e2m1(c) * e4m3(s)) * g, rounded once to fp32 (the first product is exact). */
+static void orc_deq_nvfp4_row(const uint8_t* w, long long E, long long N, long long K, long long r, float* out) {
+    long long R = E * N;
+    const uint8_t* codes = w + r * (K / 2);
+    const uint8_t* scales = w + R * (K / 2) + r * (K / 16);
+    const uint8_t* gp = w + R * (K / 2) + R * (K / 16) + 4 * (r / N);
+    uint32_t gbits = (uint32_t)gp[0] | ((uint32_t)gp[1] << 8) | ((uint32_t)gp[2] << 16) | ((uint32_t)gp[3] << 24);
+    float gf;
+    memcpy(&gf, &gbits, 4);
+    double g = gf;
+    for (long long k = 0; k < K; ++k) {
+        unsigned c = (k & 1) ? (codes[k / 2] >> 4) : (codes[k / 2] & 15);
+        double s = orc_e4m3(scales[k / 16]);
+        out[k] = (float)(orc_e2m1(c) * s * g);
+    }
+}
+
+/* Dequantize global row r (0 <= r < E*N) of a packed weight[E*N, K] into out[K]. */
+static void orc_deq_row(int fmt, const uint8_t* w, long long E, long long N, long long K, long long r, float* out) {
+    long long qk = orc_block_values(fmt), bb = orc_block_bytes(fmt);
+    long long nb = K / qk;
+    if (fmt == ORC_NVFP4) {
+        orc_deq_nvfp4_row(w, E, N, K, r, out);
+        return;
+    }
+    const uint8_t* row = w + r * nb * bb;
+    for (long long b = 0; b < nb; ++b) {
+        const uint8_t* blk = row + b * bb;
+        float* o = out + b * qk;
+        if (fmt == ORC_Q8_0) orc_deq_q8_0(blk, o);
+        else if (fmt == ORC_Q4_K) orc_deq_q4_k(blk, o);
+        else orc_deq_q6_k(blk, o);
+    }
+}
+
+/* Dequantize rows [r0, r0+nr) of weight[E*N, K] into out[nr, K].  Returns 0, or -1 on bad arguments. */
+int orc_dequant_rows(int fmt, const uint8_t* w, long long E, long long N, long long K, long long r0, long long nr,
+                     float* out) {
+    long long qk = orc_block_values(fmt);
+    if (qk == 0 || E < 0 || N < 0 || K < 0 || K % qk) return -1;
+    if (r0 < 0 || nr < 0 || r0 + nr > E * N) return -1;
+    for (long long i = 0; i < nr; ++i) orc_deq_row(fmt, w, E, N, K, r0 + i, out + i * K);
+    return 0;
+}
+
+/* ---------- the product ---------- */
+
+/* y[m, j] and bound[m, j] for output column n = cols[j] (cols == NULL: j = n over all N).
+ * x is bf16 [M, K] (raw 16-bit patterns); ids[m] selects the stacked matrix (NULL: 0).
+ * Rows whose id lies outside [0, E) get NaN in y and bound.  nthreads <= 0: all
+ * available threads.  The fp64 sums run over k in ascending order. */
+int orc_gemm(int fmt, const uint8_t* w, long long E, long long N, long long K, long long M, const uint16_t* x,
+             const int32_t* ids, long long ncols, const long long* cols, double* y, double* bound, int nthreads) {
+    if (orc_block_values(fmt) == 0 || E < 1 || N < 0 || K <= 0 || M < 0 || K % orc_block_values(fmt)) return -1;
+    if (!cols) ncols = N;
+    for (long long j = 0; j < ncols; ++j)
+        if (cols && (cols[j] < 0 || cols[j] >= N)) return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    /* one worker per output column; each dequantizes the rows it needs once per stacked matrix */
+#pragma omp parallel
+    {
+        float* wrow = (float*)malloc(sizeof(float) * (size_t)K);
+#pragma omp for schedule(dynamic, 16)
+        for (long long j = 0; j < ncols; ++j) {
+            long long n = cols ? cols[j] : j;
+            long long have = -1;
+            for (long long m = 0; m < M; ++m) {
+                long long e = ids ? ids[m] : 0;
+                if (e < 0 || e >= E) {
+                    y[m * ncols + j] = NAN;
+                    bound[m * ncols + j] = NAN;
+                    continue;
+                }
+                if (e != have) {
+                    orc_deq_row(fmt, w, E, N, K, e * N + n, wrow);
+                    have = e;
+                }
+                const uint16_t* xm = x + m * K;
+                double s = 0.0, b = 0.0;
+                for (long long k = 0; k < K; ++k) {
+                    double p = (double)wrow[k] * orc_bf16(xm[k]);
+                    s += p;
+                    b += fabs(p);
+                }
+                y[m * ncols + j] = s;
+                bound[m * ncols + j] = b;
+            }
+        }
+        free(wrow);
+    }
+    return 0;
+}
+
+/* Threads orc_gemm would use with nthreads <= 0. */
+int orc_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
