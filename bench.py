@@ -1,0 +1,269 @@
+#!/usr/bin/env python
+"""Weight-stream benchmark of the block-quantized decode GEMV on one MI355X.
+
+Default workload: Q4_K fused gate+up decode GEMV of Qwen3.8-27B's MLP
+(M = 1, N = 2 x 17,408, K = 5,120; 100,270,080 packed weight bytes per call),
+synthetic seeded weights and activations already resident in HBM.  A step is one
+call of the hot path (quant_gemv).  The weights are rotated over enough distinct
+copies (>= 1 GiB in total) that every call streams from HBM, not from the
+256 MB Infinity Cache.
+
+Printed: one JSON line with the weight-stream rate (GB/s of packed weight bytes),
+the kernel's roofline position against MI355X's 8 TB/s HBM peak, and the CPU
+oracle timed on a bounded sample of the same workload.  --all adds every
+workload shape (the parity configurations) as a "sweep" list.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+TOKEN_BYTES_GB = 16.39         # per-token weight read of the 27B Q4_K_M artifact, embedding gather excluded
+ROTATE_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Workload:
+    def __init__(self, name, fmt, N, K, M, seed, E=1, moe=None):
+        self.name, self.fmt, self.N, self.K, self.M, self.seed, self.E = name, fmt, N, K, M, seed, E
+        self.moe = moe  # (tokens, topk) for the grouped workload
+
+
+def workloads():
+    import gemm_block_quant_amd as qg
+    return {
+        "q8_0_1024": Workload("Q8_0 GEMV 1024x1024", qg.Q8_0, 1024, 1024, 1, 1),
+        "q4k_gateup": Workload("Q4_K fused gate+up GEMV, N=34816 K=5120", qg.Q4_K, 2 * 17408, 5120, 1, 2),
+        "q6k_down_m1": Workload("Q6_K down-proj, N=5120 K=17408", qg.Q6_K, 5120, 17408, 1, 3),
+        "q6k_down_m8": Workload("Q6_K down-proj, N=5120 K=17408", qg.Q6_K, 5120, 17408, 8, 3),
+        "q6k_head_m1": Workload("Q6_K LM head, N=248320 K=5120", qg.Q6_K, 248320, 5120, 1, 3),
+        "q6k_head_m8": Workload("Q6_K LM head, N=248320 K=5120", qg.Q6_K, 248320, 5120, 8, 3),
+        "nvfp4_up_m1": Workload("NVFP4 MLP, N=17408 K=5120", qg.NVFP4, 17408, 5120, 1, 4),
+        "nvfp4_up_m8": Workload("NVFP4 MLP, N=17408 K=5120", qg.NVFP4, 17408, 5120, 8, 4),
+        "nvfp4_up_m512": Workload("NVFP4 MLP prefill, N=17408 K=5120", qg.NVFP4, 17408, 5120, 512, 4),
+        "nvfp4_down_m1": Workload("NVFP4 MLP, N=5120 K=17408", qg.NVFP4, 5120, 17408, 1, 4),
+        "nvfp4_down_m8": Workload("NVFP4 MLP, N=5120 K=17408", qg.NVFP4, 5120, 17408, 8, 4),
+        "nvfp4_down_m512": Workload("NVFP4 MLP prefill, N=5120 K=17408", qg.NVFP4, 5120, 17408, 512, 4),
+        "moe_gate": Workload("Q4_K grouped experts gate, E=288 N=2048 K=4096", qg.Q4_K, 2048, 4096, 128, 5, E=288,
+                             moe=(16, 8)),
+        "moe_down": Workload("Q4_K grouped experts down, E=288 N=4096 K=2048", qg.Q4_K, 4096, 2048, 128, 5, E=288,
+                             moe=(16, 8)),
+    }
+
+
+class Prepared:
+    """Device buffers and a raw launcher for one workload."""
+
+    def __init__(self, wl: Workload, rotate: bool = True):
+        import torch
+
+        import gemm_block_quant_amd as qg
+        import synth
+        self.wl = wl
+        tid_w = 0 if wl.moe is None or wl.K == 4096 else 4
+        t0 = time.time()
+        self.w_host = synth.weights(wl.fmt, synth.rng(wl.seed, tid_w), wl.E * wl.N, wl.K, E=wl.E)
+        self.x_host = synth.x_bf16(synth.rng(wl.seed, 1 if wl.moe is None or wl.K == 4096 else 3), wl.M, wl.K)
+        self.ids_host = synth.routing(synth.rng(wl.seed, 2), wl.moe[0], wl.moe[1], wl.E) if wl.moe else None
+        self.wbytes_total = qg.quant_packed_bytes(wl.fmt, wl.E, wl.N, wl.K)
+        log("[bench] %s: generated %.1f MB in %.1f s" % (wl.name, self.wbytes_total / 1e6, time.time() - t0))
+        w0 = torch.from_numpy(self.w_host).cuda()
+        if wl.moe is None:
+            self.copies = max(1, -(-ROTATE_BYTES // self.wbytes_total)) if rotate else 1
+            self.w = [w0] + [w0.clone() for _ in range(self.copies - 1)]
+            self.bytes_per_call = self.wbytes_total
+            self.distinct = 1
+        else:
+            self.copies = 1
+            self.w = [w0]
+            self.distinct = len(np.unique(self.ids_host))
+            self.bytes_per_call = self.distinct * qg.quant_packed_bytes(wl.fmt, 1, wl.N, wl.K)
+        self.x = torch.from_numpy(self.x_host.view(np.int16)).cuda()
+        self.y = torch.empty((wl.M, wl.N), dtype=torch.float32, device="cuda")
+        self.ids = torch.from_numpy(self.ids_host).cuda() if self.ids_host is not None else None
+        self.ws = None
+        L = qg.lib()
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        xp, yp = ctypes.c_void_p(self.x.data_ptr()), ctypes.c_void_p(self.y.data_ptr())
+        wps = [ctypes.c_void_p(t.data_ptr()) for t in self.w]
+        fmt, N, K, M, E = wl.fmt, wl.N, wl.K, wl.M, wl.E
+        if wl.moe is not None:
+            wsb = qg.quant_grouped_workspace_bytes(E, M)
+            self.ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+            ip, wsp = ctypes.c_void_p(self.ids.data_ptr()), ctypes.c_void_p(self.ws.data_ptr())
+            fn = L.quant_grouped_gemm
+            self.calls = [lambda wp=wp: fn(wp, fmt, E, N, K, M, xp, ip, yp, wsp, wsb, self.stream) for wp in wps]
+        elif M == 1:
+            fn = L.quant_gemv
+            self.calls = [lambda wp=wp: fn(wp, fmt, N, K, xp, yp, self.stream) for wp in wps]
+        else:
+            fn = L.quant_gemm
+            self.calls = [lambda wp=wp: fn(wp, fmt, N, K, M, xp, yp, self.stream) for wp in wps]
+
+    def call(self, i):
+        st = self.calls[i % len(self.calls)]()
+        if st != 0:
+            import gemm_block_quant_amd as qg
+            raise qg.QuantGemmError(st, "bench launch")
+
+
+def time_workload(p: Prepared, steps: int, warmup: int):
+    """(seconds for `steps` calls, mean per-launch kernel seconds from events around each launch)."""
+    import torch
+    for i in range(warmup):
+        p.call(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(steps):
+        ev[i][0].record()
+        p.call(i)
+        ev[i][1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    total = t_start.elapsed_time(t_end) / 1e3
+    per = [a.elapsed_time(b) / 1e3 for a, b in ev]
+    return total, float(np.mean(per)), float(np.median(per))
+
+
+def cpu_baseline(p: Prepared, target_s: float = 12.0):
+    """The oracle (as it stands) on a bounded sample of output rows of the same workload."""
+    import oracle
+    wl = p.wl
+    nthreads = oracle.max_threads()
+    rows_try = 64
+    while True:
+        cols = np.arange(min(rows_try, wl.N))
+        t0 = time.time()
+        oracle.gemm(wl.fmt, p.w_host, wl.N, wl.K, p.x_host, E=wl.E, cols=cols,
+                    ids=p.ids_host if wl.moe else None)
+        dt = time.time() - t0
+        if dt >= target_s or rows_try >= wl.N:
+            break
+        rows_try = int(min(wl.N, max(rows_try * 2, rows_try * target_s / max(dt, 1e-3) * 1.05)))
+    import gemm_block_quant_amd as qg
+    if wl.moe:
+        sample_bytes = len(cols) * wl.M * qg.quant_packed_bytes(wl.fmt, 1, 1, wl.K)
+    else:
+        sample_bytes = len(cols) * qg.quant_packed_bytes(wl.fmt, 1, 1, wl.K)
+    return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": "%d of %d output rows x M=%d (%.1f MB of packed weights) in %.2f s, %d threads"
+                      % (len(cols), wl.N, wl.M, sample_bytes / 1e6, dt, nthreads)}
+
+
+def result_for(p: Prepared, steps: int, warmup: int):
+    total, per_mean, per_med = time_workload(p, steps, warmup)
+    wl = p.wl
+    gbs = p.bytes_per_call * steps / total / 1e9
+    kern_gbs = p.bytes_per_call / per_mean / 1e9
+    r = {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "E": wl.E,
+         "weight_bytes_per_call": p.bytes_per_call, "rotated_copies": p.copies,
+         "ms_per_call": round(total / steps * 1e3, 5), "kernel_ms_mean": round(per_mean * 1e3, 5),
+         "kernel_ms_median": round(per_med * 1e3, 5),
+         "weight_GBps": round(gbs, 1), "kernel_weight_GBps": round(kern_gbs, 1),
+         "pct_hbm_peak": round(100 * kern_gbs / HBM_PEAK_GBS, 2),
+         "implied_tok_s": round(wl.M * gbs / TOKEN_BYTES_GB, 1)}
+    if wl.moe:
+        r["distinct_experts"] = p.distinct
+    if wl.M >= 32:
+        flops = 2.0 * wl.M * wl.N * wl.K
+        r["TFLOPs"] = round(flops / per_mean / 1e12, 1)
+        r["pct_bf16_mfma_peak"] = round(100 * flops / per_mean / 1e12 / BF16_MFMA_PEAK_TFLOPS, 2)
+    return r, total, per_mean
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="q4k_gateup")
+    ap.add_argument("--all", action="store_true", help="also time every workload shape (sweep)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--sweep-out", default=None, help="write the sweep as JSON lines to this file")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gemm_block_quant_amd as qg
+    qg.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wls = workloads()
+    wl = wls[args.workload]
+    p = Prepared(wl)
+    torch.cuda.synchronize()
+    r, total, per_mean = result_for(p, args.steps, args.warmup)
+    log("[bench] %s" % json.dumps(r))
+    sweep = []
+    if args.all:
+        for key, w2 in wls.items():
+            if key == args.workload:
+                sweep.append(r)
+                continue
+            try:
+                p2 = Prepared(w2)
+                steps = max(10, min(args.steps, int(2.0 / max(1e-6, p2.bytes_per_call / 5e12))))
+                r2, _, _ = result_for(p2, steps, min(args.warmup, steps))
+            except Exception as e:  # a workload the build cannot run yet is reported, not fatal
+                r2 = {"workload": w2.name, "M": w2.M, "error": str(e)}
+            log("[bench] %s" % json.dumps(r2))
+            sweep.append(r2)
+            del p2
+            torch.cuda.empty_cache()
+        if args.sweep_out:
+            with open(args.sweep_out, "w") as f:
+                for s in sweep:
+                    f.write(json.dumps(s) + "\n")
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(p)
+        log("[bench] cpu baseline %s" % json.dumps(cpu))
+    value = p.bytes_per_call * args.steps / total / 1e9
+    achieved = p.bytes_per_call / per_mean / 1e9
+    out = {
+        "metric": "weight-stream HBM GB/s and % of MI355X peak for quantized decode GEMV (M=1,8)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "format": "Q4_K" if wl.fmt == qg.Q4_K else str(wl.fmt), "M": wl.M,
+                   "N": wl.N, "K": wl.K, "weight_bytes": p.bytes_per_call, "rotated_copies": p.copies,
+                   "implied_tok_s": r["implied_tok_s"], "pct_hbm_peak_whole_job": round(100 * value / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    if sweep:
+        out["sweep"] = sweep
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+"""Python binding of libquantgemm (MI355X / gfx950 block-quantized GEMV and GEMM).
+
+Argument marshalling only: every step of the product runs in the library's HIP
+kernels.  Tensors are torch tensors on the ROCm device; torch provides device
+memory and the current stream, nothing else.  The entry points mirror the C ABI
+in include/quantgemm.h:
+
+    quant_gemv(w, fmt, N, K, x, y=None)                     -> y [N] fp32
+    quant_gemm(w, fmt, N, K, M, x, y=None)                  -> y [M, N] fp32
+    quant_grouped_gemm(w, fmt, E, N, K, M, x, ids, y=None, workspace=None) -> y [M, N]
+    quant_dequantize(w, fmt, rows, K, out=None)             -> out [rows, K] fp32
+    quant_dequantize_stacked(w, fmt, E, N, K, out=None)     -> out [E*N, K] fp32
+    quant_packed_bytes(fmt, E, N, K), quant_grouped_workspace_bytes(E, M),
+    quant_block_values(fmt), quant_status_string(status)
+
+w is a uint8 tensor holding the packed bytes; x holds bf16 activations
+(torch.bfloat16, or int16/uint16 bit patterns).  A missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+Q8_0, Q4_K, Q6_K, NVFP4 = 1, 2, 3, 4
+FORMATS = {"Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K, "NVFP4": NVFP4}
+
+QG_OK, QG_EINVAL, QG_EFORMAT, QG_EALIGN, QG_ESHAPE, QG_EHIP, QG_ENOTIMPL, QG_EWORKSPACE = range(8)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libquantgemm.so")
+
+_lib = None
+
+
+class QuantGemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, quant_status_string(status), status))
+
+
+def lib():
+    """The loaded libquantgemm.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libquantgemm.so is not built (%s); run `python -m gemm_block_quant_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    L.quant_block_values.argtypes = [i32]
+    L.quant_block_values.restype = i64
+    L.quant_packed_bytes.argtypes = [i32, i64, i64, i64]
+    L.quant_packed_bytes.restype = sz
+    L.quant_gemv.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+    L.quant_gemv.restype = i32
+    L.quant_gemm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
+    L.quant_gemm.restype = i32
+    L.quant_grouped_workspace_bytes.argtypes = [i64, i64]
+    L.quant_grouped_workspace_bytes.restype = sz
+    L.quant_grouped_gemm.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+    L.quant_grouped_gemm.restype = i32
+    L.quant_dequantize.argtypes = [vp, i32, i64, i64, vp, vp]
+    L.quant_dequantize.restype = i32
+    L.quant_dequantize_stacked.argtypes = [vp, i32, i64, i64, i64, vp, vp]
+    L.quant_dequantize_stacked.restype = i32
+    L.quant_status_string.argtypes = [i32]
+    L.quant_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------- host-only queries
+
+def quant_block_values(fmt: int) -> int:
+    return int(lib().quant_block_values(fmt))
+
+
+def quant_packed_bytes(fmt: int, E: int, N: int, K: int) -> int:
+    return int(lib().quant_packed_bytes(fmt, E, N, K))
+
+
+def quant_grouped_workspace_bytes(E: int, M: int) -> int:
+    return int(lib().quant_grouped_workspace_bytes(E, M))
+
+
+def quant_status_string(status: int) -> str:
+    return lib().quant_status_string(status).decode()
+
+
+# ---------------------------------------------------------------- marshalling helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t, name, nbytes=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s holds %d bytes, needs %d" % (name, t.numel() * t.element_size(), nbytes))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _x_ptr(x, M, K):
+    torch = _torch()
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("x must be bfloat16 (or 16-bit bf16 bit patterns)")
+    return _dev_ptr(x, "x", 2 * M * K)
+
+
+def _out(y, shape, device):
+    torch = _torch()
+    if y is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if y.dtype != torch.float32:
+        raise ValueError("y must be float32")
+    return y
+
+
+def _check(status, where):
+    if status != QG_OK:
+        raise QuantGemmError(status, where)
+
+
+# ---------------------------------------------------------------- products
+
+def quant_gemm(w, fmt: int, N: int, K: int, M: int, x, y=None, stream=None):
+    """y[m, n] = sum_k W[n, k] x[m, k]; W packed [N, K] in w, x bf16 [M, K]."""
+    y = _out(y, (M, N), x.device)
+    st = lib().quant_gemm(_dev_ptr(w, "w", quant_packed_bytes(fmt, 1, N, K)), fmt, N, K, M, _x_ptr(x, M, K),
+                          _dev_ptr(y, "y", 4 * M * N), _stream(stream))
+    _check(st, "quant_gemm")
+    return y
+
+
+def quant_gemv(w, fmt: int, N: int, K: int, x, y=None, stream=None):
+    """y[n] = sum_k W[n, k] x[k]; W packed [N, K] in w, x bf16 [K]."""
+    y = _out(y, (N,), x.device)
+    st = lib().quant_gemv(_dev_ptr(w, "w", quant_packed_bytes(fmt, 1, N, K)), fmt, N, K, _x_ptr(x, 1, K),
+                          _dev_ptr(y, "y", 4 * N), _stream(stream))
+    _check(st, "quant_gemv")
+    return y
+
+
+def quant_grouped_gemm(w, fmt: int, E: int, N: int, K: int, M: int, x, ids=None, y=None, workspace=None,
+                       stream=None):
+    """y[i, n] = sum_k W_{ids[i]}[n, k] x[i, k] over stacked weight[E*N, K]; ids int32 [M] or None."""
+    torch = _torch()
+    y = _out(y, (M, N), x.device)
+    wsb = quant_grouped_workspace_bytes(E, M)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=x.device)
+    if ids is not None and ids.dtype != torch.int32:
+        raise ValueError("ids must be int32")
+    st = lib().quant_grouped_gemm(_dev_ptr(w, "w", quant_packed_bytes(fmt, E, N, K)), fmt, E, N, K, M,
+                                  _x_ptr(x, M, K), _dev_ptr(ids, "ids", 4 * M) if ids is not None else None,
+                                  _dev_ptr(y, "y", 4 * M * N), _dev_ptr(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "quant_grouped_gemm")
+    return y
+
+
+def quant_dequantize(w, fmt: int, rows: int, K: int, out=None, stream=None):
+    """fp32 [rows, K] dequantization of a packed weight[rows, K] (bit-exact)."""
+    out = _out(out, (rows, K), w.device)
+    st = lib().quant_dequantize(_dev_ptr(w, "w", quant_packed_bytes(fmt, 1, rows, K)), fmt, rows, K,
+                                _dev_ptr(out, "out", 4 * rows * K), _stream(stream))
+    _check(st, "quant_dequantize")
+    return out
+
+
+def quant_dequantize_stacked(w, fmt: int, E: int, N: int, K: int, out=None, stream=None):
+    """fp32 [E*N, K] dequantization of a stacked weight[E*N, K] (bit-exact)."""
+    out = _out(out, (E * N, K), w.device)
+    st = lib().quant_dequantize_stacked(_dev_ptr(w, "w", quant_packed_bytes(fmt, E, N, K)), fmt, E, N, K,
+                                        _dev_ptr(out, "out", 4 * E * N * K), _stream(stream))
+    _check(st, "quant_dequantize_stacked")
+    return out

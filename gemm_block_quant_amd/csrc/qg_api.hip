@@ -1,0 +1,162 @@
+// qg_api.hip -- the C ABI of libquantgemm: host-side validation and dispatch.
+// Nothing here allocates device memory or synchronizes a stream.
+#include <limits.h>
+
+#include "qg_internal.h"
+
+using namespace qg;
+
+namespace {
+
+int64_t block_values(int fmt) {
+    switch (fmt) {
+        case QG_Q8_0: return 32;
+        case QG_Q4_K: return 256;
+        case QG_Q6_K: return 256;
+        case QG_NVFP4: return 16;
+        default: return 0;
+    }
+}
+
+int64_t block_bytes(int fmt) {
+    switch (fmt) {
+        case QG_Q8_0: return 34;
+        case QG_Q4_K: return 144;
+        case QG_Q6_K: return 210;
+        default: return 0;
+    }
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Shape checks common to every product entry point.
+qg_status check_shape(int fmt, int64_t E, int64_t N, int64_t K, int64_t M) {
+    if (block_values(fmt) == 0) return QG_EFORMAT;
+    if (E < 1 || N < 0 || M < 0 || K <= 0 || K % block_values(fmt)) return QG_ESHAPE;
+    if (N > INT_MAX / 2 || K > INT_MAX / 2 || M > INT_MAX / 2) return QG_ESHAPE;
+    if (E > 0 && N > 0 && E > (int64_t)INT_MAX / N) return QG_ESHAPE;
+    return QG_OK;
+}
+
+// Streaming-kernel arguments for matrix e of a stacked weight[E*N, K].
+StreamArgs stream_args(const void* w, int fmt, int64_t E, int64_t e, int64_t N, int64_t K) {
+    StreamArgs a = {};
+    const uint8_t* base = (const uint8_t*)w;
+    const int64_t R = E * N;
+    if (fmt == QG_NVFP4) {
+        a.rb0 = K / 2;
+        a.rb1 = K / 16;
+        a.w0 = base + e * N * a.rb0;
+        a.w1 = base + R * a.rb0 + e * N * a.rb1;
+        a.gbytes = base + R * a.rb0 + R * a.rb1 + 4 * e;
+    } else {
+        a.rb0 = (K / block_values(fmt)) * block_bytes(fmt);
+        a.w0 = base + e * N * a.rb0;
+    }
+    a.N = (int)N;
+    a.K = (int)K;
+    return a;
+}
+
+qg_status from_hip(hipError_t e) { return e == hipSuccess ? QG_OK : QG_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t quant_block_values(qg_format fmt) { return block_values(fmt); }
+
+size_t quant_packed_bytes(qg_format fmt, int64_t E, int64_t N, int64_t K) {
+    const int64_t qk = block_values(fmt);
+    if (qk == 0 || E < 0 || N < 0 || K < 0 || K % qk) return 0;
+    const int64_t rows = E * N, blocks = rows * (K / qk);
+    if (fmt == QG_NVFP4) return (size_t)(blocks * 9 + 4 * E);
+    return (size_t)(blocks * block_bytes(fmt));
+}
+
+const char* quant_status_string(qg_status s) {
+    switch (s) {
+        case QG_OK: return "ok";
+        case QG_EINVAL: return "null pointer argument";
+        case QG_EFORMAT: return "unknown weight format tag";
+        case QG_EALIGN: return "pointer not aligned as required (w, x, workspace: 16 bytes; y, ids: 4 bytes)";
+        case QG_ESHAPE: return "invalid shape: negative size, K not a positive multiple of the block, or a limit exceeded";
+        case QG_EHIP: return "HIP runtime error on launch";
+        case QG_ENOTIMPL: return "not implemented for this combination";
+        case QG_EWORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+qg_status quant_gemm(const void* w, qg_format fmt, int64_t N, int64_t K, int64_t M, const uint16_t* x, float* y,
+                     void* stream) {
+    qg_status s = check_shape(fmt, 1, N, K, M);
+    if (s != QG_OK) return s;
+    if (M == 0 || N == 0) return QG_OK;
+    if (!w || !x || !y) return QG_EINVAL;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
+    const int rows = stream_rows_per_pass(fmt, (int)K, (int)(M < 16 ? M : 16));
+    if (rows <= 0) return QG_ESHAPE;
+    StreamArgs a = stream_args(w, fmt, 1, 0, N, K);
+    a.x = x;
+    a.ldx = K;
+    a.y = y;
+    a.ldy = N;
+    for (int64_t m0 = 0; m0 < M; m0 += rows) {
+        const int cnt = (int)(M - m0 < rows ? M - m0 : rows);
+        a.M = cnt;
+        for (int i = 0; i < kMaxPassRows; ++i) {
+            a.xrow[i] = (int)(m0 + (i < cnt ? i : 0));
+            a.yrow[i] = a.xrow[i];
+        }
+        hipError_t e = launch_stream_gemm(fmt, a, (hipStream_t)stream);
+        if (e != hipSuccess) return QG_EHIP;
+    }
+    return QG_OK;
+}
+
+qg_status quant_gemv(const void* w, qg_format fmt, int64_t N, int64_t K, const uint16_t* x, float* y, void* stream) {
+    return quant_gemm(w, fmt, N, K, 1, x, y, stream);
+}
+
+size_t quant_grouped_workspace_bytes(int64_t E, int64_t M) {
+    if (E < 1 || M < 0) return 0;
+    return grouped_workspace_bytes(E, M);
+}
+
+qg_status quant_grouped_gemm(const void* w, qg_format fmt, int64_t E, int64_t N, int64_t K, int64_t M,
+                             const uint16_t* x, const int32_t* ids, float* y, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    qg_status s = check_shape(fmt, E, N, K, M);
+    if (s != QG_OK) return s;
+    if (M > kGroupedMaxRows) return QG_ESHAPE;
+    if (M == 0 || N == 0) return QG_OK;
+    if (!w || !x || !y) return QG_EINVAL;
+    if (!workspace || workspace_bytes < grouped_workspace_bytes(E, M)) return QG_EWORKSPACE;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(workspace, 16) ||
+        (ids && !aligned(ids, 4)))
+        return QG_EALIGN;
+    StreamArgs a = stream_args(w, fmt, E, 0, N, K);
+    a.x = x;
+    a.ldx = K;
+    a.y = y;
+    a.ldy = N;
+    const int64_t es0 = N * a.rb0, es1 = N * a.rb1;
+    return from_hip(launch_grouped(fmt, a, ids, E, M, (int32_t*)workspace, es0, es1, (hipStream_t)stream));
+}
+
+qg_status quant_dequantize_stacked(const void* w, qg_format fmt, int64_t E, int64_t N, int64_t K, float* out,
+                                   void* stream) {
+    qg_status s = check_shape(fmt, E, N, K, 0);
+    if (s != QG_OK) return s;
+    if (N == 0) return QG_OK;
+    if (!w || !out) return QG_EINVAL;
+    if (!aligned(w, 16) || !aligned(out, 4)) return QG_EALIGN;
+    return from_hip(launch_dequant(fmt, (const uint8_t*)w, E, N, K, out, (hipStream_t)stream));
+}
+
+qg_status quant_dequantize(const void* w, qg_format fmt, int64_t rows, int64_t K, float* out, void* stream) {
+    return quant_dequantize_stacked(w, fmt, 1, rows, K, out, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,282 @@
+// qg_grouped.hip -- grouped-expert product over a stacked weight[E*N, K]:
+//     y[i, :] = W_{ids[i]} x[i, :],  W_e = rows [e*N, (e+1)*N)
+// (the operator seam of vllm.cpp issue #3030 "BACKEND-TENSTORRENT-KEEPQUANT",
+// section "Second falsification": E = 1 is the dense case, E = N the stacked
+// expert tower).
+//
+// Rows are bucketed by expert on the device first, so that each DISTINCT
+// expert's weights stream from HBM once per call however many rows route to
+// it.  "A 320B MoE on a free Kaggle TPU" (section "The decode kernel's cost is
+// not distinct experts") shows a decode path that runs one grid step per
+// (token, expert) pair instead, re-reading and re-decoding an expert for every
+// pair that selects it; its prefill path sorts slots by expert, which is what
+// the bucketing kernel below does.
+//
+//  1. k_bucket (one workgroup): sort the keys (id << 32 | row) with a bitonic
+//     network in LDS (invalid ids sort last), mark where the id changes, scan,
+//     and write slot -> (expert, first sorted row) and the sorted row list.
+//     Rows whose id is outside [0, E) get NaN in every element of y.
+//  2. k_grouped: workgroup (slot, chunk) stages the slot's activation rows
+//     (16 at most per pass) in LDS and its 4 waves stream rows [chunk*RPC,
+//     ...) of the slot's expert through the same core as the dense product,
+//     writing y rows at the original row indices.  Workgroups whose slot is
+//     past the number of distinct experts exit at once.
+// The per-row arithmetic is the dense kernel's, so E = 1 with ids = NULL
+// reproduces quant_gemm bit for bit.
+#include "qg_stream.h"
+
+namespace qg {
+
+constexpr int kBucketThreads = 1024;
+
+// Workspace (int32): [0] slot count, [4 .. 4+S) slot expert, [4+S .. 5+2S)
+// slot start, then M sorted rows.  S = min(E, M).
+__host__ __device__ inline int64_t ws_slots(int64_t E, int64_t M) { return E < M ? E : M; }
+
+__global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __restrict__ ids, int E, int M, int P,
+                                                           int32_t* __restrict__ ws, float* __restrict__ y, int N,
+                                                           int64_t ldy) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
+    QG_LDS uint64_t* keys = (QG_LDS uint64_t*)smem_generic;                       // P keys
+    QG_LDS int32_t* part = (QG_LDS int32_t*)(smem_generic + (size_t)P * 8);      // kBucketThreads partial counts
+    const int tid = threadIdx.x;
+    const int64_t S = ws_slots(E, M);
+    int32_t* slot_expert = ws + 4;
+    int32_t* slot_start = ws + 4 + S;
+    int32_t* perm = ws + 5 + 2 * S;
+
+    for (int i = tid; i < P; i += kBucketThreads) {
+        uint64_t k = ~0ull;
+        if (i < M) {
+            const int id = ids ? ids[i] : 0;
+            const uint32_t hi = (id >= 0 && id < E) ? (uint32_t)id : 0x7fffffffu;
+            k = ((uint64_t)hi << 32) | (uint32_t)i;
+        }
+        keys[i] = k;
+    }
+    __syncthreads();
+    // bitonic sort, ascending
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < P / 2; i += kBucketThreads) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool up = (lo & size) == 0;
+                const uint64_t a = keys[lo], b = keys[hi];
+                if ((a > b) == up) {
+                    keys[lo] = b;
+                    keys[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // heads of runs of equal valid ids -> slots (block scan over contiguous chunks)
+    const int per = (M + kBucketThreads - 1) / kBucketThreads;
+    const int b0 = tid * per, b1 = min(M, b0 + per);
+    int cnt = 0;
+    for (int i = b0; i < b1; ++i) {
+        const uint32_t id = (uint32_t)(keys[i] >> 32);
+        const bool valid = id != 0x7fffffffu;
+        const bool head = valid && (i == 0 || (uint32_t)(keys[i - 1] >> 32) != id);
+        cnt += head;
+    }
+    part[tid] = cnt;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int t = 0; t < kBucketThreads; ++t) {
+            const int c = part[t];
+            part[t] = run;
+            run += c;
+        }
+        ws[0] = run;
+    }
+    __syncthreads();
+    int slot = part[tid];
+    for (int i = b0; i < b1; ++i) {
+        const uint64_t k = keys[i];
+        const uint32_t id = (uint32_t)(k >> 32);
+        const bool valid = id != 0x7fffffffu;
+        const bool head = valid && (i == 0 || (uint32_t)(keys[i - 1] >> 32) != id);
+        perm[i] = (int32_t)(uint32_t)k;
+        if (head) {
+            slot_expert[slot] = (int32_t)id;
+            slot_start[slot] = i;
+            ++slot;
+        }
+    }
+    if (tid == 0) {
+        // the last slot ends at the first invalid sorted position (or M)
+        int lo = 0, hi = M;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((uint32_t)(keys[mid] >> 32) == 0x7fffffffu) hi = mid;
+            else lo = mid + 1;
+        }
+        slot_start[ws[0]] = lo;
+    }
+    // NaN rows for ids outside [0, E)
+    for (int i = M - 1; i >= 0; --i) {
+        if ((uint32_t)(keys[i] >> 32) != 0x7fffffffu) break;
+        const int row = (int)(uint32_t)keys[i];
+        for (int n = tid; n < N; n += kBucketThreads) y[(int64_t)row * ldy + n] = __builtin_nanf("");
+    }
+}
+
+// Grouped streaming kernel.  MTMAX: activation rows per pass (LDS sized for it).
+template <int F, int MTMAX, int CPL, int CPLS, int PF>
+__global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32_t* __restrict__ ws, int64_t E,
+                                                 int64_t M, int rpc, int nchunks, int64_t estride0,
+                                                 int64_t estride1) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
+    lds_u8* smem = (lds_u8*)smem_generic;
+    constexpr bool kSums = (F == QG_Q4_K || F == QG_Q6_K);
+    const int K = a.K;
+    const int slot = blockIdx.x / nchunks, chunk = blockIdx.x % nchunks;
+    const int nslots = ws[0];
+    if (slot >= nslots) return;
+    const int64_t S = ws_slots(E, M);
+    const int e = ws[4 + slot];
+    const int r0 = ws[4 + S + slot], r1 = ws[4 + S + slot + 1];
+    const int32_t* perm = ws + 5 + 2 * S;
+
+    lds_u8* xl = smem;
+    lds_f32* xs = (lds_f32*)(smem + (size_t)MTMAX * K * 2);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    lds_u8* rowbuf = smem + rowbuf_offset(MTMAX, K) + (size_t)wid * rowbuf_bytes(CPL, CPLS);
+    lds_u8* rowbuf_s = rowbuf + CPL * 1024 + 32;
+
+    MatView mv;
+    mv.w0 = a.w0 + (size_t)e * estride0;
+    mv.rb0 = a.rb0;
+    mv.w1 = a.w1 ? a.w1 + (size_t)e * estride1 : nullptr;
+    mv.rb1 = a.rb1;
+    mv.gbytes = a.gbytes ? a.gbytes + 4 * (size_t)e : nullptr;
+    const int n_begin = chunk * rpc;
+    const int n_end = min(a.N, n_begin + rpc);
+
+    for (int p0 = r0; p0 < r1; p0 += MTMAX) {
+        const int cnt = min(MTMAX, r1 - p0);
+        if (p0 != r0) __syncthreads();  // every wave is done with the previous pass's activations
+        const int64_t yrow = perm[p0 + (lane < cnt ? lane : 0)];
+        auto row_of = [&](int m) { return perm[p0 + m]; };
+        if (cnt <= 1 || MTMAX == 1) {
+            stage_x<1, kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of);
+            wave_stream<F, 1, CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf, rowbuf_s, n_begin + wid,
+                                             kWavesPerBlock, n_end, a.y, a.ldy, yrow, cnt);
+        } else if (cnt <= 2 || MTMAX == 2) {
+            stage_x<(MTMAX < 2 ? MTMAX : 2), kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of);
+            wave_stream<F, (MTMAX < 2 ? MTMAX : 2), CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf,
+                                                                   rowbuf_s, n_begin + wid, kWavesPerBlock, n_end,
+                                                                   a.y, a.ldy, yrow, cnt);
+        } else if (cnt <= 4 || MTMAX == 4) {
+            stage_x<(MTMAX < 4 ? MTMAX : 4), kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of);
+            wave_stream<F, (MTMAX < 4 ? MTMAX : 4), CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf,
+                                                                   rowbuf_s, n_begin + wid, kWavesPerBlock, n_end,
+                                                                   a.y, a.ldy, yrow, cnt);
+        } else if (cnt <= 8 || MTMAX == 8) {
+            stage_x<(MTMAX < 8 ? MTMAX : 8), kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of);
+            wave_stream<F, (MTMAX < 8 ? MTMAX : 8), CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf,
+                                                                   rowbuf_s, n_begin + wid, kWavesPerBlock, n_end,
+                                                                   a.y, a.ldy, yrow, cnt);
+        } else {
+            stage_x<MTMAX, kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of);
+            wave_stream<F, MTMAX, CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf, rowbuf_s,
+                                                 n_begin + wid, kWavesPerBlock, n_end, a.y, a.ldy, yrow, cnt);
+        }
+    }
+}
+
+size_t grouped_workspace_bytes(int64_t E, int64_t M) {
+    const int64_t S = ws_slots(E, M);
+    const int64_t ints = 5 + 2 * S + M;
+    return (size_t)((ints * 4 + 15) / 16 * 16);
+}
+
+template <int F, int MTMAX, int CPL, int CPLS, int PF>
+static hipError_t launch_grouped_one(const StreamArgs& a, const int32_t* ws, int64_t E, int64_t M, int64_t estride0,
+                                     int64_t estride1, hipStream_t st) {
+    const size_t lds = gemv_lds_bytes(MTMAX, a.K, CPL, CPLS);
+    auto kern = k_grouped<F, MTMAX, CPL, CPLS, PF>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    // enough (slot, chunk) workgroups to fill the chip even when only a few slots are live
+    const int64_t S = ws_slots(E, M);
+    const int64_t target = (int64_t)num_cus() * 4;
+    int64_t nchunks = (target + S - 1) / S;
+    const int64_t max_chunks = (a.N + 63) / 64;  // at least 16 rows per wave
+    if (nchunks > max_chunks) nchunks = max_chunks;
+    if (nchunks < 1) nchunks = 1;
+    const int rpc = (int)((a.N + nchunks - 1) / nchunks);
+    nchunks = (a.N + rpc - 1) / rpc;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(S * nchunks)), dim3(256), lds, st, a, ws, E, M, rpc, (int)nchunks,
+                       estride0, estride1);
+    return hipGetLastError();
+}
+
+template <int F, int MTMAX>
+static hipError_t grouped_cpl(StreamArgs a, const int32_t* ws, int64_t E, int64_t M, int64_t es0, int64_t es1,
+                              hipStream_t st) {
+    const int cpl = choose_cpl(F, a.K);
+    a.seg_blocks = segment_blocks(F, a.K, cpl);
+    const int nb = a.K / BlockGeom<F>::QK;
+    a.nseg = (nb + a.seg_blocks - 1) / a.seg_blocks;
+    constexpr int S = (F == QG_NVFP4) ? 1 : 0;
+    switch (cpl) {
+        case 1: return launch_grouped_one<F, MTMAX, 1, S, 4>(a, ws, E, M, es0, es1, st);
+        case 2: return launch_grouped_one<F, MTMAX, 2, S, 4>(a, ws, E, M, es0, es1, st);
+        case 3: return launch_grouped_one<F, MTMAX, 3, S, 4>(a, ws, E, M, es0, es1, st);
+        case 4: return launch_grouped_one<F, MTMAX, 4, S, 3>(a, ws, E, M, es0, es1, st);
+        default: return launch_grouped_one<F, MTMAX, 6, S, 2>(a, ws, E, M, es0, es1, st);
+    }
+}
+
+template <int F>
+static hipError_t grouped_mt(const StreamArgs& a, int mtmax, const int32_t* ws, int64_t E, int64_t M, int64_t es0,
+                             int64_t es1, hipStream_t st) {
+    switch (mtmax) {
+        case 1: return grouped_cpl<F, 1>(a, ws, E, M, es0, es1, st);
+        case 2: return grouped_cpl<F, 2>(a, ws, E, M, es0, es1, st);
+        case 4: return grouped_cpl<F, 4>(a, ws, E, M, es0, es1, st);
+        case 8: return grouped_cpl<F, 8>(a, ws, E, M, es0, es1, st);
+        default: return grouped_cpl<F, 16>(a, ws, E, M, es0, es1, st);
+    }
+}
+
+hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int64_t E, int64_t M, int32_t* ws,
+                          int64_t estride0, int64_t estride1, hipStream_t st) {
+    // 1. bucketing
+    int P = 1;
+    while (P < M) P <<= 1;
+    const size_t lds = (size_t)P * 8 + kBucketThreads * 4;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_bucket, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBucketThreads), lds, st, ids, (int)E, (int)M, P, ws, a.y, a.N, a.ldy);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // 2. rows per pass: room for the expected rows per distinct expert (twice the
+    // mean, at least 1), as LDS allows
+    const int64_t S = ws_slots(E, M);
+    int64_t want = 2 * ((M + S - 1) / S);
+    int mtmax = want <= 1 ? 1 : want <= 2 ? 2 : want <= 4 ? 4 : want <= 8 ? 8 : 16;
+    const int cpl = choose_cpl(fmt, a.K);
+    while (mtmax > 1 && gemv_lds_bytes(mtmax, a.K, cpl, fmt == QG_NVFP4 ? 1 : 0) > (size_t)kLdsBytes) mtmax >>= 1;
+    switch (fmt) {
+        case QG_Q8_0: return grouped_mt<QG_Q8_0>(a, mtmax, ws, E, M, estride0, estride1, st);
+        case QG_Q4_K: return grouped_mt<QG_Q4_K>(a, mtmax, ws, E, M, estride0, estride1, st);
+        case QG_Q6_K: return grouped_mt<QG_Q6_K>(a, mtmax, ws, E, M, estride0, estride1, st);
+        default: return grouped_mt<QG_NVFP4>(a, mtmax, ws, E, M, estride0, estride1, st);
+    }
+}
+
+}  // namespace qg

@@ -1,0 +1,42 @@
+// qg_internal.h -- declarations shared by the kernel files and the C-ABI layer.
+#pragma once
+
+#include "../../include/quantgemm.h"
+#include "qg_common.h"
+
+namespace qg {
+
+constexpr int kMaxPassRows = 16;
+
+// One launch of the weight-streaming kernel: rows [0, N) of one weight matrix
+// times up to 16 activation rows.
+struct StreamArgs {
+    const uint8_t* w0;   // row 0 of the matrix: blocks (Q8_0/Q4_K/Q6_K) or E2M1 codes (NVFP4)
+    int64_t rb0;         // bytes per row in that plane
+    const uint8_t* w1;   // NVFP4: row 0 of the E4M3 scale plane
+    int64_t rb1;         // NVFP4: scale bytes per row
+    const uint8_t* gbytes;  // NVFP4: device address of the matrix's fp32 tensor scale (any alignment)
+    int N, K;
+    int seg_blocks, nseg;  // filled by the dispatcher
+    const uint16_t* x;   // activations (bf16 bits); row m of this pass is x + xrow[m] * ldx
+    int64_t ldx;
+    float* y;            // output; row m of this pass is y + yrow[m] * ldy
+    int64_t ldy;
+    int M;               // activation rows in this pass (1..16)
+    int xrow[kMaxPassRows];
+    int yrow[kMaxPassRows];
+};
+
+hipError_t launch_stream_gemm(int fmt, StreamArgs a, hipStream_t st);
+int stream_rows_per_pass(int fmt, int K, int M);
+
+// Grouped-expert product: bucketing + streaming over the distinct experts.
+constexpr int64_t kGroupedMaxRows = 16384;
+size_t grouped_workspace_bytes(int64_t E, int64_t M);
+hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int64_t E, int64_t M, int32_t* ws,
+                          int64_t estride0, int64_t estride1, hipStream_t st);
+
+// Dequantization of rows [0, rows) to fp32.
+hipError_t launch_dequant(int fmt, const uint8_t* w, int64_t E, int64_t N, int64_t K, float* out, hipStream_t st);
+
+}  // namespace qg

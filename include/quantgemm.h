@@ -1,0 +1,145 @@
+/*
+ * quantgemm.h -- C ABI of the MI355X (gfx950) block-quantized weight x bf16
+ * activation library (libquantgemm.so).
+ *
+ * The library multiplies a packed low-bit weight matrix W[N, K] ("BT" layout:
+ * one output per stored row, blocks running along K) by bf16 activations
+ * x[M, K] and writes fp32 y[M, N]:
+ *
+ *     y[m, n] = sum_k W[n, k] * x[m, k]
+ *
+ * Each packed weight block is read from device memory once per call and
+ * dequantized in registers; the dequantized matrix never exists in memory.
+ * This is the fused dequant-matvec of "A 320B MoE on a free Kaggle TPU"
+ * (section "The kernel, and why 64 tok/s is not a bandwidth number"), and the
+ * decode weight stream whose bytes / bandwidth set the token rate in
+ * "Qwen3.8-27B on one Tenstorrent P150" (section "4. Measuring the ceiling").
+ * The grouped entry point follows the operator seam weight[E*N, K] of vllm.cpp
+ * issue #3030 ("BACKEND-TENSTORRENT-KEEPQUANT", section "Second
+ * falsification"): E stacked matrices, E = 1 being the dense case.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named w, x, y, ids, out and workspace are DEVICE pointers owned by
+ *    the caller; the library allocates nothing, keeps no per-call state and
+ *    never synchronizes.  `stream` is a hipStream_t (NULL = the null stream);
+ *    work is enqueued on it and the call returns immediately.
+ *  - Arguments are validated on the host before anything is launched.  On
+ *    failure a non-zero qg_status is returned and nothing is enqueued.  A
+ *    failed launch returns QG_EHIP.  No C++ exception crosses this ABI.
+ *  - Alignment: w 16 bytes, x 4 bytes, y / out 4 bytes, ids 4 bytes,
+ *    workspace 16 bytes (QG_EALIGN otherwise).
+ *  - Shapes: N, M, E >= 0; K > 0 and a multiple of the format's block
+ *    (QG_ESHAPE otherwise).  M == 0 or N == 0 is a valid no-op.
+ *
+ * Packed layouts (all multi-byte fields little endian; rows contiguous, row r
+ * of weight[R, K] holding K / QK blocks in K order):
+ *  - QG_Q8_0 (QK = 32, 34 bytes): fp16 d, then 32 int8 q.  w = d * q.
+ *  - QG_Q4_K (QK = 256, 144 bytes): fp16 d, fp16 dmin, 12 bytes of packed
+ *    6-bit sub-block scales sc[8] and mins m[8], 128 bytes of 4-bit codes.
+ *    w = d * sc_j * q - dmin * m_j for sub-block j of 32 values.
+ *  - QG_Q6_K (QK = 256, 210 bytes): 128 bytes low nibbles, 64 bytes high
+ *    2-bit pairs, 16 int8 sub-scales (one per 16 values), fp16 d.
+ *    w = d * s * (q - 32).
+ *    (Q8_0 = 34 B and Q6_K = 210 B blocks: vllm.cpp issue #3030, issue body,
+ *    residency budget.  Bit positions inside the K-quant blocks follow the
+ *    GGUF convention.)
+ *  - QG_NVFP4 (QK = 16): three planes over R = E*N rows:
+ *      codes  [R][K/2]   E2M1 nibbles, value k in the low nibble of byte k/2
+ *                        when k is even, the high nibble when odd;
+ *      scales [R][K/16]  one E4M3 (fn) scale per 16 values;
+ *      g      [E]        one fp32 scale per stacked matrix.
+ *    w = (e2m1 * e4m3) * g  ("I Built a Custom Blackwell Kernel for
+ *    Qwen3.8-27B", section "What the custom path actually does": E2M1 codes,
+ *    block scales and a per-site weight scale kept in the artefact).
+ *  quant_packed_bytes() is the single source of truth for buffer sizes.
+ *
+ * Numerics: the dequantized weights of quant_dequantize are bit-exact fp32
+ * (one rounding at most, round to nearest even).  Products accumulate in fp32
+ * in a fixed order: results are deterministic run to run, row m of any
+ * quant_gemm call with M <= 16 is bitwise equal to quant_gemv on x[m], and
+ * quant_gemm is bitwise equal to quant_grouped_gemm with E = 1 and ids = NULL.
+ */
+#ifndef QUANTGEMM_H
+#define QUANTGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { QG_Q8_0 = 1, QG_Q4_K = 2, QG_Q6_K = 3, QG_NVFP4 = 4 } qg_format;
+
+typedef enum {
+    QG_OK = 0,
+    QG_EINVAL = 1,   /* null pointer where one is required */
+    QG_EFORMAT = 2,  /* unknown format tag */
+    QG_EALIGN = 3,   /* a pointer violates the alignment above */
+    QG_ESHAPE = 4,   /* negative size, K not a positive multiple of the block, size overflow, limits */
+    QG_EHIP = 5,     /* the HIP runtime reported an error on launch */
+    QG_ENOTIMPL = 6, /* combination not implemented by this build */
+    QG_EWORKSPACE = 7 /* workspace missing or smaller than quant_grouped_workspace_bytes() */
+} qg_status;
+
+/* Values per block (32, 256, 256, 16) for a tag, 0 for an unknown tag.  Host only. */
+int64_t quant_block_values(qg_format fmt);
+
+/* Bytes of a packed weight[E*N, K] tensor in the layout above; 0 when the tag
+ * is unknown, a size is negative or K is not a multiple of the block.  Host
+ * only, touches no device. */
+size_t quant_packed_bytes(qg_format fmt, int64_t E, int64_t N, int64_t K);
+
+/* Decode GEMV (M = 1): y[n] = sum_k W[n, k] * x[k].
+ * w: packed weight[N, K]; x: bf16 bit patterns [K]; y: fp32 [N] (overwritten). */
+qg_status quant_gemv(const void* w, qg_format fmt, int64_t N, int64_t K, const uint16_t* x, float* y,
+                     void* stream);
+
+/* Skinny / prefill product: y[m, n] = sum_k W[n, k] * x[m, k] for m < M.
+ * x: bf16 [M, K] row-major; y: fp32 [M, N] row-major (overwritten).
+ * Each weight block is read once per call for M <= 16 (speculative-verify
+ * blocks of 8 positions: "Qwen3.8-27B on one Tenstorrent P150", section "5.
+ * DFlash2 on Blackhole"); QG_NVFP4 with M >= 32 runs a bf16 matrix-core tile
+ * path; other formats with M > 16 take passes of 16 rows. */
+qg_status quant_gemm(const void* w, qg_format fmt, int64_t N, int64_t K, int64_t M, const uint16_t* x, float* y,
+                     void* stream);
+
+/* Bytes of workspace quant_grouped_gemm needs for E experts and M rows.  Host only. */
+size_t quant_grouped_workspace_bytes(int64_t E, int64_t M);
+
+/* Grouped-expert product over stacked weights:
+ *     y[i, n] = sum_k W_{ids[i]}[n, k] * x[i, k],  W_e = rows [e*N, (e+1)*N) of weight[E*N, K].
+ * w: packed weight[E*N, K] (for QG_NVFP4 the planes span all E*N rows and g
+ * holds E scales); x: bf16 [M, K]; ids: int32 [M] expert ids, or NULL meaning
+ * expert 0 for every row; y: fp32 [M, N].
+ * Rows are bucketed by expert on the device so that each distinct expert's
+ * weights are read once per call, whatever the number of rows routed to it
+ * ("A 320B MoE on a free Kaggle TPU", section "The decode kernel's cost is not
+ * distinct experts").
+ * An id outside [0, E) cannot be reported without a synchronization: every
+ * element of that row of y is set to NaN.
+ * workspace: device scratch of at least quant_grouped_workspace_bytes(E, M)
+ * bytes, contents undefined between calls; calls sharing a workspace must be
+ * ordered on one stream.  Limits: M <= 16384 (QG_ESHAPE beyond). */
+qg_status quant_grouped_gemm(const void* w, qg_format fmt, int64_t E, int64_t N, int64_t K, int64_t M,
+                             const uint16_t* x, const int32_t* ids, float* y, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Dequantize rows [0, rows) of a packed weight[rows, K] to fp32 out[rows, K]
+ * (bit-exact; a test and debugging aid, the products never call it).
+ * For QG_NVFP4, `rows` is E*N of the tensor and all rows use g[0]; use
+ * quant_dequantize_stacked for several stacked matrices. */
+qg_status quant_dequantize(const void* w, qg_format fmt, int64_t rows, int64_t K, float* out, void* stream);
+
+/* As quant_dequantize for a stacked weight[E*N, K]: out is [E*N, K]. */
+qg_status quant_dequantize_stacked(const void* w, qg_format fmt, int64_t E, int64_t N, int64_t K, float* out,
+                                   void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* quant_status_string(qg_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QUANTGEMM_H */

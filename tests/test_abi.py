@@ -1,0 +1,105 @@
+"""The C ABI without a GPU: symbols, host-only queries and host-side validation.
+
+Nothing here launches device work: every call either is host-only or is
+rejected by argument validation before the HIP runtime is touched.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gemm_block_quant_amd as qg
+import oracle
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "quantgemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(quant_[a-z_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 9, names
+    L = qg.lib()
+    for n in names:
+        assert getattr(L, n) is not None, n
+
+
+def test_packed_bytes_agrees_with_oracle():
+    g = np.random.default_rng(0)
+    for _ in range(300):
+        fmt = int(g.integers(0, 6))
+        E = int(g.integers(0, 5))
+        N = int(g.integers(0, 3000))
+        K = int(g.integers(0, 40)) * 16
+        assert qg.quant_packed_bytes(fmt, E, N, K) == oracle.packed_bytes(fmt, E, N, K), (fmt, E, N, K)
+    for fmt in (1, 2, 3, 4):
+        assert qg.quant_block_values(fmt) == oracle.block_values(fmt)
+    assert qg.quant_block_values(0) == 0 and qg.quant_block_values(7) == 0
+
+
+def test_status_strings():
+    for s in range(9):
+        assert isinstance(qg.quant_status_string(s), str) and qg.quant_status_string(s)
+
+
+def _raw(name):
+    return getattr(qg.lib(), name)
+
+
+FAKE_W = ctypes.c_void_p(0x100000)
+FAKE_X = ctypes.c_void_p(0x200000)
+FAKE_Y = ctypes.c_void_p(0x300000)
+
+
+def test_validation_rejects_before_launch():
+    gemm = _raw("quant_gemm")
+    # unknown format, bad K, negative sizes
+    assert gemm(FAKE_W, 9, 4, 256, 1, FAKE_X, FAKE_Y, None) == qg.QG_EFORMAT
+    assert gemm(FAKE_W, qg.Q4_K, 4, 100, 1, FAKE_X, FAKE_Y, None) == qg.QG_ESHAPE
+    assert gemm(FAKE_W, qg.Q4_K, 4, 0, 1, FAKE_X, FAKE_Y, None) == qg.QG_ESHAPE
+    assert gemm(FAKE_W, qg.Q4_K, -1, 256, 1, FAKE_X, FAKE_Y, None) == qg.QG_ESHAPE
+    assert gemm(FAKE_W, qg.Q4_K, 4, 256, -2, FAKE_X, FAKE_Y, None) == qg.QG_ESHAPE
+    assert gemm(FAKE_W, qg.NVFP4, 4, 24, 1, FAKE_X, FAKE_Y, None) == qg.QG_ESHAPE
+    # empty products are valid no-ops, even with null pointers
+    assert gemm(None, qg.Q4_K, 0, 256, 3, None, None, None) == qg.QG_OK
+    assert gemm(None, qg.Q4_K, 5, 256, 0, None, None, None) == qg.QG_OK
+    # null pointers
+    assert gemm(None, qg.Q4_K, 4, 256, 1, FAKE_X, FAKE_Y, None) == qg.QG_EINVAL
+    assert gemm(FAKE_W, qg.Q4_K, 4, 256, 1, None, FAKE_Y, None) == qg.QG_EINVAL
+    assert gemm(FAKE_W, qg.Q4_K, 4, 256, 1, FAKE_X, None, None) == qg.QG_EINVAL
+    # alignment: w and x 16 bytes, y 4 bytes
+    assert gemm(ctypes.c_void_p(0x100008), qg.Q4_K, 4, 256, 1, FAKE_X, FAKE_Y, None) == qg.QG_EALIGN
+    assert gemm(FAKE_W, qg.Q4_K, 4, 256, 1, ctypes.c_void_p(0x200004), FAKE_Y, None) == qg.QG_EALIGN
+    assert gemm(FAKE_W, qg.Q4_K, 4, 256, 1, FAKE_X, ctypes.c_void_p(0x300002), None) == qg.QG_EALIGN
+    gemv = _raw("quant_gemv")
+    assert gemv(FAKE_W, qg.Q8_0, 4, 48, FAKE_X, FAKE_Y, None) == qg.QG_ESHAPE
+    deq = _raw("quant_dequantize")
+    assert deq(FAKE_W, 0, 4, 256, FAKE_Y, None) == qg.QG_EFORMAT
+    assert deq(None, qg.Q6_K, 4, 256, FAKE_Y, None) == qg.QG_EINVAL
+    assert deq(FAKE_W, qg.Q6_K, 0, 256, FAKE_Y, None) == qg.QG_OK
+
+
+def test_grouped_validation():
+    grouped = _raw("quant_grouped_gemm")
+    E, N, K, M = 4, 8, 256, 3
+    wsb = qg.quant_grouped_workspace_bytes(E, M)
+    assert wsb > 0
+    ws = ctypes.c_void_p(0x400000)
+    ids = ctypes.c_void_p(0x500000)
+    args = lambda **kw: [kw.get("w", FAKE_W), kw.get("fmt", qg.Q4_K), kw.get("E", E), N, K, kw.get("M", M), FAKE_X,
+                         kw.get("ids", ids), FAKE_Y, kw.get("ws", ws), kw.get("wsb", wsb), None]
+    assert grouped(*args(E=0)) == qg.QG_ESHAPE
+    assert grouped(*args(fmt=5)) == qg.QG_EFORMAT
+    assert grouped(*args(ws=None)) == qg.QG_EWORKSPACE
+    assert grouped(*args(wsb=wsb - 1)) == qg.QG_EWORKSPACE
+    assert grouped(*args(ws=ctypes.c_void_p(0x400004))) == qg.QG_EALIGN
+    assert grouped(*args(ids=ctypes.c_void_p(0x500002))) == qg.QG_EALIGN
+    assert grouped(*args(M=0, ws=None, wsb=0)) == qg.QG_OK
+    assert grouped(*args(M=20000)) == qg.QG_ESHAPE

@@ -1,0 +1,75 @@
+"""GPU parity of the grouped-expert product over stacked weight[E*N, K]."""
+import numpy as np
+import pytest
+
+import gemm_block_quant_amd as qg
+import oracle
+import synth
+from helpers import assert_band, dev_bytes, dev_x, same_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _ids_dev(ids):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+
+
+@pytest.mark.parametrize("fmt,E,N,K,M", [
+    (qg.Q4_K, 5, 100, 512, 12), (qg.Q6_K, 4, 77, 768, 9), (qg.Q8_0, 6, 50, 1024, 20),
+    (qg.NVFP4, 3, 64, 592, 7), (qg.Q4_K, 40, 130, 2048, 37),
+])
+def test_grouped_band_and_invalid_rows(fmt, E, N, K, M):
+    w = synth.weights(fmt, synth.rng(21, 0), E * N, K, E=E)
+    x = synth.x_bf16(synth.rng(21, 1), M, K)
+    g = np.random.default_rng(E + M)
+    ids = g.integers(0, E, M).astype(np.int32)
+    ids[1] = -1
+    ids[M // 2] = E  # out of range
+    ids[2:5] = ids[0]  # repeats
+    y = qg.quant_grouped_gemm(dev_bytes(w), fmt, E, N, K, M, dev_x(x), _ids_dev(ids)).cpu().numpy()
+    y_ref, bound = oracle.gemm(fmt, w, N, K, x, E=E, ids=ids)
+    bad = (ids < 0) | (ids >= E)
+    assert np.isnan(y[bad]).all()
+    assert_band(y[~bad], y_ref[~bad], bound[~bad], "grouped fmt %d" % fmt)
+
+
+@pytest.mark.parametrize("fmt,K", [(qg.Q4_K, 4096), (qg.NVFP4, 5120), (qg.Q6_K, 2048)])
+def test_grouped_e1_is_dense_bitwise(fmt, K):
+    N, M = 257, 11
+    w = synth.weights(fmt, synth.rng(22, 0), N, K)
+    x = synth.x_bf16(synth.rng(22, 1), M, K)
+    wd, xd = dev_bytes(w), dev_x(x)
+    yd = qg.quant_gemm(wd, fmt, N, K, M, xd).cpu().numpy()
+    yg = qg.quant_grouped_gemm(wd, fmt, 1, N, K, M, xd, None).cpu().numpy()
+    assert same_bits(yg, yd)
+    # each row of a grouped call equals the decode GEMV of its own expert
+    E = 3
+    ws = synth.weights(fmt, synth.rng(23, 0), E * N, K, E=E)
+    ids = np.array([2, 0, 2, 1, 2, 0, 1, 1, 2, 0, 2], np.int32)
+    yg = qg.quant_grouped_gemm(dev_bytes(ws), fmt, E, N, K, M, xd, _ids_dev(ids)).cpu().numpy()
+    for i, e in enumerate(ids):
+        if fmt == qg.NVFP4:
+            R = E * N
+            codes = ws[e * N * K // 2:(e + 1) * N * K // 2]
+            sc = ws[R * K // 2 + e * N * K // 16: R * K // 2 + (e + 1) * N * K // 16]
+            gs = ws[R * K // 2 + R * K // 16 + 4 * e: R * K // 2 + R * K // 16 + 4 * e + 4]
+            we = np.concatenate([codes, sc, gs])
+        else:
+            eb = oracle.packed_bytes(fmt, 1, N, K)
+            we = ws[e * eb:(e + 1) * eb]
+        y1 = qg.quant_gemv(dev_bytes(we), fmt, N, K, xd[i].contiguous()).cpu().numpy()
+        assert same_bits(yg[i], y1), i
+
+
+@pytest.mark.parametrize("N,K", [(2048, 4096), (4096, 2048)])
+def test_grouped_moe_layer_sampled(N, K):
+    """288 stacked Q4_K experts, 16 tokens each routed to 8 distinct experts."""
+    E, T, topk = 288, 16, 8
+    w = synth.weights(qg.Q4_K, synth.rng(5, 0 if K == 4096 else 4), E * N, K, E=E)
+    x = synth.x_bf16(synth.rng(5, 1 if K == 4096 else 3), T * topk, K)
+    ids = synth.routing(synth.rng(5, 2), T, topk, E)
+    y = qg.quant_grouped_gemm(dev_bytes(w), qg.Q4_K, E, N, K, T * topk, dev_x(x), _ids_dev(ids)).cpu().numpy()
+    cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(1).integers(0, N, 62)]))
+    y_ref, bound = oracle.gemm(qg.Q4_K, w, N, K, x, E=E, ids=ids, cols=cols)
+    assert_band(y[:, cols], y_ref, bound, "moe N %d K %d" % (N, K))

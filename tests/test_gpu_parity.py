@@ -1,0 +1,149 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+* dequantization: bit-exact fp32 (NaN matches NaN);
+* products: |y - y_ref| <= 2e-3 * sum_k |w x| for every output element;
+* invariants: row m of an M-row call equals the M = 1 call bit for bit, runs
+  repeat bit for bit.
+Shapes span several row tiles, ragged N, K of one block, K-segmented rows and
+every row-pass width.
+"""
+import numpy as np
+import pytest
+
+import gemm_block_quant_amd as qg
+import oracle
+import synth
+from helpers import assert_band, dev_bytes, dev_x, make_case, same_bits
+
+pytestmark = pytest.mark.gpu
+
+DEQ_SHAPES = [
+    (qg.Q8_0, 37, 96), (qg.Q8_0, 5, 1024),
+    (qg.Q4_K, 13, 512), (qg.Q4_K, 3, 5120),
+    (qg.Q6_K, 11, 768), (qg.Q6_K, 2, 17408),
+    (qg.NVFP4, 9, 48), (qg.NVFP4, 17, 5120),
+]
+
+
+def _put_f16(buf, off, value_bits):
+    buf[off] = value_bits & 0xFF
+    buf[off + 1] = value_bits >> 8
+
+
+def _with_specials(fmt, w, N, K):
+    """Overwrite a few blocks with edge values: zero / subnormal / max / negative fp16
+    scales, int8 sub-scale -128, E4M3 subnormal, max, zero, -0 and NaN scales."""
+    w = w.copy()
+    if fmt == qg.NVFP4:
+        R = N
+        sc0 = R * K // 2
+        specials = [0x00, 0x01, 0x07, 0x7E, 0x7F, 0x80, 0xFE, 0x08]
+        for i, s in enumerate(specials[: R * K // 16]):
+            w[sc0 + i] = s
+        w[0] = 0x08  # codes -0 and +0
+        return w
+    bb = {qg.Q8_0: 34, qg.Q4_K: 144, qg.Q6_K: 210}[fmt]
+    doff = {qg.Q8_0: 0, qg.Q4_K: 0, qg.Q6_K: 208}[fmt]
+    nblk = w.size // bb
+    for i, bits in enumerate([0x0000, 0x0001, 0x03FF, 0x7BFF, 0x8000 | 0x2E66, 0x0400]):
+        if i < nblk:
+            _put_f16(w, i * bb + doff, bits)
+    if fmt == qg.Q4_K and nblk > 2:
+        _put_f16(w, 2 * bb + 2, 0x0001)  # subnormal dmin
+    if fmt == qg.Q6_K and nblk > 1:
+        w[bb + 192: bb + 208] = 0x80  # sub-scales -128
+    return w
+
+
+@pytest.mark.parametrize("fmt,N,K", DEQ_SHAPES)
+def test_dequant_bit_exact(fmt, N, K):
+    w, _ = make_case(fmt, N, K, 1, seed=100 + fmt)
+    w = _with_specials(fmt, w, N, K)
+    ref = oracle.dequant_rows(fmt, w, 1, N, K)
+    got = qg.quant_dequantize(dev_bytes(w), fmt, N, K).cpu().numpy()
+    assert same_bits(got, ref)
+
+
+def test_dequant_stacked_nvfp4_scales():
+    E, N, K = 3, 5, 64
+    w, _ = make_case(qg.NVFP4, N, K, 1, seed=7, E=E)
+    ref = oracle.dequant_rows(qg.NVFP4, w, E, N, K)
+    got = qg.quant_dequantize_stacked(dev_bytes(w), qg.NVFP4, E, N, K).cpu().numpy()
+    assert same_bits(got, ref)
+
+
+PRODUCT_CASES = [
+    # (fmt, N, K, M)
+    (qg.Q8_0, 1, 32, 1), (qg.Q8_0, 300, 1024, 1), (qg.Q8_0, 1000, 2048, 3), (qg.Q8_0, 129, 4192, 8),
+    (qg.Q4_K, 1, 256, 1), (qg.Q4_K, 5, 512, 2), (qg.Q4_K, 1000, 5120, 1), (qg.Q4_K, 777, 5120, 8),
+    (qg.Q4_K, 257, 1792, 16), (qg.Q4_K, 130, 17408, 1), (qg.Q4_K, 64, 17408, 17),
+    (qg.Q6_K, 1, 256, 1), (qg.Q6_K, 3, 768, 4), (qg.Q6_K, 1000, 5120, 1), (qg.Q6_K, 150, 17408, 1),
+    (qg.Q6_K, 99, 17408, 8), (qg.Q6_K, 333, 5120, 33),
+    (qg.NVFP4, 1, 16, 1), (qg.NVFP4, 3, 48, 2), (qg.NVFP4, 1000, 5120, 1), (qg.NVFP4, 100, 17408, 1),
+    (qg.NVFP4, 77, 592, 8), (qg.NVFP4, 200, 5120, 16), (qg.NVFP4, 51, 17408, 8),
+]
+
+
+@pytest.mark.parametrize("fmt,N,K,M", PRODUCT_CASES)
+def test_product_band(fmt, N, K, M):
+    w, x = make_case(fmt, N, K, M, seed=1000 + N + K + M)
+    y_ref, bound = oracle.gemm(fmt, w, N, K, x)
+    wd, xd = dev_bytes(w), dev_x(x)
+    if M == 1:
+        y = qg.quant_gemv(wd, fmt, N, K, xd).cpu().numpy().reshape(1, N)
+    else:
+        y = qg.quant_gemm(wd, fmt, N, K, M, xd).cpu().numpy()
+    assert_band(y, y_ref, bound, "fmt %d N %d K %d M %d" % (fmt, N, K, M))
+
+
+@pytest.mark.parametrize("fmt,K", [(qg.Q8_0, 1024), (qg.Q4_K, 5120), (qg.Q6_K, 17408), (qg.NVFP4, 5120)])
+def test_rows_match_decode_bitwise_and_repeat(fmt, K):
+    """Row m of M = 8 (and M = 16) equals the M = 1 result bit for bit; runs repeat."""
+    N, M = 300, 16
+    w, x = make_case(fmt, N, K, M, seed=55)
+    wd, xd = dev_bytes(w), dev_x(x)
+    y16 = qg.quant_gemm(wd, fmt, N, K, M, xd).cpu().numpy()
+    y8 = qg.quant_gemm(wd, fmt, N, K, 8, xd[:8].contiguous()).cpu().numpy()
+    for m in range(M):
+        y1 = qg.quant_gemv(wd, fmt, N, K, xd[m].contiguous()).cpu().numpy()
+        assert same_bits(y16[m], y1), m
+        if m < 8:
+            assert same_bits(y8[m], y1), m
+    again = qg.quant_gemm(wd, fmt, N, K, M, xd).cpu().numpy()
+    assert same_bits(again, y16)
+
+
+def test_zero_activations_and_zero_weights():
+    fmt, N, K = qg.Q4_K, 64, 512
+    w, x = make_case(fmt, N, K, 1, seed=3)
+    y = qg.quant_gemv(dev_bytes(w), fmt, N, K, dev_x(np.zeros_like(x))).cpu().numpy()
+    assert not y.any()
+    wz = w.copy().reshape(-1, 144)
+    wz[:, 0:4] = 0  # d = dmin = 0
+    y = qg.quant_gemv(dev_bytes(wz.reshape(-1)), fmt, N, K, dev_x(x)).cpu().numpy()
+    assert not y.any()
+
+
+FULL = [
+    # the workload shapes: Q8_0 1024x1024; Q4_K fused gate+up; Q6_K down and LM head; NVFP4 both MLP shapes
+    (qg.Q8_0, 1024, 1024, 1),
+    (qg.Q4_K, 2 * 17408, 5120, 1),
+    (qg.Q6_K, 5120, 17408, 1), (qg.Q6_K, 5120, 17408, 8),
+    (qg.Q6_K, 248320, 5120, 1), (qg.Q6_K, 248320, 5120, 8),
+    (qg.NVFP4, 17408, 5120, 1), (qg.NVFP4, 17408, 5120, 8),
+    (qg.NVFP4, 5120, 17408, 1), (qg.NVFP4, 5120, 17408, 8),
+]
+
+
+@pytest.mark.parametrize("fmt,N,K,M", FULL)
+def test_full_size_sampled(fmt, N, K, M):
+    seed = {qg.Q8_0: 1, qg.Q4_K: 2, qg.Q6_K: 3, qg.NVFP4: 4}[fmt]
+    w = synth.weights(fmt, synth.rng(seed, 0), N, K)
+    x = synth.x_bf16(synth.rng(seed, 1), M, K)
+    wd, xd = dev_bytes(w), dev_x(x)
+    y = (qg.quant_gemv(wd, fmt, N, K, xd).reshape(1, N) if M == 1 else qg.quant_gemm(wd, fmt, N, K, M, xd))
+    y = y.cpu().numpy()
+    cols = np.unique(np.concatenate([np.arange(8), N - 1 - np.arange(8),
+                                     np.random.default_rng(seed).integers(0, N, 240)]))
+    y_ref, bound = oracle.gemm(fmt, w, N, K, x, cols=cols)
+    assert_band(y[:, cols], y_ref, bound, "full fmt %d N %d K %d M %d" % (fmt, N, K, M))
