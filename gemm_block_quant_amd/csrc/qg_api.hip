@@ -2,7 +2,10 @@
 // Nothing here allocates device memory or synchronizes a stream.
 #include <limits.h>
 
-#include "qg_internal.h"
+#include <mutex>
+#include <unordered_map>
+
+#include "qg_stream.h"
 
 using namespace qg;
 
@@ -61,6 +64,34 @@ StreamArgs stream_args(const void* w, int fmt, int64_t E, int64_t e, int64_t N, 
 qg_status from_hip(hipError_t e) { return e == hipSuccess ? QG_OK : QG_EHIP; }
 
 }  // namespace
+
+namespace qg {
+
+hipError_t kernel_residency(const void* fn, size_t lds, int* per_cu, int block) {
+    static std::mutex mu;
+    static std::unordered_map<const void*, std::unordered_map<size_t, int>> cache;  // per kernel, per LDS size
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(fn);
+    if (it == cache.end()) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        if (e != hipSuccess) return e;
+        it = cache.emplace(fn, std::unordered_map<size_t, int>()).first;
+    }
+    auto jt = it->second.find(lds);
+    if (jt != it->second.end()) {
+        *per_cu = jt->second;
+        return hipSuccess;
+    }
+    int fit = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, fn, block, lds);
+    if (e != hipSuccess) return e;
+    if (fit < 1) fit = 1;
+    it->second.emplace(lds, fit);
+    *per_cu = fit;
+    return hipSuccess;
+}
+
+}  // namespace qg
 
 extern "C" {
 

@@ -12,6 +12,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 #define QG_LDS __attribute__((address_space(3)))
+#define QG_GLOBAL __attribute__((address_space(1)))
 typedef QG_LDS uint8_t lds_u8;
 typedef QG_LDS uint16_t lds_u16;
 typedef QG_LDS uint32_t lds_u32;
@@ -89,10 +90,16 @@ __device__ __forceinline__ uint32_t lds_ld32_a2(const lds_u8* p) {
 
 // ---------------------------------------------------------------- global access
 
-// Streaming 16-byte load that should not displace cached data.
+// Streaming 16-byte load that should not displace cached data.  The explicit
+// global address space keeps it a global_load (a flat load would also count
+// against the LDS wait counter and serialize the row ring with the decode).
 __device__ __forceinline__ u32x4 ld_stream128(const uint8_t* p) {
-    return __builtin_nontemporal_load((const u32x4*)p);
+    return __builtin_nontemporal_load((const QG_GLOBAL u32x4*)(uintptr_t)p);
 }
+
+// Ordinary global 16-byte load / 4-byte store through the global address space.
+__device__ __forceinline__ u32x4 ld_global128(const void* p) { return *(const QG_GLOBAL u32x4*)(uintptr_t)p; }
+__device__ __forceinline__ void st_global_f32(float* p, float v) { *(QG_GLOBAL float*)(uintptr_t)p = v; }
 
 // 16 bytes starting at p where only [p, limit) may be read (limit - p < 16),
 // one byte at a time; bytes past limit read as zero.  Only the final chunk of a

@@ -1,11 +1,18 @@
 // qg_gemv.hip -- dense decode GEMV (M = 1) and skinny product (M <= 16 rows
 // per pass) over one packed weight matrix: persistent workgroups, the grid's
-// waves taking rows n = gw, gw + GW, ...  The streaming core is qg_stream.h.
-#include "qg_stream.h"
+// waves taking rows n = gw, gw + GW, ...  Q4_K and NVFP4 (K % 32 == 0) stream
+// straight into registers (qg_direct.h); Q6_K and Q8_0, whose blocks are not
+// 16-byte aligned, go through a wave-private LDS row buffer (qg_stream.h).
+#include "qg_direct.h"
 
 namespace qg {
 
-// LDS layout: [x bf16: MT*K][x sums fp32: MT*K/16][per-wave row buffers]
+// LDS one launch needs for `mt` activation rows.
+size_t stream_lds_bytes(int fmt, int K, int mt) {
+    if (direct_eligible(fmt, K)) return direct_lds_bytes(fmt, mt, K);
+    return gemv_lds_bytes(mt, K, choose_cpl(fmt, K), fmt == QG_NVFP4 ? 1 : 0);
+}
+
 template <int F, int MT, int CPL, int CPLS, int PF>
 __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
@@ -17,78 +24,143 @@ __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     lds_u8* rowbuf = smem + rowbuf_offset(MT, K) + (size_t)wid * rowbuf_bytes(CPL, CPLS);
     lds_u8* rowbuf_s = rowbuf + CPL * 1024 + 32;
-
-    stage_x<MT, kSums>(xl, xs, a.x, a.ldx, a.M, K, [&](int m) { return a.xrow[m]; });
-
     const int lane = threadIdx.x & 63;
     const int GW = gridDim.x * kWavesPerBlock;
     const int gw = blockIdx.x * kWavesPerBlock + wid;
     MatView mv = {a.w0, a.rb0, a.w1, a.rb1, a.gbytes};
     const int64_t yrow = a.yrow[lane < a.M ? lane : 0];
+    auto stage = [&] { stage_x<MT, kSums>(xl, xs, a.x, a.ldx, a.M, K, [&](int m) { return a.xrow[m]; }); };
     wave_stream<F, MT, CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf, rowbuf_s, gw, GW, a.N, a.y,
-                                      a.ldy, yrow, a.M);
+                                      a.ldy, yrow, a.M, stage);
 }
 
-template <int F, int MT, int CPL, int CPLS, int PF>
-static hipError_t launch_one(const StreamArgs& a, int per_cu, hipStream_t st) {
-    const size_t lds = gemv_lds_bytes(MT, a.K, CPL, CPLS);
-    auto kern = k_stream_gemm<F, MT, CPL, CPLS, PF>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    // persistent grid: as many 4-wave workgroups as fit at once, never more waves than rows
-    int fit = (int)(kLdsBytes / lds);
-    if (fit > per_cu) fit = per_cu;
-    if (fit < 1) fit = 1;
+// Direct path: one 16-wave workgroup per CU.  Workgroup b owns an equal
+// contiguous share of the row groups and its waves take them one at a time
+// from a counter in LDS, so every CU finishes within about one row group of
+// the others.  The order in which waves take rows does not change any row's
+// arithmetic.
+constexpr int kDirectWaves = 16;
+
+template <int F, int MT, int SP, int PF>
+__global__ __launch_bounds__(1024) void k_direct_gemm(const StreamArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
+    lds_u8* smem = (lds_u8*)smem_generic;
+    constexpr int G = Direct<F>::G, RW = 64 / G;
+    const int K = a.K;
+    QG_LDS int* counter = (QG_LDS int*)smem;
+    lds_u8* xl = smem + 16;
+    lds_f32* xs = (lds_f32*)(xl + (size_t)MT * direct_xrow_bytes(F, K));
+    const int lane = threadIdx.x & 63;
+    const int li = threadIdx.x & (G - 1);
+    const int groups = (a.N + RW - 1) / RW;
+    const int per = (groups + gridDim.x - 1) / gridDim.x;
+    const int g0 = blockIdx.x * per, g1 = min(groups, g0 + per);
+    if (threadIdx.x == 0) *counter = 0;
+    auto next_group = [&]() {
+        int t = 0;
+        if (lane == 0) t = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        t = __builtin_amdgcn_readfirstlane(t);
+        return g0 + t < g1 ? g0 + t : -1;
+    };
+    MatView mv = {a.w0, a.rb0, a.w1, a.rb1, a.gbytes};
+    const int64_t yrow = a.yrow[li < a.M ? li : 0];
+    auto row_of = [&](int m) { return a.xrow[m]; };
+    XStage<F, MT, 2> xst;
+    xst.issue(a.x, a.ldx, a.M, K, row_of);
+    __syncthreads();  // the counter is initialised before any wave takes work
+    auto between = [&] { xst.commit(xl, xs, a.x, a.ldx, a.M, K, row_of); };
+    wave_stream_direct<F, MT, SP, PF>(mv, a.N, K, xl, xs, next_group, a.y, a.ldy, yrow, a.M, between);
+}
+
+// Persistent grid: as many 4-wave workgroups as can be resident at once (by
+// registers and LDS), never more waves than work items (rows / rows per wave).
+template <class Kern>
+static hipError_t launch_persistent(Kern kern, const StreamArgs& a, size_t lds, int rows_per_wave, hipStream_t st) {
+    int fit = 0;
+    hipError_t e = kernel_residency((const void*)kern, lds, &fit, 256);
+    if (e != hipSuccess) return e;
     long waves = (long)num_cus() * fit * kWavesPerBlock;
-    if (waves > a.N) waves = a.N;
+    const long need = (a.N + rows_per_wave - 1) / rows_per_wave;
+    if (waves > need) waves = need;
     const int grid = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }
 
 template <int F, int MT>
-static hipError_t dispatch_cpl(StreamArgs a, hipStream_t st) {
+static hipError_t dispatch_rlt(StreamArgs a, hipStream_t st) {
     const int cpl = choose_cpl(F, a.K);
     a.seg_blocks = segment_blocks(F, a.K, cpl);
     const int nb = a.K / BlockGeom<F>::QK;
     a.nseg = (nb + a.seg_blocks - 1) / a.seg_blocks;
     constexpr int S = (F == QG_NVFP4) ? 1 : 0;
+    const size_t lds = gemv_lds_bytes(MT, a.K, cpl, S);
     switch (cpl) {
-        case 1: return launch_one<F, MT, 1, S, 4>(a, 4, st);
-        case 2: return launch_one<F, MT, 2, S, 4>(a, 4, st);
-        case 3: return launch_one<F, MT, 3, S, 4>(a, 4, st);
-        case 4: return launch_one<F, MT, 4, S, 3>(a, 4, st);
-        default: return launch_one<F, MT, 6, S, 2>(a, 4, st);
+        case 1: return launch_persistent(k_stream_gemm<F, MT, 1, S, 4>, a, lds, 1, st);
+        case 2: return launch_persistent(k_stream_gemm<F, MT, 2, S, 4>, a, lds, 1, st);
+        case 3: return launch_persistent(k_stream_gemm<F, MT, 3, S, 4>, a, lds, 1, st);
+        case 4: return launch_persistent(k_stream_gemm<F, MT, 4, S, 3>, a, lds, 1, st);
+        default: return launch_persistent(k_stream_gemm<F, MT, 6, S, 2>, a, lds, 1, st);
     }
+}
+
+// Direct path: SP passes per ring slot, PF slots (pure tuning: the per-row
+// arithmetic does not depend on them).
+template <int F, int MT> struct DirectTune;
+template <int MT> struct DirectTune<QG_Q4_K, MT> { static constexpr int SP = 1, PF = MT <= 4 ? 2 : MT <= 8 ? 3 : 2; };
+template <int MT> struct DirectTune<QG_NVFP4, MT> { static constexpr int SP = 2, PF = 3; };
+
+template <int F, int MT>
+static hipError_t dispatch_direct(const StreamArgs& a, hipStream_t st) {
+    const size_t lds = 16 + direct_lds_bytes(F, MT, a.K);
+    auto kern = k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF>;
+    int fit = 0;
+    hipError_t e = kernel_residency((const void*)kern, lds, &fit, 1024);
+    if (e != hipSuccess) return e;
+    constexpr int RW = 64 / Direct<F>::G;
+    const long groups = (a.N + RW - 1) / RW;
+    long grid = (long)num_cus() * fit;
+    if (grid > groups) grid = groups;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(1024), lds, st, a);
+    return hipGetLastError();
 }
 
 template <int F>
 static hipError_t dispatch_mt(const StreamArgs& a, int mt, hipStream_t st) {
-    switch (mt) {
-        case 1: return dispatch_cpl<F, 1>(a, st);
-        case 2: return dispatch_cpl<F, 2>(a, st);
-        case 4: return dispatch_cpl<F, 4>(a, st);
-        case 8: return dispatch_cpl<F, 8>(a, st);
-        default: return dispatch_cpl<F, 16>(a, st);
+    if constexpr (F == QG_Q4_K || F == QG_NVFP4) {
+        if (direct_eligible(F, a.K)) {
+            switch (mt) {
+                case 1: return dispatch_direct<F, 1>(a, st);
+                case 2: return dispatch_direct<F, 2>(a, st);
+                case 4: return dispatch_direct<F, 4>(a, st);
+                case 8: return dispatch_direct<F, 8>(a, st);
+                default: return dispatch_direct<F, 16>(a, st);
+            }
+        }
     }
+    if constexpr (F != QG_Q4_K) {
+        switch (mt) {
+            case 1: return dispatch_rlt<F, 1>(a, st);
+            case 2: return dispatch_rlt<F, 2>(a, st);
+            case 4: return dispatch_rlt<F, 4>(a, st);
+            case 8: return dispatch_rlt<F, 8>(a, st);
+            default: return dispatch_rlt<F, 16>(a, st);
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 static int mt_for(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16; }
 
 // Activation rows one pass of the streaming kernel can take: the largest of
-// 16, 8, 4, 2, 1 (capped by M) whose activations, activation sums and row
-// buffers fit in the 160 KB of LDS.  0 when not even one row fits.
+// 16, 8, 4, 2, 1 (capped by M) whose LDS needs fit in 160 KB.  0 when not
+// even one row fits.
 int stream_rows_per_pass(int fmt, int K, int M) {
     const int cands[5] = {16, 8, 4, 2, 1};
-    const int cpl = choose_cpl(fmt, K);
     for (int i = 0; i < 5; ++i) {
         const int mt = cands[i];
         if (mt > 1 && mt / 2 >= M) continue;  // a smaller instantiation already covers M
-        if (gemv_lds_bytes(mt, K, cpl, fmt == QG_NVFP4 ? 1 : 0) <= (size_t)kLdsBytes) return mt < M ? mt : M;
+        if (stream_lds_bytes(fmt, K, mt) <= (size_t)kLdsBytes) return mt < M ? mt : M;
     }
     return 0;
 }

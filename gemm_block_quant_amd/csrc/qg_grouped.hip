@@ -23,7 +23,9 @@
 //     past the number of distinct experts exit at once.
 // The per-row arithmetic is the dense kernel's, so E = 1 with ids = NULL
 // reproduces quant_gemm bit for bit.
-#include "qg_stream.h"
+#include <type_traits>
+
+#include "qg_direct.h"
 
 namespace qg {
 
@@ -124,25 +126,27 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
     }
 }
 
-// Grouped streaming kernel.  MTMAX: activation rows per pass (LDS sized for it).
-template <int F, int MTMAX, int CPL, int CPLS, int PF>
+// Grouped streaming kernel.  MTMAX: activation rows per pass (LDS sized for
+// it); DIRECT: register-direct streaming (Q4_K, NVFP4 with K % 32 == 0) with SP
+// passes per ring slot, else the LDS row-buffer path with CPL/CPLS chunks.
+template <int F, int MTMAX, bool DIRECT, int CPL, int CPLS, int SP, int PF>
 __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32_t* __restrict__ ws, int64_t E,
                                                  int64_t M, int rpc, int nchunks, int64_t estride0,
                                                  int64_t estride1) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8* smem = (lds_u8*)smem_generic;
-    constexpr bool kSums = (F == QG_Q4_K || F == QG_Q6_K);
+    constexpr bool kSums = DIRECT ? (F == QG_Q4_K) : (F == QG_Q4_K || F == QG_Q6_K);
     const int K = a.K;
     const int slot = blockIdx.x / nchunks, chunk = blockIdx.x % nchunks;
     const int nslots = ws[0];
-    if (slot >= nslots) return;
+    if (slot >= nslots) return;  // uniform across the workgroup: no barrier is skipped by part of it
     const int64_t S = ws_slots(E, M);
     const int e = ws[4 + slot];
     const int r0 = ws[4 + S + slot], r1 = ws[4 + S + slot + 1];
     const int32_t* perm = ws + 5 + 2 * S;
 
     lds_u8* xl = smem;
-    lds_f32* xs = (lds_f32*)(smem + (size_t)MTMAX * K * 2);
+    lds_f32* xs = (lds_f32*)(smem + (DIRECT ? (size_t)MTMAX * direct_xrow_bytes(F, K) : (size_t)MTMAX * K * 2));
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     lds_u8* rowbuf = smem + rowbuf_offset(MTMAX, K) + (size_t)wid * rowbuf_bytes(CPL, CPLS);
@@ -160,32 +164,37 @@ __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32
     for (int p0 = r0; p0 < r1; p0 += MTMAX) {
         const int cnt = min(MTMAX, r1 - p0);
         if (p0 != r0) __syncthreads();  // every wave is done with the previous pass's activations
-        const int64_t yrow = perm[p0 + (lane < cnt ? lane : 0)];
+        const int li = DIRECT ? (lane & (direct_group_lanes(F) - 1)) : lane;
+        const int64_t yrow = perm[p0 + (li < cnt ? li : 0)];
         auto row_of = [&](int m) { return perm[p0 + m]; };
-        if (cnt <= 1 || MTMAX == 1) {
-            stage_x<1, kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of);
-            wave_stream<F, 1, CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf, rowbuf_s, n_begin + wid,
-                                             kWavesPerBlock, n_end, a.y, a.ldy, yrow, cnt);
-        } else if (cnt <= 2 || MTMAX == 2) {
-            stage_x<(MTMAX < 2 ? MTMAX : 2), kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of);
-            wave_stream<F, (MTMAX < 2 ? MTMAX : 2), CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf,
-                                                                   rowbuf_s, n_begin + wid, kWavesPerBlock, n_end,
-                                                                   a.y, a.ldy, yrow, cnt);
-        } else if (cnt <= 4 || MTMAX == 4) {
-            stage_x<(MTMAX < 4 ? MTMAX : 4), kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of);
-            wave_stream<F, (MTMAX < 4 ? MTMAX : 4), CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf,
-                                                                   rowbuf_s, n_begin + wid, kWavesPerBlock, n_end,
-                                                                   a.y, a.ldy, yrow, cnt);
-        } else if (cnt <= 8 || MTMAX == 8) {
-            stage_x<(MTMAX < 8 ? MTMAX : 8), kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of);
-            wave_stream<F, (MTMAX < 8 ? MTMAX : 8), CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf,
-                                                                   rowbuf_s, n_begin + wid, kWavesPerBlock, n_end,
-                                                                   a.y, a.ldy, yrow, cnt);
-        } else {
-            stage_x<MTMAX, kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of);
-            wave_stream<F, MTMAX, CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf, rowbuf_s,
-                                                 n_begin + wid, kWavesPerBlock, n_end, a.y, a.ldy, yrow, cnt);
-        }
+        auto run = [&](auto mt_tag) {
+            constexpr int MT = decltype(mt_tag)::value;
+            if constexpr (DIRECT) {
+                constexpr int RW = 64 / direct_group_lanes(F);
+                XStage<F, MT, 1> xst;
+                xst.issue(a.x, a.ldx, cnt, K, row_of);
+                auto between = [&] { xst.commit(xl, xs, a.x, a.ldx, cnt, K, row_of); };
+                // rpc is a multiple of RW, so row groups never straddle chunks; the
+                // workgroup's waves take its groups round robin
+                int next = n_begin / RW + wid;
+                const int gend = (n_end + RW - 1) / RW;
+                auto next_group = [&]() {
+                    const int g = next;
+                    next += kWavesPerBlock;
+                    return g < gend ? g : -1;
+                };
+                wave_stream_direct<F, MT, SP, PF>(mv, n_end, K, xl, xs, next_group, a.y, a.ldy, yrow, cnt, between);
+            } else {
+                auto stage = [&] { stage_x<MT, kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of); };
+                wave_stream<F, MT, CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf, rowbuf_s,
+                                                  n_begin + wid, kWavesPerBlock, n_end, a.y, a.ldy, yrow, cnt, stage);
+            }
+        };
+        if (cnt <= 1 || MTMAX == 1) run(std::integral_constant<int, 1>{});
+        else if (cnt <= 2 || MTMAX == 2) run(std::integral_constant<int, (MTMAX < 2 ? MTMAX : 2)>{});
+        else if (cnt <= 4 || MTMAX == 4) run(std::integral_constant<int, (MTMAX < 4 ? MTMAX : 4)>{});
+        else if (cnt <= 8 || MTMAX == 8) run(std::integral_constant<int, (MTMAX < 8 ? MTMAX : 8)>{});
+        else run(std::integral_constant<int, MTMAX>{});
     }
 }
 
@@ -195,25 +204,21 @@ size_t grouped_workspace_bytes(int64_t E, int64_t M) {
     return (size_t)((ints * 4 + 15) / 16 * 16);
 }
 
-template <int F, int MTMAX, int CPL, int CPLS, int PF>
-static hipError_t launch_grouped_one(const StreamArgs& a, const int32_t* ws, int64_t E, int64_t M, int64_t estride0,
-                                     int64_t estride1, hipStream_t st) {
-    const size_t lds = gemv_lds_bytes(MTMAX, a.K, CPL, CPLS);
-    auto kern = k_grouped<F, MTMAX, CPL, CPLS, PF>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+template <class Kern>
+static hipError_t launch_grouped_one(Kern kern, size_t lds, const StreamArgs& a, const int32_t* ws, int64_t E,
+                                     int64_t M, int64_t estride0, int64_t estride1, hipStream_t st) {
+    int fit = 0;
+    hipError_t e = kernel_residency((const void*)kern, lds, &fit);
+    if (e != hipSuccess) return e;
     // enough (slot, chunk) workgroups to fill the chip even when only a few slots are live
     const int64_t S = ws_slots(E, M);
-    const int64_t target = (int64_t)num_cus() * 4;
+    const int64_t target = (int64_t)num_cus() * fit;
     int64_t nchunks = (target + S - 1) / S;
     const int64_t max_chunks = (a.N + 63) / 64;  // at least 16 rows per wave
     if (nchunks > max_chunks) nchunks = max_chunks;
     if (nchunks < 1) nchunks = 1;
-    const int rpc = (int)((a.N + nchunks - 1) / nchunks);
+    int rpc = (int)((a.N + nchunks - 1) / nchunks);
+    rpc = (rpc + 3) & ~3;  // a multiple of every rows-per-wave (1, 2, 4)
     nchunks = (a.N + rpc - 1) / rpc;
     hipLaunchKernelGGL(kern, dim3((unsigned)(S * nchunks)), dim3(256), lds, st, a, ws, E, M, rpc, (int)nchunks,
                        estride0, estride1);
@@ -221,31 +226,42 @@ static hipError_t launch_grouped_one(const StreamArgs& a, const int32_t* ws, int
 }
 
 template <int F, int MTMAX>
-static hipError_t grouped_cpl(StreamArgs a, const int32_t* ws, int64_t E, int64_t M, int64_t es0, int64_t es1,
-                              hipStream_t st) {
-    const int cpl = choose_cpl(F, a.K);
-    a.seg_blocks = segment_blocks(F, a.K, cpl);
-    const int nb = a.K / BlockGeom<F>::QK;
-    a.nseg = (nb + a.seg_blocks - 1) / a.seg_blocks;
-    constexpr int S = (F == QG_NVFP4) ? 1 : 0;
-    switch (cpl) {
-        case 1: return launch_grouped_one<F, MTMAX, 1, S, 4>(a, ws, E, M, es0, es1, st);
-        case 2: return launch_grouped_one<F, MTMAX, 2, S, 4>(a, ws, E, M, es0, es1, st);
-        case 3: return launch_grouped_one<F, MTMAX, 3, S, 4>(a, ws, E, M, es0, es1, st);
-        case 4: return launch_grouped_one<F, MTMAX, 4, S, 3>(a, ws, E, M, es0, es1, st);
-        default: return launch_grouped_one<F, MTMAX, 6, S, 2>(a, ws, E, M, es0, es1, st);
+static hipError_t grouped_paths(StreamArgs a, const int32_t* ws, int64_t E, int64_t M, int64_t es0, int64_t es1,
+                                hipStream_t st) {
+    if constexpr (F == QG_Q4_K || F == QG_NVFP4) {
+        if (direct_eligible(F, a.K)) {
+            const size_t lds = direct_lds_bytes(F, MTMAX, a.K);
+            constexpr int SP = F == QG_Q4_K ? 1 : 2, PF = 6;
+            return launch_grouped_one(k_grouped<F, MTMAX, true, 1, 0, SP, PF>, lds, a, ws, E, M, es0, es1, st);
+        }
     }
+    if constexpr (F != QG_Q4_K) {
+        const int cpl = choose_cpl(F, a.K);
+        a.seg_blocks = segment_blocks(F, a.K, cpl);
+        const int nb = a.K / BlockGeom<F>::QK;
+        a.nseg = (nb + a.seg_blocks - 1) / a.seg_blocks;
+        constexpr int S = (F == QG_NVFP4) ? 1 : 0;
+        const size_t lds = gemv_lds_bytes(MTMAX, a.K, cpl, S);
+        switch (cpl) {
+            case 1: return launch_grouped_one(k_grouped<F, MTMAX, false, 1, S, 1, 4>, lds, a, ws, E, M, es0, es1, st);
+            case 2: return launch_grouped_one(k_grouped<F, MTMAX, false, 2, S, 1, 4>, lds, a, ws, E, M, es0, es1, st);
+            case 3: return launch_grouped_one(k_grouped<F, MTMAX, false, 3, S, 1, 4>, lds, a, ws, E, M, es0, es1, st);
+            case 4: return launch_grouped_one(k_grouped<F, MTMAX, false, 4, S, 1, 3>, lds, a, ws, E, M, es0, es1, st);
+            default: return launch_grouped_one(k_grouped<F, MTMAX, false, 6, S, 1, 2>, lds, a, ws, E, M, es0, es1, st);
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int F>
 static hipError_t grouped_mt(const StreamArgs& a, int mtmax, const int32_t* ws, int64_t E, int64_t M, int64_t es0,
                              int64_t es1, hipStream_t st) {
     switch (mtmax) {
-        case 1: return grouped_cpl<F, 1>(a, ws, E, M, es0, es1, st);
-        case 2: return grouped_cpl<F, 2>(a, ws, E, M, es0, es1, st);
-        case 4: return grouped_cpl<F, 4>(a, ws, E, M, es0, es1, st);
-        case 8: return grouped_cpl<F, 8>(a, ws, E, M, es0, es1, st);
-        default: return grouped_cpl<F, 16>(a, ws, E, M, es0, es1, st);
+        case 1: return grouped_paths<F, 1>(a, ws, E, M, es0, es1, st);
+        case 2: return grouped_paths<F, 2>(a, ws, E, M, es0, es1, st);
+        case 4: return grouped_paths<F, 4>(a, ws, E, M, es0, es1, st);
+        case 8: return grouped_paths<F, 8>(a, ws, E, M, es0, es1, st);
+        default: return grouped_paths<F, 16>(a, ws, E, M, es0, es1, st);
     }
 }
 
@@ -269,8 +285,7 @@ hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int6
     const int64_t S = ws_slots(E, M);
     int64_t want = 2 * ((M + S - 1) / S);
     int mtmax = want <= 1 ? 1 : want <= 2 ? 2 : want <= 4 ? 4 : want <= 8 ? 8 : 16;
-    const int cpl = choose_cpl(fmt, a.K);
-    while (mtmax > 1 && gemv_lds_bytes(mtmax, a.K, cpl, fmt == QG_NVFP4 ? 1 : 0) > (size_t)kLdsBytes) mtmax >>= 1;
+    while (mtmax > 1 && stream_lds_bytes(fmt, a.K, mtmax) > (size_t)kLdsBytes) mtmax >>= 1;
     switch (fmt) {
         case QG_Q8_0: return grouped_mt<QG_Q8_0>(a, mtmax, ws, E, M, estride0, estride1, st);
         case QG_Q4_K: return grouped_mt<QG_Q4_K>(a, mtmax, ws, E, M, estride0, estride1, st);

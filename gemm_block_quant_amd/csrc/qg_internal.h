@@ -29,6 +29,7 @@ struct StreamArgs {
 
 hipError_t launch_stream_gemm(int fmt, StreamArgs a, hipStream_t st);
 int stream_rows_per_pass(int fmt, int K, int M);
+size_t stream_lds_bytes(int fmt, int K, int mt);
 
 // Grouped-expert product: bucketing + streaming over the distinct experts.
 constexpr int64_t kGroupedMaxRows = 16384;

@@ -289,7 +289,7 @@ __device__ __forceinline__ void stage_x(lds_u8* xl, lds_f32* xs, const uint16_t*
     for (int i = threadIdx.x; i < nvec; i += blockDim.x) {
         const int m = (i * 8) / K, k = (i * 8) % K;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (m < cnt) v = *(const u32x4*)(x + (size_t)row_of(m) * ldx + k);
+        if (m < cnt) v = ld_global128(x + (size_t)row_of(m) * ldx + k);
         *(lds_u32x4*)(xl + (size_t)i * 16) = v;
     }
     if (SUMS) {
@@ -309,20 +309,25 @@ __device__ __forceinline__ void stage_x(lds_u8* xl, lds_f32* xs, const uint16_t*
     __syncthreads();
 }
 
-// One wave streams rows n0, n0 + step, ... (< n_end) of matrix mv against the
-// staged activations; each row is nseg segments of segb blocks.  Lane m < cnt
-// writes y[yrow * ldy + n] for activation row m of the pass.
-template <int F, int MT, int CPL, int CPLS, int PF>
+// One wave streams rows n0, n0 + step, ... (< n_end) of matrix mv through a
+// wave-private LDS row buffer; each row is nseg segments of segb blocks.  Lane
+// m < cnt writes y[yrow * ldy + n] for activation row m.  stage() stages the
+// activations (a workgroup barrier inside): every wave calls it exactly once,
+// after its first PF slots of weight loads are in flight.
+template <int F, int MT, int CPL, int CPLS, int PF, class Stage>
 __device__ __forceinline__ void wave_stream(const MatView& mv, int K, int segb, int nseg, const lds_u8* xl,
                                             const lds_f32* xs, lds_u8* rowbuf, lds_u8* rowbuf_s, int n0, int step,
-                                            int n_end, float* y, int64_t ldy, int64_t yrow, int cnt) {
+                                            int n_end, float* y, int64_t ldy, int64_t yrow, int cnt, Stage stage) {
     constexpr int QK = BlockGeom<F>::QK, BB = BlockGeom<F>::BB;
     constexpr int CS = CPLS > 0 ? CPLS : 1;
     const int lane = threadIdx.x & 63;
     const int nb = K / QK;
     const int nrows = n0 < n_end ? (n_end - 1 - n0) / step + 1 : 0;
     const int nitems = nrows * nseg;
-    if (nitems == 0) return;
+    if (nitems == 0) {
+        stage();
+        return;
+    }
 
     float gscale = 1.f;
     if (F == QG_NVFP4) {
@@ -335,24 +340,20 @@ __device__ __forceinline__ void wave_stream(const MatView& mv, int K, int segb, 
     u32x4 R[PF][CPL];
     u32x4 RS[PF][CS];
 
-    auto item_geom = [&](int t, int& n, int& s, int& b0, int& b1) {
-        n = n0 + (t / nseg) * step;
-        s = t % nseg;
-        b0 = s * segb;
-        b1 = min(nb, b0 + segb);
-    };
-    // Loads of item t into one ring slot.  Every lane loads CPL (+CPLS) aligned
-    // 16-byte granules; each holds at least one byte of the tensor, so no load
-    // leaves the tensor's pages.  Items past the end load one shared granule
-    // so that every path issues the same number of loads.
-    auto issue = [&](int t, u32x4 (&r)[CPL], u32x4 (&rs)[CS]) {
-        const bool live = t < nitems;
-        int n, s, b0, b1;
-        item_geom(live ? t : 0, n, s, b0, b1);
+    // Loads of one item (row, segment) into a ring slot.  Every lane loads CPL
+    // (+CPLS) aligned 16-byte granules; each holds at least one byte of the
+    // tensor, so no load leaves the tensor's pages.  Items past the end reload
+    // the first granule of row n0 so that every path issues the same loads.
+    int in_ = n0, is_ = 0, it_ = 0;
+    auto issue = [&](u32x4 (&r)[CPL], u32x4 (&rs)[CS]) {
+        const bool live = it_ < nitems;
+        const int n = live ? in_ : n0;
+        const int b0 = live ? is_ * segb : 0;
+        const int b1 = live ? min(nb, b0 + segb) : 1;
         const uint8_t* beg = mv.w0 + (size_t)n * mv.rb0 + (size_t)b0 * BB;
         const uint8_t* end = mv.w0 + (size_t)n * mv.rb0 + (size_t)b1 * BB;
         const uint8_t* b16 = (const uint8_t*)((uintptr_t)beg & ~(uintptr_t)15);
-        const int nch = live ? (int)((end - b16 + 15) >> 4) : 1;
+        const int nch = (int)((end - b16 + 15) >> 4);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             const int idx = lane + 64 * c;
@@ -362,12 +363,17 @@ __device__ __forceinline__ void wave_stream(const MatView& mv, int K, int segb, 
             const uint8_t* sbeg = mv.w1 + (size_t)n * mv.rb1 + b0;
             const uint8_t* send = mv.w1 + (size_t)n * mv.rb1 + b1;
             const uint8_t* s16 = (const uint8_t*)((uintptr_t)sbeg & ~(uintptr_t)15);
-            const int nchs = live ? (int)((send - s16 + 15) >> 4) : 1;
+            const int nchs = (int)((send - s16 + 15) >> 4);
 #pragma unroll
             for (int c = 0; c < CPLS; ++c) {
                 const int idx = lane + 64 * c;
                 rs[c] = ld_stream128(s16 + 16 * (idx < nchs ? idx : 0));
             }
+        }
+        ++it_;
+        if (++is_ == nseg) {
+            is_ = 0;
+            in_ += step;
         }
     };
 
@@ -375,9 +381,9 @@ __device__ __forceinline__ void wave_stream(const MatView& mv, int K, int segb, 
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.f;
 
-    auto process = [&](int t, const u32x4 (&r)[CPL], const u32x4 (&rs)[CS]) {
-        int n, s, b0, b1;
-        item_geom(t, n, s, b0, b1);
+    int pn_ = n0, ps_ = 0;
+    auto process = [&](const u32x4 (&r)[CPL], const u32x4 (&rs)[CS]) {
+        const int b0 = ps_ * segb, b1 = min(nb, b0 + segb);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) *(lds_u32x4*)(rowbuf + 16 * (lane + 64 * c)) = r[c];
         if (CPLS > 0) {
@@ -385,10 +391,10 @@ __device__ __forceinline__ void wave_stream(const MatView& mv, int K, int segb, 
             for (int c = 0; c < CPLS; ++c) *(lds_u32x4*)(rowbuf_s + 16 * (lane + 64 * c)) = rs[c];
         }
         DecodeCtx dc;
-        const uintptr_t beg = (uintptr_t)(mv.w0 + (size_t)n * mv.rb0 + (size_t)b0 * BB);
+        const uintptr_t beg = (uintptr_t)(mv.w0 + (size_t)pn_ * mv.rb0 + (size_t)b0 * BB);
         dc.seg = rowbuf + (beg & 15);
         if (CPLS > 0) {
-            const uintptr_t sbeg = (uintptr_t)(mv.w1 + (size_t)n * mv.rb1 + b0);
+            const uintptr_t sbeg = (uintptr_t)(mv.w1 + (size_t)pn_ * mv.rb1 + b0);
             dc.segs = rowbuf_s + (sbeg & 15);
         } else {
             dc.segs = rowbuf_s;
@@ -409,7 +415,7 @@ __device__ __forceinline__ void wave_stream(const MatView& mv, int K, int segb, 
                 else unit_q8_0<MT>(dc, u, acc);
             }
         }
-        if (s == nseg - 1) {
+        if (++ps_ == nseg) {
             float mine = 0.f;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
@@ -418,24 +424,27 @@ __device__ __forceinline__ void wave_stream(const MatView& mv, int K, int segb, 
                 acc[m] = 0.f;
             }
             if (F == QG_NVFP4) mine *= gscale;
-            if (lane < cnt) y[yrow * ldy + n] = mine;
+            if (lane < cnt) st_global_f32(y + yrow * ldy + pn_, mine);
+            ps_ = 0;
+            pn_ += step;
         }
     };
 
-    // fill the ring, then: land slot, refill it PF items ahead, decode
+    // fill the ring, stage the activations, then: land a slot, refill it PF items ahead
 #pragma unroll
-    for (int sl = 0; sl < PF; ++sl) issue(sl, R[sl], RS[sl]);
+    for (int sl = 0; sl < PF; ++sl) issue(R[sl], RS[sl]);
+    stage();
     const int nfull = nitems - nitems % PF;
     for (int t0 = 0; t0 < nfull; t0 += PF) {
 #pragma unroll
         for (int sl = 0; sl < PF; ++sl) {
-            process(t0 + sl, R[sl], RS[sl]);
-            issue(t0 + sl + PF, R[sl], RS[sl]);
+            process(R[sl], RS[sl]);
+            issue(R[sl], RS[sl]);
         }
     }
 #pragma unroll
     for (int sl = 0; sl < PF; ++sl)
-        if (nfull + sl < nitems) process(nfull + sl, R[sl], RS[sl]);
+        if (nfull + sl < nitems) process(R[sl], RS[sl]);
 }
 
 // ------------------------------------------------------------------ host-side geometry
@@ -460,6 +469,11 @@ inline int segment_blocks(int fmt, int K, int cpl) {
     if (fmt == QG_NVFP4) sb &= ~1;  // units span 2 blocks
     return sb < nb ? sb : nb;
 }
+
+// Workgroups of `block` threads with `lds` bytes of dynamic LDS that one CU holds
+// at once for kernel `fn` (at least 1).  The first call per kernel also lifts
+// the kernel's dynamic-LDS limit to 160 KB.  Cached per (kernel, lds).
+hipError_t kernel_residency(const void* fn, size_t lds, int* per_cu, int block = 256);
 
 inline int num_cus() {
     static int n = 0;
