@@ -67,6 +67,18 @@ qg_status from_hip(hipError_t e) { return e == hipSuccess ? QG_OK : QG_EHIP; }
 
 namespace qg {
 
+int num_cus() {
+    static int n = 0;
+    if (!n) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        n = v;
+    }
+    return n;
+}
+
 hipError_t kernel_residency(const void* fn, size_t lds, int* per_cu, int block) {
     static std::mutex mu;
     static std::unordered_map<const void*, std::unordered_map<size_t, int>> cache;  // per kernel, per LDS size
@@ -126,9 +138,16 @@ qg_status quant_gemm(const void* w, qg_format fmt, int64_t N, int64_t K, int64_t
     if (M == 0 || N == 0) return QG_OK;
     if (!w || !x || !y) return QG_EINVAL;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
+    StreamArgs a = stream_args(w, fmt, 1, 0, N, K);
+    if (fmt == QG_NVFP4 && M >= kMfmaMinRows) {
+        if (M > INT32_MAX) return QG_ESHAPE;
+        return launch_mfma_nvfp4(a.w0, a.w1, a.gbytes, (int)N, (int)K, x, K, (int)M, y, N, (hipStream_t)stream) ==
+                       hipSuccess
+                   ? QG_OK
+                   : QG_EHIP;
+    }
     const int rows = stream_rows_per_pass(fmt, (int)K, (int)(M < 16 ? M : 16));
     if (rows <= 0) return QG_ESHAPE;
-    StreamArgs a = stream_args(w, fmt, 1, 0, N, K);
     a.x = x;
     a.ldx = K;
     a.y = y;

@@ -115,13 +115,13 @@ static hipError_t dispatch_direct(const StreamArgs& a, hipStream_t st) {
     const size_t lds = 16 + direct_lds_bytes(F, MT, a.K);
     auto kern = k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF>;
     int fit = 0;
-    hipError_t e = kernel_residency((const void*)kern, lds, &fit, 1024);
+    hipError_t e = kernel_residency((const void*)kern, lds, &fit, kDirectWaves * 64);
     if (e != hipSuccess) return e;
     constexpr int RW = 64 / Direct<F>::G;
     const long groups = (a.N + RW - 1) / RW;
     long grid = (long)num_cus() * fit;
     if (grid > groups) grid = groups;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(1024), lds, st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kDirectWaves * 64), lds, st, a);
     return hipGetLastError();
 }
 

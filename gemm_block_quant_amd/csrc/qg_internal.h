@@ -37,6 +37,12 @@ size_t grouped_workspace_bytes(int64_t E, int64_t M);
 hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int64_t E, int64_t M, int32_t* ws,
                           int64_t estride0, int64_t estride1, hipStream_t st);
 
+// NVFP4 product for M >= kMfmaMinRows on the bf16 matrix cores.
+constexpr int kMfmaMinRows = 32;
+hipError_t launch_mfma_nvfp4(const uint8_t* codes, const uint8_t* scales, const uint8_t* gbytes, int N, int K,
+                             const uint16_t* x, int64_t ldx, int M, float* y, int64_t ldy, hipStream_t st);
+int num_cus();
+
 // Dequantization of rows [0, rows) to fp32.
 hipError_t launch_dequant(int fmt, const uint8_t* w, int64_t E, int64_t N, int64_t K, float* out, hipStream_t st);
 

@@ -1,0 +1,194 @@
+// qg_mfma.hip -- NVFP4 product for M >= 32 activation rows on the bf16 matrix
+// cores (v_mfma_f32_32x32x16_bf16).
+//
+// With many activation rows the product is a dense contraction, so weights are
+// decoded once per workgroup tile and used by every activation row of the tile
+// ("I Built a Custom Blackwell Kernel for Qwen3.8-27B", section "What the
+// custom path actually does": E2M1 codes, one E4M3 scale per 16 values, one
+// fp32 scale per tensor).  An E2M1 value has at most 2 significant bits and an
+// E4M3 scale at most 4, so their product is exact in bf16 (8 bits): the tile
+// holds bf16(c * s) with no rounding, the matrix cores form exact fp32
+// products with the bf16 activations and accumulate in fp32, and the tensor
+// scale g multiplies the fp32 sum once per output.
+//
+// Tiling: a 256-thread workgroup computes a BM x BN tile of y (activation rows
+// x weight rows); its four waves each own a (BM/2) x (BN/2) quarter as
+// (BM/64) x (BN/64) 32x32 accumulators.  K advances 32 values (two NVFP4
+// blocks) per step through two LDS buffers: while the matrix cores work on
+// one, the next step's activations and codes are in flight from memory and
+// are then decoded into the other.
+#include "qg_internal.h"
+
+namespace qg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kMfmaKStep = 32;
+constexpr int kMfmaRowBytes = 80;  // one tile row: 32 bf16 (64 B) + 16 B padding (conflict-free fragment reads)
+constexpr int kMfmaThreads = 256;
+
+__device__ __forceinline__ uint32_t bf16_pair_from_exact(float lo, float hi) {
+    // lo, hi are exact in bf16: their top 16 bits are the bf16 encodings.
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+}
+
+// 16 NVFP4 values (8 code bytes c0, c1; E4M3 scale s) -> 8 dwords of bf16
+// pairs bf16(e2m1 * s), value order k = 0..15.
+__device__ __forceinline__ void decode_nvfp4_block_bf16(uint32_t c0, uint32_t c1, float s, uint32_t (&o)[8]) {
+    auto pair = [&](uint32_t c, int sel) -> uint32_t {
+        f32x2 v;
+        switch (sel) {
+            case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0); break;
+            case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1); break;
+            case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2); break;
+            default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3); break;
+        }
+        const float lo = v.x * s, hi = v.y * s;
+        return bf16_pair_from_exact(lo, hi);
+    };
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        o[b] = pair(c0, b);
+        o[4 + b] = pair(c1, b);
+    }
+}
+
+struct MfmaArgs {
+    const uint16_t* x;  // bf16 [M, K], row stride ldx
+    int64_t ldx;
+    const uint8_t* codes;   // E2M1 plane, K/2 bytes per row
+    const uint8_t* scales;  // E4M3 plane, K/16 bytes per row
+    const uint8_t* gbytes;  // fp32 tensor scale (any alignment)
+    float* y;               // fp32 [M, N], row stride ldy
+    int64_t ldy;
+    int M, N, K;
+};
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kMfmaThreads) void k_mfma_nvfp4(const MfmaArgs a) {
+    constexpr int FM = BM / 64, FN = BN / 64;          // 32x32 fragments per wave
+    constexpr int XCH = BM * 4 / kMfmaThreads;         // 16-byte activation chunks per thread per step
+    constexpr int TILE_X = BM * kMfmaRowBytes, TILE_W = BN * kMfmaRowBytes;
+    __shared__ __attribute__((aligned(16))) uint8_t smem_generic[2 * (TILE_X + TILE_W)];
+    lds_u8* smem = (lds_u8*)smem_generic;
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int wm = (wid >> 1) * (BM / 2), wn = (wid & 1) * (BN / 2);
+    const int K = a.K, M = a.M, N = a.N;
+    const int nsteps = (K + kMfmaKStep - 1) / kMfmaKStep;
+    const int64_t crow = K / 2, srow = K / 16;
+
+    // Per-thread staging of one step: activation chunks and one NVFP4 block.
+    u32x4 xr[XCH];
+    uint32_t wc0 = 0, wc1 = 0, wsb = 0;
+    const int wr = tid >> 1, wh = tid & 1;  // weight tile row and block half owned by this thread
+    const bool w_owner = tid < BN * 2;
+
+    auto load = [&](int s) {
+        const int k0 = s * kMfmaKStep;
+#pragma unroll
+        for (int c = 0; c < XCH; ++c) {
+            const int i = tid + c * kMfmaThreads;
+            const int r = i >> 2, q = i & 3;
+            const int m = m0 + r, k = k0 + q * 8;
+            xr[c] = u32x4{0u, 0u, 0u, 0u};
+            if (m < M && k < K) xr[c] = ld_global128(a.x + (size_t)m * a.ldx + k);
+        }
+        wc0 = wc1 = wsb = 0;
+        const int n = n0 + wr, kb = k0 + wh * 16;
+        if (w_owner && n < N && kb < K) {
+            const u32x2 c = *(const QG_GLOBAL u32x2*)(uintptr_t)(a.codes + (size_t)n * crow + kb / 2);
+            wc0 = c.x;
+            wc1 = c.y;
+            wsb = *(const QG_GLOBAL uint8_t*)(uintptr_t)(a.scales + (size_t)n * srow + kb / 16);
+        }
+    };
+    auto store = [&](int buf) {
+        lds_u8* tx = smem + buf * (TILE_X + TILE_W);
+        lds_u8* tw = tx + TILE_X;
+#pragma unroll
+        for (int c = 0; c < XCH; ++c) {
+            const int i = tid + c * kMfmaThreads;
+            *(lds_u32x4*)(tx + (i >> 2) * kMfmaRowBytes + (i & 3) * 16) = xr[c];
+        }
+        if (w_owner) {
+            uint32_t o[8];
+            decode_nvfp4_block_bf16(wc0, wc1, e4m3_to_f32<0>(wsb), o);
+            lds_u8* p = tw + wr * kMfmaRowBytes + wh * 32;
+            *(lds_u32x4*)p = u32x4{o[0], o[1], o[2], o[3]};
+            *(lds_u32x4*)(p + 16) = u32x4{o[4], o[5], o[6], o[7]};
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+    load(0);
+    store(0);
+    __syncthreads();
+    const int frow = lane & 31, fcol = (lane >> 5) * 16;
+    for (int s = 0; s < nsteps; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nsteps) load(s + 1);
+        const lds_u8* tx = smem + buf * (TILE_X + TILE_W);
+        const lds_u8* tw = tx + TILE_X;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8_t fa[FM], fb[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                fa[i] = __builtin_bit_cast(bf16x8_t, lds_ld128(tx + (wm + 32 * i + frow) * kMfmaRowBytes + kk * 32 + fcol));
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                fb[j] = __builtin_bit_cast(bf16x8_t, lds_ld128(tw + (wn + 32 * j + frow) * kMfmaRowBytes + kk * 32 + fcol));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+        if (s + 1 < nsteps) store(buf ^ 1);
+        __syncthreads();
+    }
+
+    const uint8_t* gb = a.gbytes;
+    const uint32_t gbits = (uint32_t)gb[0] | ((uint32_t)gb[1] << 8) | ((uint32_t)gb[2] << 16) | ((uint32_t)gb[3] << 24);
+    const float g = __builtin_bit_cast(float, gbits);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int n = n0 + wn + 32 * j + (lane & 31);
+                if (m < M && n < N) st_global_f32(a.y + (size_t)m * a.ldy + n, g * acc[i][j][r]);
+            }
+}
+
+// Tile shape: the largest whose tile count still gives every CU at least two
+// workgroups, else the smallest.
+hipError_t launch_mfma_nvfp4(const uint8_t* codes, const uint8_t* scales, const uint8_t* gbytes, int N, int K,
+                             const uint16_t* x, int64_t ldx, int M, float* y, int64_t ldy, hipStream_t st) {
+    MfmaArgs a = {x, ldx, codes, scales, gbytes, y, ldy, M, N, K};
+    const long cus = num_cus();
+    auto tiles = [&](int bm, int bn) { return (long)((N + bn - 1) / bn) * ((M + bm - 1) / bm); };
+    if (tiles(128, 128) >= 2 * cus) {
+        dim3 grid((N + 127) / 128, (M + 127) / 128);
+        hipLaunchKernelGGL((k_mfma_nvfp4<128, 128>), grid, dim3(kMfmaThreads), 0, st, a);
+    } else if (tiles(128, 64) >= cus) {
+        dim3 grid((N + 63) / 64, (M + 127) / 128);
+        hipLaunchKernelGGL((k_mfma_nvfp4<128, 64>), grid, dim3(kMfmaThreads), 0, st, a);
+    } else {
+        dim3 grid((N + 63) / 64, (M + 63) / 64);
+        hipLaunchKernelGGL((k_mfma_nvfp4<64, 64>), grid, dim3(kMfmaThreads), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace qg

@@ -475,15 +475,5 @@ inline int segment_blocks(int fmt, int K, int cpl) {
 // the kernel's dynamic-LDS limit to 160 KB.  Cached per (kernel, lds).
 hipError_t kernel_residency(const void* fn, size_t lds, int* per_cu, int block = 256);
 
-inline int num_cus() {
-    static int n = 0;
-    if (!n) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-    }
-    return n;
-}
 
 }  // namespace qg

@@ -81,6 +81,9 @@ PRODUCT_CASES = [
     (qg.Q6_K, 99, 17408, 8), (qg.Q6_K, 333, 5120, 33),
     (qg.NVFP4, 1, 16, 1), (qg.NVFP4, 3, 48, 2), (qg.NVFP4, 1000, 5120, 1), (qg.NVFP4, 100, 17408, 1),
     (qg.NVFP4, 77, 592, 8), (qg.NVFP4, 200, 5120, 16), (qg.NVFP4, 51, 17408, 8),
+    # matrix-core path (NVFP4, M >= 32): ragged M and N tiles, K % 32 == 16 (half step)
+    (qg.NVFP4, 200, 5120, 37), (qg.NVFP4, 130, 48, 33), (qg.NVFP4, 300, 1040, 130), (qg.NVFP4, 1000, 512, 64),
+    (qg.NVFP4, 64, 16, 32),
 ]
 
 
@@ -132,6 +135,7 @@ FULL = [
     (qg.Q6_K, 248320, 5120, 1), (qg.Q6_K, 248320, 5120, 8),
     (qg.NVFP4, 17408, 5120, 1), (qg.NVFP4, 17408, 5120, 8),
     (qg.NVFP4, 5120, 17408, 1), (qg.NVFP4, 5120, 17408, 8),
+    (qg.NVFP4, 17408, 5120, 512), (qg.NVFP4, 5120, 17408, 512),
 ]
 
 
@@ -147,3 +151,17 @@ def test_full_size_sampled(fmt, N, K, M):
                                      np.random.default_rng(seed).integers(0, N, 240)]))
     y_ref, bound = oracle.gemm(fmt, w, N, K, x, cols=cols)
     assert_band(y[:, cols], y_ref, bound, "full fmt %d N %d K %d M %d" % (fmt, N, K, M))
+
+
+def test_mfma_rows_independent_of_tiling_and_repeat():
+    """NVFP4 with M >= 32: each output is one fixed fp32 accumulation over K, so
+    the rows of a 37-row call equal those rows of a 512-row call (other tile
+    shapes and grid) bit for bit, and runs repeat."""
+    fmt, N, K = qg.NVFP4, 1000, 1040
+    w, x = make_case(fmt, N, K, 512, seed=77)
+    wd, xd = dev_bytes(w), dev_x(x)
+    y512 = qg.quant_gemm(wd, fmt, N, K, 512, xd).cpu().numpy()
+    y37 = qg.quant_gemm(wd, fmt, N, K, 37, xd[:37].contiguous()).cpu().numpy()
+    assert same_bits(y37, y512[:37])
+    again = qg.quant_gemm(wd, fmt, N, K, 512, xd).cpu().numpy()
+    assert same_bits(again, y512)
