@@ -31,6 +31,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 TOKEN_BYTES_GB = 16.39         # per-token weight read of the 27B Q4_K_M artifact, embedding gather excluded
 ROTATE_BYTES = 1 << 30
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
+COPY_ELEMS = 64 << 20  # fp32 elements of the calibration copy: 256 MiB read, 256 MiB written
 
 
 def log(*a):
@@ -122,50 +125,146 @@ class Prepared:
 
 
 def time_workload(p: Prepared, steps: int, warmup: int):
-    """(seconds for `steps` calls, mean per-launch kernel seconds from events around each launch)."""
+    """Two timed regions of `steps` calls on the launch stream (torch's current stream).
+
+    The first has events only at its two ends: the whole-job time.  The second
+    brackets every launch with its own event pair: the mean and median launch
+    duration of the kernel(s) of one call.  (Events between launches add a few
+    microseconds per call, so they stay out of the first region.)"""
     import torch
     for i in range(warmup):
         p.call(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_start.record()
+    for i in range(steps):
+        p.call(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    total = t_start.elapsed_time(t_end) / 1e3
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
         ev[i][0].record()
         p.call(i)
         ev[i][1].record()
-    t_end.record()
     torch.cuda.synchronize()
-    total = t_start.elapsed_time(t_end) / 1e3
     per = [a.elapsed_time(b) / 1e3 for a, b in ev]
     return total, float(np.mean(per)), float(np.median(per))
 
 
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: HBM-traffic figures taken from counters are only
+    reported while the kernels they were taken on are unchanged."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "gemm_block_quant_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(key: str):
+    """Calibrated HBM bytes per call (fetched + written) from profiles/traffic.json, or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return int(d["fetch_bytes"] + d["write_bytes"])
+
+
+def copy_calibration():
+    """A plain elementwise pass of known traffic (torch.neg over 256 MiB of fp32,
+    into a second 256 MiB buffer), five times: the reference the FETCH_SIZE /
+    WRITE_SIZE counters are scaled by."""
+    import torch
+    src = torch.ones(COPY_ELEMS, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def _counter_means(out_dir: str, counter: str):
+    """{kernel name: mean counter value per dispatch} from rocprofv3 counter CSVs under out_dir."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(out_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] == counter:
+                    vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, key: str, fetch_cmd: str, write_cmd: str):
+    """Turn a FETCH_SIZE run and a WRITE_SIZE run (each over bench.py --calibrate-copy)
+    into calibrated bytes per call, stored under `key` in profiles/traffic.json."""
+    out = {"source_hash": kernel_source_hash(), "fetch_command": fetch_cmd, "write_command": write_cmd,
+           "copy_bytes_each_way": COPY_ELEMS * 4}
+    for name, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        means = _counter_means(d, counter)
+        ours = {k: v for k, v in means.items() if "qg::" in k}
+        copy = [v for k, v in means.items() if "neg" in k.lower() and "qg::" not in k]
+        if not ours or not copy:
+            raise SystemExit("pmc summary: no %s rows for %s in %s" % (counter, "our kernels" if not ours else "the copy", d))
+        factor = COPY_ELEMS * 4 / (copy[0] * 1024)
+        per_call_kib = sum(ours.values())
+        out[name + "_kib_per_call_raw"] = round(per_call_kib, 3)
+        out[name + "_copy_kib_raw"] = round(copy[0], 3)
+        out[name + "_factor"] = round(factor, 5)
+        out[name + "_bytes"] = int(round(per_call_kib * 1024 * factor))
+        out[name + "_kernels"] = {k: round(v, 3) for k, v in ours.items()}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            allt = json.load(f)
+    except (OSError, ValueError):
+        allt = {}
+    allt[key] = out
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(allt, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def cpu_baseline(p: Prepared, target_s: float = 12.0):
-    """The oracle (as it stands) on a bounded sample of output rows of the same workload."""
+    """The oracle (as it stands) on a bounded sample of the same workload: the first
+    output rows, doubling until one pass takes about target_s; when the whole
+    matrix takes less, whole passes are repeated until target_s has elapsed."""
     import oracle
     wl = p.wl
     nthreads = oracle.max_threads()
+    ids = p.ids_host if wl.moe else None
     rows_try = 64
     while True:
         cols = np.arange(min(rows_try, wl.N))
         t0 = time.time()
-        oracle.gemm(wl.fmt, p.w_host, wl.N, wl.K, p.x_host, E=wl.E, cols=cols,
-                    ids=p.ids_host if wl.moe else None)
+        oracle.gemm(wl.fmt, p.w_host, wl.N, wl.K, p.x_host, E=wl.E, cols=cols, ids=ids)
         dt = time.time() - t0
         if dt >= target_s or rows_try >= wl.N:
             break
         rows_try = int(min(wl.N, max(rows_try * 2, rows_try * target_s / max(dt, 1e-3) * 1.05)))
-    import gemm_block_quant_amd as qg
-    if wl.moe:
-        sample_bytes = len(cols) * wl.M * qg.quant_packed_bytes(wl.fmt, 1, 1, wl.K)
-    else:
-        sample_bytes = len(cols) * qg.quant_packed_bytes(wl.fmt, 1, 1, wl.K)
-    return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
-            "sample": "%d of %d output rows x M=%d (%.1f MB of packed weights) in %.2f s, %d threads"
-                      % (len(cols), wl.N, wl.M, sample_bytes / 1e6, dt, nthreads)}
+    passes = 1
+    if dt < target_s:
+        t0 = time.time()
+        passes = 0
+        while time.time() - t0 < target_s:
+            oracle.gemm(wl.fmt, p.w_host, wl.N, wl.K, p.x_host, E=wl.E, cols=cols, ids=ids)
+            passes += 1
+        dt = time.time() - t0
+    # the workload's weight bytes in proportion to the outputs computed (same unit as the GPU figure)
+    pass_bytes = p.bytes_per_call * len(cols) / wl.N
+    return {"value": round(pass_bytes * passes / dt / 1e9, 4), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": "%d of %d output rows x M=%d (%.1f MB of packed weights per pass), %d pass(es) in %.2f s, "
+                      "%d threads" % (len(cols), wl.N, wl.M, pass_bytes / 1e6, passes, dt, nthreads)}
 
 
 def result_for(p: Prepared, steps: int, warmup: int):
@@ -198,7 +297,15 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time every workload shape (sweep)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep-out", default=None, help="write the sweep as JSON lines to this file")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed regions, run the known-size copy the HBM counters are scaled by")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json")
+    ap.add_argument("--pmc-commands", nargs=2, default=("", ""), help="the two commands, recorded with the summary")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, *args.pmc_commands)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -234,6 +341,8 @@ def main():
             with open(args.sweep_out, "w") as f:
                 for s in sweep:
                     f.write(json.dumps(s) + "\n")
+    if args.calibrate_copy:
+        copy_calibration()
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(p)
@@ -257,7 +366,7 @@ def main():
                    "N": wl.N, "K": wl.K, "weight_bytes": p.bytes_per_call, "rotated_copies": p.copies,
                    "implied_tok_s": r["implied_tok_s"], "pct_hbm_peak_whole_job": round(100 * value / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(args.workload)},
         "cpu_baseline": cpu,
     }
     if sweep:

@@ -26,8 +26,11 @@
  *  - Arguments are validated on the host before anything is launched.  On
  *    failure a non-zero qg_status is returned and nothing is enqueued.  A
  *    failed launch returns QG_EHIP.  No C++ exception crosses this ABI.
- *  - Alignment: w 16 bytes, x 4 bytes, y / out 4 bytes, ids 4 bytes,
+ *  - Alignment: w 16 bytes, x 16 bytes, y / out 4 bytes, ids 4 bytes,
  *    workspace 16 bytes (QG_EALIGN otherwise).
+ *  - Weight reads are whole aligned 16-byte granules: the last granule of a
+ *    weight plane may be read past the plane's final byte (never past the
+ *    granule, so never onto another page); those bytes are not used.
  *  - Shapes: N, M, E >= 0; K > 0 and a multiple of the format's block
  *    (QG_ESHAPE otherwise).  M == 0 or N == 0 is a valid no-op.
  *
@@ -57,7 +60,9 @@
  * (one rounding at most, round to nearest even).  Products accumulate in fp32
  * in a fixed order: results are deterministic run to run, row m of any
  * quant_gemm call with M <= 16 is bitwise equal to quant_gemv on x[m], and
- * quant_gemm is bitwise equal to quant_grouped_gemm with E = 1 and ids = NULL.
+ * such a call is bitwise equal to quant_grouped_gemm with E = 1 and ids =
+ * NULL.  QG_NVFP4 with M >= 32 accumulates on the matrix cores in another
+ * (still fixed) order: its rows do not depend on M or on the other rows.
  */
 #ifndef QUANTGEMM_H
 #define QUANTGEMM_H
