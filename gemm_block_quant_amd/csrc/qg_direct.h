@@ -1,52 +1,77 @@
 // qg_direct.h -- register-direct weight streaming for the 16-byte aligned
-// formats (Q4_K, and NVFP4 with K a multiple of 32).
+// formats (Q4_K, and NVFP4 with K a multiple of 32), with the products formed
+// on the matrix cores by the 16-block 4x4x4 bf16 MFMA.
 //
-// A wave works on 64/G rows at once, G lanes per row.  Every lane loads its
-// own decode unit straight into registers: Q4_K one quarter of a super-block
-// (32 code bytes = 64 values, sub-blocks 2g and 2g+1) plus the block's 16-byte
-// header; NVFP4 16 code bytes (32 values) plus their two E4M3 scales.  Across
-// the G lanes of a row these loads cover a contiguous stretch of the row, so
-// the stream stays coalesced and the weights never pass through LDS.  Unit
-// u of a row sits on lane u % G in pass u / G, so every constant derived from
-// a lane's place inside a block is fixed for the whole kernel, and the per-row
-// summation order depends only on (format, K).
+// A wave works on 4 weight rows at once.  Lane l serves row j = l % 4 and
+// unit slot b = l / 4 (16 slots): in pass p it loads unit u = 16 p + b of its
+// row straight into registers -- Q4_K one quarter of a super-block (32 code
+// bytes = 64 values of two sub-blocks) plus the block's 16-byte header; NVFP4
+// 16 code bytes (32 values = two blocks) plus their two E4M3 scales.  The 16
+// lanes of a row cover a contiguous stretch of it, so the stream stays
+// coalesced and the weights never pass through LDS.
 //
-// Activations live in LDS with 16 bytes of padding after each unit's span of
-// values, so the G lanes of a row read them without bank conflicts; the lanes
-// of the other rows of the wave read the same addresses (a broadcast).
+// v_mfma_f32_4x4x4_16b_bf16 computes 16 independent products
+// D[b] = A[b] (4 x 4) * B[b] (4 x 4): lane l supplies row l % 4 of A[b] and
+// column l % 4 of B[b] (4 values along k each) and receives column l % 4 of
+// D[b] (4 values).  Here block b is unit slot b, B[b] holds 4 decoded weights
+// of each of the 4 rows (exact bf16: 128 + q for Q4_K, e2m1 for NVFP4), and
+// A[b] holds the activations of up to 4 activation rows at the same 4
+// positions.  So one instruction forms, for every lane, the partial dot
+// products of its own weight row with 4 activation rows, and a lane's decoded
+// codes serve every activation row without further VALU work.  Eight (Q4_K) or
+// four (NVFP4) instructions accumulate one scale block; the lane then applies
+// that block's scale to its 4 results in fp32.
+//
+// Every output element therefore has one fixed arithmetic: the matrix-core
+// sum over each 4-value group, fixed accumulation order over a scale block,
+// fixed fp32 scaling order, and a fixed xor-butterfly over the unit slots.
+// Nothing depends on how many activation rows share the call, so row m of an
+// M-row call is bitwise the M = 1 result ("Qwen3.8-27B on one Tenstorrent
+// P150", section "8. Quality, then a better quant": verify rows must round
+// exactly like single-token decode).
+//
+// Activations live in LDS interleaved for the A operand: for each unit, 16
+// bytes (8 values) per (position group, activation row), the position groups
+// of unit u rotated by u % 4 so that the four slots of a 16-lane row read
+// different banks.
 #pragma once
 
 #include "qg_stream.h"
 
 namespace qg {
 
-// Lane-group reductions with DPP (the groups are 16-lane DPP rows); the
-// result lands in every lane of the group.
-__device__ __forceinline__ float dpp_sum16(float v) {
-    auto add = [](float x, int ctrl) {
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// D += A * B on the 16-block 4x4x4 bf16 MFMA.  a, b: 4 bf16 values each (two
+// dwords, value order = k order).
+__device__ __forceinline__ f32x4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4_t c) {
+    const i16x4_t a = __builtin_bit_cast(i16x4_t, u32x2{a0, a1});
+    const i16x4_t b = __builtin_bit_cast(i16x4_t, u32x2{b0, b1});
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Sum over the 16 unit slots of a lane's row (lanes l, l ^ 4, l ^ 8, ...):
+// an xor butterfly, so every lane of the row ends with the same bits.
+__device__ __forceinline__ float slot_sum(float v) {
+    auto swz = [](float x, int pattern) -> float {
         int y;
-        switch (ctrl) {
-            case 0: y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false); break;
-            case 1: y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false); break;
-            case 2: y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false); break;
-            default: y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false); break;
+        switch (pattern) {
+            case 4: y = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), (4 << 10) | 0x1F); break;
+            case 8: y = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), (8 << 10) | 0x1F); break;
+            default: y = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), (16 << 10) | 0x1F); break;
         }
-        return x + __builtin_bit_cast(float, y);
+        return __builtin_bit_cast(float, y);
     };
-    v = add(v, 0);  // quad_perm [1,0,3,2]: pairs
-    v = add(v, 1);  // quad_perm [2,3,0,1]: quads
-    v = add(v, 2);  // row_half_mirror: 8 lanes
-    v = add(v, 3);  // row_mirror: 16 lanes
+    v += swz(v, 4);
+    v += swz(v, 8);
+    v += swz(v, 16);
+    v += __shfl_xor(v, 32, kWave);
     return v;
 }
 
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-    v = dpp_sum16(v);
-    if (G >= 32) v += __shfl_xor(v, 16, kWave);
-    if (G >= 64) v += __shfl_xor(v, 32, kWave);
-    return v;
-}
+constexpr int kDirectRows = 4;    // weight rows per wave at a time
+constexpr int kDirectSlots = 16;  // unit slots per row per pass
 
 template <int F> struct Direct;
 
@@ -56,8 +81,7 @@ template <int F> struct Direct;
 // sum w x = a0 (D0 - 128 X0) - dmin m0 X0 + a1 (...) with a = d * sc,
 // D = sum (128 + q) x and X = sum x over the sub-block.
 template <> struct Direct<QG_Q4_K> {
-    static constexpr int G = 16;    // lanes per row
-    static constexpr int XG = 64;   // activation values per unit (padding granule)
+    static constexpr int UV = 64;  // activation values per unit
     static constexpr int REGS = 12;
     static constexpr bool SUMS = true;
     // 6-bit scale and min of sub-blocks 2g and 2g+1: for g < 2 they sit whole
@@ -69,17 +93,15 @@ template <> struct Direct<QG_Q4_K> {
     struct Lane {
         bool hi4;
         uint32_t off, oam, wa, wb;
-        int unit0;  // unit index in pass 0
     };
     __device__ static Lane lane_consts(int lane) {
         Lane L;
-        const int i = lane & (G - 1), g = i & 3;
+        const int g = (lane >> 2) & 3;  // slot b = lane / 4, and u % 4 = b % 4 in every pass
         L.hi4 = g >= 2;
         L.off = 16u * (uint32_t)(g & 1);
         L.oam = L.off + (L.hi4 ? 4u : 0u);
         L.wa = L.hi4 ? 4u : 6u;
         L.wb = L.hi4 ? 2u : 0u;
-        L.unit0 = i;
         return L;
     }
     __device__ __host__ static int units_per_row(int K) { return (K / 256) * 4; }
@@ -93,9 +115,14 @@ template <> struct Direct<QG_Q4_K> {
         r[4] = qb.x; r[5] = qb.y; r[6] = qb.z; r[7] = qb.w;
         r[8] = h.x; r[9] = h.y; r[10] = h.z; r[11] = h.w;
     }
+    // xa: this lane's A-operand base for unit u; xmg_bytes: bytes per group of
+    // 4 activation rows; xs: per sub-block activation sums [group][sub-block][4];
+    // live: the unit exists (the matrix-core work is wave-wide, only the
+    // accumulation is skipped).
     template <int MT>
-    __device__ static void decode(const uint32_t (&r)[REGS], const Lane& L, int u, const lds_u8* xl,
-                                  const lds_f32* xs, int xrow_bytes, int xs_row, float (&acc)[MT]) {
+    __device__ static void decode(const uint32_t (&r)[REGS], const Lane& L, int u, bool live, const lds_u8* xa,
+                                  int xmg_bytes, const lds_f32* xs, int xs_mg, float (&acc)[MT]) {
+        constexpr int MG = (MT + 3) / 4;
         const uint32_t y = r[9], z = r[10], w = r[11];
         const uint32_t as = L.hi4 ? w : y, am = L.hi4 ? w : z;
         const uint32_t sc0 = __builtin_amdgcn_ubfe(as, L.off, L.wa) | (__builtin_amdgcn_ubfe(y, L.off + 6, L.wb) << 4);
@@ -108,40 +135,48 @@ template <> struct Direct<QG_Q4_K> {
         const float a0 = d * (float)sc0, a1 = d * (float)sc1;
         const float b0 = -fmaf(dmin, (float)m0, 128.f * a0);
         const float b1 = -fmaf(dmin, (float)m1, 128.f * a1);
-        uint32_t lo[8], hi[8];
+
+        f32x4_t c0[MG], c1[MG];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            lo[i] = r[i] & 0x0F0F0F0Fu;
-            hi[i] = (r[i] >> 4) & 0x0F0F0F0Fu;
+        for (int g = 0; g < MG; ++g) c0[g] = c1[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int rot = u & 3;
+#pragma unroll
+        for (int rp = 0; rp < 4; ++rp) {
+            // values 8rp..8rp+7 of each sub-block: code dwords 2rp, 2rp+1 (low
+            // nibbles: sub-block 2g; high nibbles: sub-block 2g+1)
+            const uint32_t l0 = r[2 * rp] & 0x0F0F0F0Fu, l1 = r[2 * rp + 1] & 0x0F0F0F0Fu;
+            const uint32_t h0 = (r[2 * rp] >> 4) & 0x0F0F0F0Fu, h1 = (r[2 * rp + 1] >> 4) & 0x0F0F0F0Fu;
+            const uint32_t bl0 = bias128_pair(l0, kSelB0B1), bl1 = bias128_pair(l0, kSelB2B3);
+            const uint32_t bl2 = bias128_pair(l1, kSelB0B1), bl3 = bias128_pair(l1, kSelB2B3);
+            const uint32_t bh0 = bias128_pair(h0, kSelB0B1), bh1 = bias128_pair(h0, kSelB2B3);
+            const uint32_t bh2 = bias128_pair(h1, kSelB0B1), bh3 = bias128_pair(h1, kSelB2B3);
+#pragma unroll
+            for (int g = 0; g < MG; ++g) {
+                const u32x4 xl = lds_ld128(xa + g * xmg_bytes + ((rp ^ rot) * 4 * 16));
+                const u32x4 xh = lds_ld128(xa + g * xmg_bytes + (((4 + rp) ^ rot) * 4 * 16));
+                c0[g] = mfma4(xl.x, xl.y, bl0, bl1, c0[g]);
+                c1[g] = mfma4(xh.x, xh.y, bh0, bh1, c1[g]);
+                c0[g] = mfma4(xl.z, xl.w, bl2, bl3, c0[g]);
+                c1[g] = mfma4(xh.z, xh.w, bh2, bh3, c1[g]);
+            }
         }
+        if (live) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const lds_u8* xp = xl + (size_t)m * xrow_bytes + (size_t)u * (2 * XG + 16);
-            const XPairs x0 = load_x16(xp, 0), x1 = load_x16(xp, 16), x2 = load_x16(xp, 32), x3 = load_x16(xp, 48);
-            // The two sums as a float pair: __builtin_bit_cast of a vector element
-            // (s.y) read element 0 under this compiler.
-            const f32x2 s = *(const QG_LDS f32x2*)(xs + (size_t)m * xs_row + 2 * u);
-            float d0 = 0.f, d1 = 0.f;
+            for (int g = 0; g < MG; ++g) {
+                const f32x4_t s0 = *(const QG_LDS f32x4_t*)(xs + (size_t)g * xs_mg + 8 * u);
+                const f32x4_t s1 = *(const QG_LDS f32x4_t*)(xs + (size_t)g * xs_mg + 8 * u + 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                d0 = dot2bf(bias128_pair(lo[i], kSelB0B1), x0.v[2 * i], d0);
-                d0 = dot2bf(bias128_pair(lo[i], kSelB2B3), x0.v[2 * i + 1], d0);
-                d1 = dot2bf(bias128_pair(hi[i], kSelB0B1), x2.v[2 * i], d1);
-                d1 = dot2bf(bias128_pair(hi[i], kSelB2B3), x2.v[2 * i + 1], d1);
+                for (int i = 0; i < 4; ++i) {
+                    if (4 * g + i < MT) {
+                        float a = acc[4 * g + i];
+                        a = fmaf(a0, c0[g][i], a);
+                        a = fmaf(b0, s0[i], a);
+                        a = fmaf(a1, c1[g][i], a);
+                        a = fmaf(b1, s1[i], a);
+                        acc[4 * g + i] = a;
+                    }
+                }
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                d0 = dot2bf(bias128_pair(lo[4 + i], kSelB0B1), x1.v[2 * i], d0);
-                d0 = dot2bf(bias128_pair(lo[4 + i], kSelB2B3), x1.v[2 * i + 1], d0);
-                d1 = dot2bf(bias128_pair(hi[4 + i], kSelB0B1), x3.v[2 * i], d1);
-                d1 = dot2bf(bias128_pair(hi[4 + i], kSelB2B3), x3.v[2 * i + 1], d1);
-            }
-            float a = acc[m];
-            a = fmaf(a0, d0, a);
-            a = fmaf(b0, s.x, a);
-            a = fmaf(a1, d1, a);
-            a = fmaf(b1, s.y, a);
-            acc[m] = a;
         }
     }
 };
@@ -150,14 +185,11 @@ template <> struct Direct<QG_Q4_K> {
 // (values 32u + [0,32), blocks 2u and 2u + 1) and the two E4M3 scales of those
 // blocks.  sum w x = g * sum_b s_b * sum c x; g is applied once per output.
 template <> struct Direct<QG_NVFP4> {
-    static constexpr int G = 32;
-    static constexpr int XG = 32;
+    static constexpr int UV = 32;
     static constexpr int REGS = 5;
     static constexpr bool SUMS = false;
-    struct Lane {
-        int unit0;
-    };
-    __device__ static Lane lane_consts(int lane) { return Lane{lane & (G - 1)}; }
+    struct Lane {};
+    __device__ static Lane lane_consts(int) { return Lane{}; }
     __device__ __host__ static int units_per_row(int K) { return K / 32; }
     __device__ static void load(uint32_t (&r)[REGS], const uint8_t* row_codes, const uint8_t* row_scales, int u) {
         const u32x4 q = ld_stream128(row_codes + 16 * u);
@@ -165,52 +197,73 @@ template <> struct Direct<QG_NVFP4> {
         r[4] = __builtin_nontemporal_load((const QG_GLOBAL uint16_t*)(uintptr_t)(row_scales + 2 * u));
     }
     template <int MT>
-    __device__ static void decode(const uint32_t (&r)[REGS], const Lane&, int u, const lds_u8* xl, const lds_f32*,
-                                  int xrow_bytes, int, float (&acc)[MT]) {
-        const float s0 = e4m3_to_f32<0>(r[4]), s1 = e4m3_to_f32<1>(r[4]);
-        uint32_t p0[8], p1[8];
-        p0[0] = e2m1x2_to_bf16x2<0>(r[0]); p0[1] = e2m1x2_to_bf16x2<1>(r[0]);
-        p0[2] = e2m1x2_to_bf16x2<2>(r[0]); p0[3] = e2m1x2_to_bf16x2<3>(r[0]);
-        p0[4] = e2m1x2_to_bf16x2<0>(r[1]); p0[5] = e2m1x2_to_bf16x2<1>(r[1]);
-        p0[6] = e2m1x2_to_bf16x2<2>(r[1]); p0[7] = e2m1x2_to_bf16x2<3>(r[1]);
-        p1[0] = e2m1x2_to_bf16x2<0>(r[2]); p1[1] = e2m1x2_to_bf16x2<1>(r[2]);
-        p1[2] = e2m1x2_to_bf16x2<2>(r[2]); p1[3] = e2m1x2_to_bf16x2<3>(r[2]);
-        p1[4] = e2m1x2_to_bf16x2<0>(r[3]); p1[5] = e2m1x2_to_bf16x2<1>(r[3]);
-        p1[6] = e2m1x2_to_bf16x2<2>(r[3]); p1[7] = e2m1x2_to_bf16x2<3>(r[3]);
+    __device__ static void decode(const uint32_t (&r)[REGS], const Lane&, int u, bool live, const lds_u8* xa,
+                                  int xmg_bytes, const lds_f32*, int, float (&acc)[MT]) {
+        constexpr int MG = (MT + 3) / 4;
+        f32x4_t c0[MG], c1[MG];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const lds_u8* xp = xl + (size_t)m * xrow_bytes + (size_t)u * (2 * XG + 16);
-            const XPairs x0 = load_x16(xp, 0), x1 = load_x16(xp, 16);
-            float d0 = 0.f, d1 = 0.f;
+        for (int g = 0; g < MG; ++g) c0[g] = c1[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int rot = u & 3;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                d0 = dot2bf(p0[i], x0.v[i], d0);
-                d1 = dot2bf(p1[i], x1.v[i], d1);
+        for (int q = 0; q < 2; ++q) {
+            // block 0: values 8q..8q+7 (code dword q); block 1: values 16+8q.. (dword 2+q)
+            const uint32_t w0 = r[q], w1 = r[2 + q];
+            const uint32_t p00 = e2m1x2_to_bf16x2<0>(w0), p01 = e2m1x2_to_bf16x2<1>(w0);
+            const uint32_t p02 = e2m1x2_to_bf16x2<2>(w0), p03 = e2m1x2_to_bf16x2<3>(w0);
+            const uint32_t p10 = e2m1x2_to_bf16x2<0>(w1), p11 = e2m1x2_to_bf16x2<1>(w1);
+            const uint32_t p12 = e2m1x2_to_bf16x2<2>(w1), p13 = e2m1x2_to_bf16x2<3>(w1);
+#pragma unroll
+            for (int g = 0; g < MG; ++g) {
+                const u32x4 x0 = lds_ld128(xa + g * xmg_bytes + ((q ^ rot) * 4 * 16));
+                const u32x4 x1 = lds_ld128(xa + g * xmg_bytes + (((2 + q) ^ rot) * 4 * 16));
+                c0[g] = mfma4(x0.x, x0.y, p00, p01, c0[g]);
+                c1[g] = mfma4(x1.x, x1.y, p10, p11, c1[g]);
+                c0[g] = mfma4(x0.z, x0.w, p02, p03, c0[g]);
+                c1[g] = mfma4(x1.z, x1.w, p12, p13, c1[g]);
             }
-            acc[m] = fmaf(s1, d1, fmaf(s0, d0, acc[m]));
+        }
+        if (live) {
+            const float s0 = e4m3_to_f32<0>(r[4]), s1 = e4m3_to_f32<1>(r[4]);
+#pragma unroll
+            for (int g = 0; g < MG; ++g)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * g + i < MT) acc[4 * g + i] = fmaf(s1, c1[g][i], fmaf(s0, c0[g][i], acc[4 * g + i]));
         }
     }
 };
 
-__host__ __device__ constexpr int direct_group_lanes(int fmt) { return fmt == QG_Q4_K ? 16 : 32; }
-__host__ __device__ constexpr int direct_xg(int fmt) { return fmt == QG_Q4_K ? 64 : 32; }
+// ---------------------------------------------------------------- activation layout
+//
+// Group mg of 4 activation rows, unit u, position group pg (values 8pg..8pg+7
+// of the unit), row slot m4: 16 bytes at
+//     mg * MGB + u * UB + ((pg ^ (u % 4)) * 4 + m4) * 16.
+// The 4 row slots are always allocated (rows >= MT are simply never written);
+// A operands of lanes whose slot is >= MT read slot 0 instead.
 
-// Bytes of one padded activation row and of the per-row sums (Q4_K: one fp32
-// per 32 values).
-__host__ __device__ constexpr int direct_xrow_bytes(int fmt, int K) {
-    return (K / direct_xg(fmt)) * (2 * direct_xg(fmt) + 16);
-}
-__host__ __device__ constexpr int direct_xs_row(int fmt, int K) { return fmt == QG_Q4_K ? K / 32 : 0; }
+__host__ __device__ constexpr int direct_uv(int fmt) { return fmt == QG_Q4_K ? 64 : 32; }
+__host__ __device__ constexpr int direct_mg(int mt) { return (mt + 3) / 4; }
+// Bytes of one unit for one group of 4 activation rows.
+__host__ __device__ constexpr int direct_unit_bytes(int fmt) { return direct_uv(fmt) / 8 * 4 * 16; }
+// Bytes of one group of 4 activation rows (all units).
+__host__ __device__ constexpr int direct_mg_bytes(int fmt, int K) { return (K / direct_uv(fmt)) * direct_unit_bytes(fmt); }
+// Floats of per-sub-block sums per group of 4 rows (Q4_K: one per 32 values per row slot).
+__host__ __device__ constexpr int direct_xs_mg(int fmt, int K) { return fmt == QG_Q4_K ? (K / 32) * 4 : 0; }
 __host__ __device__ constexpr size_t direct_lds_bytes(int fmt, int mt, int K) {
-    return (size_t)mt * direct_xrow_bytes(fmt, K) + (size_t)mt * direct_xs_row(fmt, K) * 4;
+    return (size_t)direct_mg(mt) * direct_mg_bytes(fmt, K) + (size_t)direct_mg(mt) * direct_xs_mg(fmt, K) * 4;
+}
+// Byte offset of activation row m, values k..k+7 (k a multiple of 8).
+__host__ __device__ constexpr int direct_x_offset(int fmt, int K, int m, int k) {
+    return (m / 4) * direct_mg_bytes(fmt, K) + (k / direct_uv(fmt)) * direct_unit_bytes(fmt) +
+           ((((k % direct_uv(fmt)) / 8) ^ ((k / direct_uv(fmt)) & 3)) * 4 + (m % 4)) * 16;
 }
 
-// Activation staging in the padded layout, split in two so that the weight
-// loads can be issued in between: issue() loads up to XV 16-byte vectors per
-// thread into registers, commit() writes them (and any vectors beyond XV per
-// thread, loaded and written on the spot) to LDS, then, for Q4_K, computes the
-// per-32-value sums (sequential order).  Rows >= cnt are zero.  commit() ends
-// with a workgroup barrier.
+// Activation staging in the interleaved layout, split in two so that the
+// weight loads can be issued in between: issue() loads up to XV 16-byte
+// vectors per thread into registers, commit() writes them (and any vectors
+// beyond XV per thread, loaded and written on the spot) to LDS, then, for
+// Q4_K, computes the per-32-value sums (sequential order).  Rows >= cnt are
+// zero.  commit() ends with a workgroup barrier.
 template <int F, int MT, int XV>
 struct XStage {
     u32x4 v[XV];
@@ -230,12 +283,10 @@ struct XStage {
     template <class RowOf>
     __device__ __forceinline__ void commit(lds_u8* xl, lds_f32* xs, const uint16_t* x, int64_t ldx, int cnt, int K,
                                            RowOf row_of) {
-        constexpr int XG = Direct<F>::XG;
-        const int xrow = direct_xrow_bytes(F, K);
         const int nvec = MT * K / 8;
         auto put = [&](int i, const u32x4& val) {
             const int m = (i * 8) / K, k = (i * 8) % K;
-            *(lds_u32x4*)(xl + (size_t)m * xrow + (k / XG) * (2 * XG + 16) + (k % XG) * 2) = val;
+            *(lds_u32x4*)(xl + direct_x_offset(F, K, m, k)) = val;
         };
 #pragma unroll
         for (int j = 0; j < XV; ++j) {
@@ -253,49 +304,55 @@ struct XStage {
             const int per = K / 32;
             for (int i = threadIdx.x; i < MT * per; i += blockDim.x) {
                 const int m = i / per, k = (i % per) * 32;
-                const lds_u8* p = xl + (size_t)m * xrow + (k / XG) * (2 * XG + 16) + (k % XG) * 2;
-                const XPairs a = load_x16(p, 0), b = load_x16(p, 16);
                 float s = 0.f;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    s += bf16_to_f32(a.v[t]);
-                    s += bf16_to_f32(a.v[t] >> 16);
-                }
+                for (int t = 0; t < 4; ++t) {
+                    const u32x4 q = lds_ld128(xl + direct_x_offset(F, K, m, k + 8 * t));
+                    const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    s += bf16_to_f32(b.v[t]);
-                    s += bf16_to_f32(b.v[t] >> 16);
+                    for (int e = 0; e < 4; ++e) {
+                        s += bf16_to_f32(wv[e]);
+                        s += bf16_to_f32(wv[e] >> 16);
+                    }
                 }
-                xs[i] = s;
+                xs[(size_t)(m / 4) * direct_xs_mg(F, K) + (k / 32) * 4 + (m % 4)] = s;
             }
         }
         __syncthreads();
     }
 };
 
+// Activation row slot a lane writes its result for: its unit slot.
+__device__ __forceinline__ int direct_out_slot(int lane) { return lane >> 2; }
+
 // One wave streams row groups handed out by next_group() (a row-group index,
 // or a negative value when there are none left) of mv; row group rg is rows
-// RW*rg .. RW*rg + RW - 1 (rows >= N idle), RW = 64 / G, lane group lane / G
-// taking one row.  A row is P passes of G units, SP passes per ring slot, PF
-// slots in flight; the ring always holds the next PF slots of work, refilled
-// as soon as a slot is decoded.  Lane m < cnt of each group writes
-// y[yrow * ldy + n] for activation row m.  between() runs once, after the
-// first PF slots are in flight (the activation staging: a workgroup barrier
-// inside, so every wave of the workgroup must call this function).
+// 4 rg .. 4 rg + 3 (rows >= N idle), lane l serving row l % 4.  A row is P
+// passes of 16 units, SP passes per ring slot, PF slots in flight; the ring
+// always holds the next PF slots of work, refilled as soon as a slot is
+// decoded.  Lane l with slot s = l / 4 < cnt writes y[yrow * ldy + n] for
+// activation row s (yrow given for that slot).  between() runs once, after
+// the first PF slots are in flight (the activation staging: a workgroup
+// barrier inside, so every wave of the workgroup must call this function).
 template <int F, int MT, int SP, int PF, class Next, class Between>
 __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int K, const lds_u8* xl,
                                                    const lds_f32* xs, Next next_group, float* y, int64_t ldy,
                                                    int64_t yrow, int cnt, Between between) {
     using D = Direct<F>;
-    constexpr int G = D::G, RW = 64 / G;
+    constexpr int RW = kDirectRows, G = kDirectSlots;
     const int lane = threadIdx.x & 63;
-    const int grp = lane / G;
+    const int grp = lane & 3, slot = lane >> 2;
     const int U = D::units_per_row(K);
     const int P = (U + G - 1) / G;
     const int nseg = (P + SP - 1) / SP;
     const typename D::Lane L = D::lane_consts(lane);
-    const int xrow_bytes = direct_xrow_bytes(F, K);
-    const int xs_row = direct_xs_row(F, K);
+    const int ub = direct_unit_bytes(F);
+    const int mgb = direct_mg_bytes(F, K);
+    const int xs_mg = direct_xs_mg(F, K);
+    // A-operand row slot of this lane: lane % 4 (slots >= MT read slot 0: their
+    // products land in result rows nobody uses)
+    const int aslot = (lane & 3) < MT ? (lane & 3) : 0;
+    const lds_u8* xa_lane = xl + aslot * 16;
 
     float gscale = 1.f;
     if (F == QG_NVFP4) {
@@ -318,13 +375,13 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
         int n = 0;
         if (live) {
             n = RW * cur_g + grp;
-            if (n >= N) n = RW * cur_g;  // idle lane group: duplicate the group's first row
+            if (n >= N) n = RW * cur_g;  // idle row of the group: duplicate the group's first row
         }
         const uint8_t* rc = mv.w0 + (size_t)n * mv.rb0;
         const uint8_t* rs = F == QG_NVFP4 ? mv.w1 + (size_t)n * mv.rb1 : nullptr;
 #pragma unroll
         for (int p = 0; p < SP; ++p) {
-            const int u = ((live ? cur_s : 0) * SP + p) * G + L.unit0;
+            const int u = ((live ? cur_s : 0) * SP + p) * G + slot;
             D::load(r[p], rc, rs, u < U ? u : 0);
         }
         if (live && ++cur_s == nseg) {
@@ -340,20 +397,22 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
     auto process = [&](const uint32_t (&r)[SP][D::REGS], int sg, int ss) {
 #pragma unroll
         for (int p = 0; p < SP; ++p) {
-            const int u = (ss * SP + p) * G + L.unit0;
-            if (u < U) D::template decode<MT>(r[p], L, u, xl, xs, xrow_bytes, xs_row, acc);
+            const int u = (ss * SP + p) * G + slot;
+            const bool live = u < U;
+            const int ux = live ? u : 0;
+            D::template decode<MT>(r[p], L, ux, live, xa_lane + (size_t)ux * ub, mgb, xs, xs_mg, acc);
         }
         if (ss == nseg - 1) {
             const int n = RW * sg + grp;
             float mine = 0.f;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const float tot = group_sum<G>(acc[m]);
-                if ((lane & (G - 1)) == m) mine = tot;
+                const float tot = slot_sum(acc[m]);
+                if (slot == m) mine = tot;
                 acc[m] = 0.f;
             }
             if (F == QG_NVFP4) mine *= gscale;
-            if ((lane & (G - 1)) < cnt && n < N) st_global_f32(y + yrow * ldy + n, mine);
+            if (slot < cnt && n < N) st_global_f32(y + yrow * ldy + n, mine);
         }
     };
 

@@ -7,9 +7,12 @@
 
 namespace qg {
 
+// The direct kernel's LDS starts with its row-group counter.
+constexpr int kDirectCounterBytes = 16;
+
 // LDS one launch needs for `mt` activation rows.
 size_t stream_lds_bytes(int fmt, int K, int mt) {
-    if (direct_eligible(fmt, K)) return direct_lds_bytes(fmt, mt, K);
+    if (direct_eligible(fmt, K)) return kDirectCounterBytes + direct_lds_bytes(fmt, mt, K);
     return gemv_lds_bytes(mt, K, choose_cpl(fmt, K), fmt == QG_NVFP4 ? 1 : 0);
 }
 
@@ -39,19 +42,21 @@ __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
 // from a counter in LDS, so every CU finishes within about one row group of
 // the others.  The order in which waves take rows does not change any row's
 // arithmetic.
-constexpr int kDirectWaves = 16;
+// 16 waves per workgroup; 8 for 16 activation rows, whose accumulators need
+// more registers than 4 waves per SIMD allow.
+template <int MT> constexpr int direct_waves() { return MT >= 16 ? 8 : 16; }
 
 template <int F, int MT, int SP, int PF>
-__global__ __launch_bounds__(1024) void k_direct_gemm(const StreamArgs a) {
+__global__ __launch_bounds__(direct_waves<MT>() * 64) void k_direct_gemm(const StreamArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8* smem = (lds_u8*)smem_generic;
-    constexpr int G = Direct<F>::G, RW = 64 / G;
+    constexpr int RW = kDirectRows;
     const int K = a.K;
     QG_LDS int* counter = (QG_LDS int*)smem;
-    lds_u8* xl = smem + 16;
-    lds_f32* xs = (lds_f32*)(xl + (size_t)MT * direct_xrow_bytes(F, K));
+    lds_u8* xl = smem + kDirectCounterBytes;
+    lds_f32* xs = (lds_f32*)(xl + (size_t)direct_mg(MT) * direct_mg_bytes(F, K));
     const int lane = threadIdx.x & 63;
-    const int li = threadIdx.x & (G - 1);
+    const int li = direct_out_slot(lane);
     const int groups = (a.N + RW - 1) / RW;
     const int per = (groups + gridDim.x - 1) / gridDim.x;
     const int g0 = blockIdx.x * per, g1 = min(groups, g0 + per);
@@ -112,16 +117,16 @@ template <int MT> struct DirectTune<QG_NVFP4, MT> { static constexpr int SP = 2,
 
 template <int F, int MT>
 static hipError_t dispatch_direct(const StreamArgs& a, hipStream_t st) {
-    const size_t lds = 16 + direct_lds_bytes(F, MT, a.K);
+    const size_t lds = kDirectCounterBytes + direct_lds_bytes(F, MT, a.K);
     auto kern = k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF>;
     int fit = 0;
-    hipError_t e = kernel_residency((const void*)kern, lds, &fit, kDirectWaves * 64);
+    hipError_t e = kernel_residency((const void*)kern, lds, &fit, direct_waves<MT>() * 64);
     if (e != hipSuccess) return e;
-    constexpr int RW = 64 / Direct<F>::G;
+    constexpr int RW = kDirectRows;
     const long groups = (a.N + RW - 1) / RW;
     long grid = (long)num_cus() * fit;
     if (grid > groups) grid = groups;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kDirectWaves * 64), lds, st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(direct_waves<MT>() * 64), lds, st, a);
     return hipGetLastError();
 }
 

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32
     const int32_t* perm = ws + 5 + 2 * S;
 
     lds_u8* xl = smem;
-    lds_f32* xs = (lds_f32*)(smem + (DIRECT ? (size_t)MTMAX * direct_xrow_bytes(F, K) : (size_t)MTMAX * K * 2));
+    lds_f32* xs = (lds_f32*)(smem + (DIRECT ? (size_t)direct_mg(MTMAX) * direct_mg_bytes(F, K) : (size_t)MTMAX * K * 2));
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     lds_u8* rowbuf = smem + rowbuf_offset(MTMAX, K) + (size_t)wid * rowbuf_bytes(CPL, CPLS);
@@ -164,13 +164,13 @@ __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32
     for (int p0 = r0; p0 < r1; p0 += MTMAX) {
         const int cnt = min(MTMAX, r1 - p0);
         if (p0 != r0) __syncthreads();  // every wave is done with the previous pass's activations
-        const int li = DIRECT ? (lane & (direct_group_lanes(F) - 1)) : lane;
+        const int li = DIRECT ? direct_out_slot(lane) : lane;
         const int64_t yrow = perm[p0 + (li < cnt ? li : 0)];
         auto row_of = [&](int m) { return perm[p0 + m]; };
         auto run = [&](auto mt_tag) {
             constexpr int MT = decltype(mt_tag)::value;
             if constexpr (DIRECT) {
-                constexpr int RW = 64 / direct_group_lanes(F);
+                constexpr int RW = kDirectRows;
                 XStage<F, MT, 1> xst;
                 xst.issue(a.x, a.ldx, cnt, K, row_of);
                 auto between = [&] { xst.commit(xl, xs, a.x, a.ldx, cnt, K, row_of); };
