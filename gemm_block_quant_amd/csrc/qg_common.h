@@ -8,6 +8,10 @@ namespace qg {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// The same vectors at only 2-byte alignment (gfx950 serves 16- and 8-byte
+// global loads at any byte alignment).
+typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -99,6 +103,16 @@ __device__ __forceinline__ u32x4 ld_stream128(const uint8_t* p) {
 
 // Ordinary global 16-byte load / 4-byte store through the global address space.
 __device__ __forceinline__ u32x4 ld_global128(const void* p) { return *(const QG_GLOBAL u32x4*)(uintptr_t)p; }
+// 16 / 8 / 2 bytes at a 2-byte aligned address.
+__device__ __forceinline__ u32x4 ld_global128_a2(const void* p) {
+    const u32x4_a2 v = *(const QG_GLOBAL u32x4_a2*)(uintptr_t)p;
+    return u32x4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ u32x2 ld_global64_a2(const void* p) {
+    const u32x2_a2 v = *(const QG_GLOBAL u32x2_a2*)(uintptr_t)p;
+    return u32x2{v.x, v.y};
+}
+__device__ __forceinline__ uint32_t ld_global16(const void* p) { return *(const QG_GLOBAL uint16_t*)(uintptr_t)p; }
 __device__ __forceinline__ void st_global_f32(float* p, float v) { *(QG_GLOBAL float*)(uintptr_t)p = v; }
 
 // 16 bytes starting at p where only [p, limit) may be read (limit - p < 16),

@@ -1,25 +1,27 @@
-// qg_direct.h -- register-direct weight streaming for the 16-byte aligned
-// formats (Q4_K, and NVFP4 with K a multiple of 32), with the products formed
-// on the matrix cores by the 16-block 4x4x4 bf16 MFMA.
+// qg_direct.h -- register-direct weight streaming for Q4_K, Q6_K and NVFP4
+// (K a multiple of 64), with the products formed on the matrix cores by the
+// 16-block 4x4x4 bf16 MFMA.
 //
 // A wave works on 4 weight rows at once.  Lane l serves row j = l % 4 and
 // unit slot b = l / 4 (16 slots): in pass p it loads unit u = 16 p + b of its
-// row straight into registers -- Q4_K one quarter of a super-block (32 code
-// bytes = 64 values of two sub-blocks) plus the block's 16-byte header; NVFP4
-// 16 code bytes (32 values = two blocks) plus their two E4M3 scales.  The 16
-// lanes of a row cover a contiguous stretch of it, so the stream stays
-// coalesced and the weights never pass through LDS.
+// row (64 values) straight into registers -- Q4_K one quarter of a
+// super-block (32 code bytes) plus the block's 16-byte header; Q6_K the code
+// bytes, high bits and sub-scales of one quarter of a 210-byte block (2-byte
+// aligned loads, which gfx950 serves at full width); NVFP4 32 code bytes plus
+// their four E4M3 scales.  The 16 lanes of a row cover a contiguous stretch of
+// it, so the stream stays coalesced and the weights never pass through LDS.
 //
 // v_mfma_f32_4x4x4_16b_bf16 computes 16 independent products
 // D[b] = A[b] (4 x 4) * B[b] (4 x 4): lane l supplies row l % 4 of A[b] and
 // column l % 4 of B[b] (4 values along k each) and receives column l % 4 of
 // D[b] (4 values).  Here block b is unit slot b, B[b] holds 4 decoded weights
-// of each of the 4 rows (exact bf16: 128 + q for Q4_K, e2m1 for NVFP4), and
+// of each of the 4 rows (exact bf16: 128 + q for Q4_K and Q6_K, e2m1 for
+// NVFP4), and
 // A[b] holds the activations of up to 4 activation rows at the same 4
 // positions.  So one instruction forms, for every lane, the partial dot
 // products of its own weight row with 4 activation rows, and a lane's decoded
 // codes serve every activation row without further VALU work.  Eight (Q4_K) or
-// four (NVFP4) instructions accumulate one scale block; the lane then applies
+// four (Q6_K, NVFP4) instructions accumulate one scale block; the lane then applies
 // that block's scale to its 4 results in fp32.
 //
 // Every output element therefore has one fixed arithmetic: the matrix-core
@@ -181,54 +183,151 @@ template <> struct Direct<QG_Q4_K> {
     }
 };
 
-// NVFP4 (K a multiple of 32).  Unit u of a row = code bytes [16u, 16u + 16)
-// (values 32u + [0,32), blocks 2u and 2u + 1) and the two E4M3 scales of those
-// blocks.  sum w x = g * sum_b s_b * sum c x; g is applied once per output.
+// NVFP4 (K a multiple of 64).  Unit u of a row = code bytes [32u, 32u + 32)
+// (values 64u + [0,64), blocks 4u .. 4u + 3) and the four E4M3 scales of
+// those blocks (one 4-byte load).  sum w x = g * sum_b s_b * sum c x; g is
+// applied once per output.
 template <> struct Direct<QG_NVFP4> {
-    static constexpr int UV = 32;
-    static constexpr int REGS = 5;
+    static constexpr int UV = 64;
+    static constexpr int REGS = 9;
     static constexpr bool SUMS = false;
     struct Lane {};
     __device__ static Lane lane_consts(int) { return Lane{}; }
-    __device__ __host__ static int units_per_row(int K) { return K / 32; }
+    __device__ __host__ static int units_per_row(int K) { return K / 64; }
     __device__ static void load(uint32_t (&r)[REGS], const uint8_t* row_codes, const uint8_t* row_scales, int u) {
-        const u32x4 q = ld_stream128(row_codes + 16 * u);
-        r[0] = q.x; r[1] = q.y; r[2] = q.z; r[3] = q.w;
-        r[4] = __builtin_nontemporal_load((const QG_GLOBAL uint16_t*)(uintptr_t)(row_scales + 2 * u));
+        const u32x4 q0 = ld_stream128(row_codes + 32 * u), q1 = ld_stream128(row_codes + 32 * u + 16);
+        r[0] = q0.x; r[1] = q0.y; r[2] = q0.z; r[3] = q0.w;
+        r[4] = q1.x; r[5] = q1.y; r[6] = q1.z; r[7] = q1.w;
+        r[8] = __builtin_nontemporal_load((const QG_GLOBAL uint32_t*)(uintptr_t)(row_scales + 4 * u));
     }
     template <int MT>
     __device__ static void decode(const uint32_t (&r)[REGS], const Lane&, int u, bool live, const lds_u8* xa,
                                   int xmg_bytes, const lds_f32*, int, float (&acc)[MT]) {
         constexpr int MG = (MT + 3) / 4;
-        f32x4_t c0[MG], c1[MG];
+        f32x4_t c[4][MG];
 #pragma unroll
-        for (int g = 0; g < MG; ++g) c0[g] = c1[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int g = 0; g < MG; ++g) c[q][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         const int rot = u & 3;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            // block 0: values 8q..8q+7 (code dword q); block 1: values 16+8q.. (dword 2+q)
-            const uint32_t w0 = r[q], w1 = r[2 + q];
-            const uint32_t p00 = e2m1x2_to_bf16x2<0>(w0), p01 = e2m1x2_to_bf16x2<1>(w0);
-            const uint32_t p02 = e2m1x2_to_bf16x2<2>(w0), p03 = e2m1x2_to_bf16x2<3>(w0);
-            const uint32_t p10 = e2m1x2_to_bf16x2<0>(w1), p11 = e2m1x2_to_bf16x2<1>(w1);
-            const uint32_t p12 = e2m1x2_to_bf16x2<2>(w1), p13 = e2m1x2_to_bf16x2<3>(w1);
+        for (int h = 0; h < 2; ++h) {
+            // values 8h..8h+7 of each block q: code dword 2q + h
 #pragma unroll
-            for (int g = 0; g < MG; ++g) {
-                const u32x4 x0 = lds_ld128(xa + g * xmg_bytes + ((q ^ rot) * 4 * 16));
-                const u32x4 x1 = lds_ld128(xa + g * xmg_bytes + (((2 + q) ^ rot) * 4 * 16));
-                c0[g] = mfma4(x0.x, x0.y, p00, p01, c0[g]);
-                c1[g] = mfma4(x1.x, x1.y, p10, p11, c1[g]);
-                c0[g] = mfma4(x0.z, x0.w, p02, p03, c0[g]);
-                c1[g] = mfma4(x1.z, x1.w, p12, p13, c1[g]);
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t wv = r[2 * q + h];
+                const uint32_t p0 = e2m1x2_to_bf16x2<0>(wv), p1 = e2m1x2_to_bf16x2<1>(wv);
+                const uint32_t p2 = e2m1x2_to_bf16x2<2>(wv), p3 = e2m1x2_to_bf16x2<3>(wv);
+#pragma unroll
+                for (int g = 0; g < MG; ++g) {
+                    const u32x4 xv = lds_ld128(xa + g * xmg_bytes + (((2 * q + h) ^ rot) * 4 * 16));
+                    c[q][g] = mfma4(xv.x, xv.y, p0, p1, c[q][g]);
+                    c[q][g] = mfma4(xv.z, xv.w, p2, p3, c[q][g]);
+                }
             }
         }
         if (live) {
-            const float s0 = e4m3_to_f32<0>(r[4]), s1 = e4m3_to_f32<1>(r[4]);
+            const float s0 = e4m3_to_f32<0>(r[8]), s1 = e4m3_to_f32<1>(r[8]);
+            const float s2 = e4m3_to_f32<2>(r[8]), s3 = e4m3_to_f32<3>(r[8]);
 #pragma unroll
             for (int g = 0; g < MG; ++g)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (4 * g + i < MT) acc[4 * g + i] = fmaf(s1, c1[g][i], fmaf(s0, c0[g][i], acc[4 * g + i]));
+                    if (4 * g + i < MT) {
+                        float a = acc[4 * g + i];
+                        a = fmaf(s0, c[0][g][i], a);
+                        a = fmaf(s1, c[1][g][i], a);
+                        a = fmaf(s2, c[2][g][i], a);
+                        a = fmaf(s3, c[3][g][i], a);
+                        acc[4 * g + i] = a;
+                    }
+        }
+    }
+};
+
+// Q6_K.  Unit u of a row = quarter of super-block u / 4: half h = (u / 2) % 2,
+// part t = u % 2, i.e. the 64 values 128h + 32p + 16t + [0,16), p = 0..3,
+// each group of 16 with its own int8 sub-scale s[8h + 2p + t].  Its bytes: low
+// nibbles ql[64h + 16t ..] (p = 0, 2: low / high nibble) and
+// ql[64h + 32 + 16t ..] (p = 1, 3), 2-bit high parts qh[32h + 16t ..], the 8
+// sub-scales of the half and d.  Blocks are 210 bytes, so these loads are
+// only 2-byte aligned.
+// w = d s (q - 32)  ->  sum w x = d s (D - 160 X) with D = sum (128 + q) x.
+template <> struct Direct<QG_Q6_K> {
+    static constexpr int UV = 64;
+    static constexpr int REGS = 15;
+    static constexpr bool SUMS = true;
+    struct Lane {
+        uint32_t tsh;  // 8 * t: selects the part's sub-scales
+    };
+    __device__ static Lane lane_consts(int lane) { return Lane{8u * (uint32_t)((lane >> 2) & 1)}; }
+    __device__ __host__ static int units_per_row(int K) { return (K / 256) * 4; }
+    __device__ static void load(uint32_t (&r)[REGS], const uint8_t* row, const uint8_t*, int u) {
+        const uint8_t* blk = row + 210 * (u >> 2);
+        const int h = (u >> 1) & 1, t = u & 1;
+        const u32x4 qa = ld_global128_a2(blk + 64 * h + 16 * t);
+        const u32x4 qb = ld_global128_a2(blk + 64 * h + 32 + 16 * t);
+        const u32x4 qh = ld_global128_a2(blk + 128 + 32 * h + 16 * t);
+        const u32x2 sc = ld_global64_a2(blk + 192 + 8 * h);
+        r[0] = qa.x; r[1] = qa.y; r[2] = qa.z; r[3] = qa.w;
+        r[4] = qb.x; r[5] = qb.y; r[6] = qb.z; r[7] = qb.w;
+        r[8] = qh.x; r[9] = qh.y; r[10] = qh.z; r[11] = qh.w;
+        r[12] = sc.x; r[13] = sc.y;
+        r[14] = ld_global16(blk + 208);
+    }
+    template <int MT>
+    __device__ static void decode(const uint32_t (&r)[REGS], const Lane& L, int u, bool live, const lds_u8* xa,
+                                  int xmg_bytes, const lds_f32* xs, int xs_mg, float (&acc)[MT]) {
+        constexpr int MG = (MT + 3) / 4;
+        f32x4_t c[4][MG];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int g = 0; g < MG; ++g) c[p][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int rot = u & 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // values 4i..4i+3 of each of the 4 groups: 6-bit codes in bytes
+            const uint32_t A = r[i], B = r[4 + i], H = r[8 + i];
+            const uint32_t v[4] = {(A & 0x0F0F0F0Fu) | ((H << 4) & 0x30303030u),
+                                   (B & 0x0F0F0F0Fu) | ((H << 2) & 0x30303030u),
+                                   ((A >> 4) & 0x0F0F0F0Fu) | (H & 0x30303030u),
+                                   ((B >> 4) & 0x0F0F0F0Fu) | ((H >> 2) & 0x30303030u)};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t b0 = bias128_pair(v[p], kSelB0B1), b1 = bias128_pair(v[p], kSelB2B3);
+#pragma unroll
+                for (int g = 0; g < MG; ++g) {
+                    // position group 2p + i/2 holds values 8(i/2)..8(i/2)+7 of group p
+                    const u32x4 xv = lds_ld128(xa + g * xmg_bytes + (((2 * p + (i >> 1)) ^ rot) * 4 * 16));
+                    c[p][g] = (i & 1) ? mfma4(xv.z, xv.w, b0, b1, c[p][g]) : mfma4(xv.x, xv.y, b0, b1, c[p][g]);
+                }
+            }
+        }
+        if (live) {
+            const float d = f16_to_f32(r[14]);
+            const uint32_t st = r[12] >> L.tsh, su = r[13] >> L.tsh;
+            float a[4];
+            a[0] = d * (float)(int8_t)(st & 0xffu);
+            a[1] = d * (float)(int8_t)((st >> 16) & 0xffu);
+            a[2] = d * (float)(int8_t)(su & 0xffu);
+            a[3] = d * (float)(int8_t)((su >> 16) & 0xffu);
+#pragma unroll
+            for (int g = 0; g < MG; ++g) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const f32x4_t sx = *(const QG_LDS f32x4_t*)(xs + (size_t)g * xs_mg + (4 * u + p) * 4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (4 * g + i < MT) {
+                            float t = acc[4 * g + i];
+                            t = fmaf(a[p], c[p][g][i], t);
+                            t = fmaf(-160.f * a[p], sx[i], t);
+                            acc[4 * g + i] = t;
+                        }
+                    }
+                }
+            }
         }
     }
 };
@@ -241,21 +340,38 @@ template <> struct Direct<QG_NVFP4> {
 // The 4 row slots are always allocated (rows >= MT are simply never written);
 // A operands of lanes whose slot is >= MT read slot 0 instead.
 
-__host__ __device__ constexpr int direct_uv(int fmt) { return fmt == QG_Q4_K ? 64 : 32; }
+__host__ __device__ constexpr int direct_uv(int) { return 64; }
 __host__ __device__ constexpr int direct_mg(int mt) { return (mt + 3) / 4; }
+__host__ __device__ constexpr int direct_units(int K) { return K / 64; }
+// Activation sub-blocks (one scale, one sum) per unit: Q4_K 2 x 32 values,
+// Q6_K 4 x 16 values; NVFP4 needs no sums.
+__host__ __device__ constexpr int direct_sub(int fmt) { return fmt == QG_Q4_K ? 2 : fmt == QG_Q6_K ? 4 : 0; }
 // Bytes of one unit for one group of 4 activation rows.
-__host__ __device__ constexpr int direct_unit_bytes(int fmt) { return direct_uv(fmt) / 8 * 4 * 16; }
+__host__ __device__ constexpr int direct_unit_bytes(int) { return 8 * 4 * 16; }
 // Bytes of one group of 4 activation rows (all units).
-__host__ __device__ constexpr int direct_mg_bytes(int fmt, int K) { return (K / direct_uv(fmt)) * direct_unit_bytes(fmt); }
-// Floats of per-sub-block sums per group of 4 rows (Q4_K: one per 32 values per row slot).
-__host__ __device__ constexpr int direct_xs_mg(int fmt, int K) { return fmt == QG_Q4_K ? (K / 32) * 4 : 0; }
+__host__ __device__ constexpr int direct_mg_bytes(int fmt, int K) { return direct_units(K) * direct_unit_bytes(fmt); }
+// Floats of per-sub-block sums per group of 4 rows.
+__host__ __device__ constexpr int direct_xs_mg(int fmt, int K) { return direct_units(K) * direct_sub(fmt) * 4; }
 __host__ __device__ constexpr size_t direct_lds_bytes(int fmt, int mt, int K) {
     return (size_t)direct_mg(mt) * direct_mg_bytes(fmt, K) + (size_t)direct_mg(mt) * direct_xs_mg(fmt, K) * 4;
 }
+// Unit and position group (8 values) holding activation position k (a
+// multiple of 8).  Q4_K / NVFP4: units are 64 consecutive values.  Q6_K: unit
+// 4 b + 2 h + t holds values 256 b + 128 h + 32 p + 16 t + 8 e + [0,8) as
+// position group 2 p + e.
+__host__ __device__ constexpr int direct_pos_unit(int fmt, int k) {
+    return fmt == QG_Q6_K ? 4 * (k >> 8) + 2 * ((k >> 7) & 1) + ((k >> 4) & 1) : k >> 6;
+}
+__host__ __device__ constexpr int direct_pos_group(int fmt, int k) {
+    return fmt == QG_Q6_K ? 2 * ((k >> 5) & 3) + ((k >> 3) & 1) : (k & 63) >> 3;
+}
+// Byte offset of (activation row m, unit u, position group pg).
+__host__ __device__ constexpr int direct_x_at(int fmt, int K, int m, int u, int pg) {
+    return (m / 4) * direct_mg_bytes(fmt, K) + u * direct_unit_bytes(fmt) + (((pg ^ (u & 3)) * 4) + (m % 4)) * 16;
+}
 // Byte offset of activation row m, values k..k+7 (k a multiple of 8).
 __host__ __device__ constexpr int direct_x_offset(int fmt, int K, int m, int k) {
-    return (m / 4) * direct_mg_bytes(fmt, K) + (k / direct_uv(fmt)) * direct_unit_bytes(fmt) +
-           ((((k % direct_uv(fmt)) / 8) ^ ((k / direct_uv(fmt)) & 3)) * 4 + (m % 4)) * 16;
+    return direct_x_at(fmt, K, m, direct_pos_unit(fmt, k), direct_pos_group(fmt, k));
 }
 
 // Activation staging in the interleaved layout, split in two so that the
@@ -299,15 +415,17 @@ struct XStage {
             if (m < cnt) val = ld_global128(x + (size_t)row_of(m) * ldx + k);
             put(i, val);
         }
-        if (Direct<F>::SUMS) {
+        if constexpr (Direct<F>::SUMS) {
+            // sum of each sub-block's values (K order) per activation row
+            constexpr int SUB = direct_sub(F), PPS = 8 / SUB;  // position groups per sub-block
             __syncthreads();
-            const int per = K / 32;
-            for (int i = threadIdx.x; i < MT * per; i += blockDim.x) {
-                const int m = i / per, k = (i % per) * 32;
+            const int U = direct_units(K);
+            for (int i = threadIdx.x; i < MT * U * SUB; i += blockDim.x) {
+                const int m = i / (U * SUB), rem = i % (U * SUB), u = rem / SUB, p = rem % SUB;
                 float s = 0.f;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const u32x4 q = lds_ld128(xl + direct_x_offset(F, K, m, k + 8 * t));
+                for (int t = 0; t < PPS; ++t) {
+                    const u32x4 q = lds_ld128(xl + direct_x_at(F, K, m, u, p * PPS + t));
                     const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -315,7 +433,7 @@ struct XStage {
                         s += bf16_to_f32(wv[e] >> 16);
                     }
                 }
-                xs[(size_t)(m / 4) * direct_xs_mg(F, K) + (k / 32) * 4 + (m % 4)] = s;
+                xs[(size_t)(m / 4) * direct_xs_mg(F, K) + (u * SUB + p) * 4 + (m % 4)] = s;
             }
         }
         __syncthreads();
@@ -429,7 +547,7 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
 }
 
 inline bool direct_eligible(int fmt, int K) {
-    return fmt == QG_Q4_K || (fmt == QG_NVFP4 && K % 32 == 0);
+    return fmt == QG_Q4_K || fmt == QG_Q6_K || (fmt == QG_NVFP4 && K % 64 == 0);
 }
 
 }  // namespace qg

@@ -1,8 +1,8 @@
 // qg_gemv.hip -- dense decode GEMV (M = 1) and skinny product (M <= 16 rows
-// per pass) over one packed weight matrix: persistent workgroups, the grid's
-// waves taking rows n = gw, gw + GW, ...  Q4_K and NVFP4 (K % 32 == 0) stream
-// straight into registers (qg_direct.h); Q6_K and Q8_0, whose blocks are not
-// 16-byte aligned, go through a wave-private LDS row buffer (qg_stream.h).
+// per pass) over one packed weight matrix.  Q4_K, Q6_K and NVFP4 (K % 64 ==
+// 0) stream straight into registers and multiply on the matrix cores
+// (qg_direct.h); Q8_0 and NVFP4 with K % 64 == 32 go through a wave-private
+// LDS row buffer (qg_stream.h).
 #include "qg_direct.h"
 
 namespace qg {
@@ -42,12 +42,12 @@ __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
 // from a counter in LDS, so every CU finishes within about one row group of
 // the others.  The order in which waves take rows does not change any row's
 // arithmetic.
-// 16 waves per workgroup; 8 for 16 activation rows, whose accumulators need
-// more registers than 4 waves per SIMD allow.
-template <int MT> constexpr int direct_waves() { return MT >= 16 ? 8 : 16; }
+// 16 waves per workgroup; 8 where the accumulators of many activation rows
+// need more registers than 4 waves per SIMD allow.
+template <int F, int MT> constexpr int direct_waves() { return MT >= 16 || (F == QG_Q6_K && MT >= 8) ? 8 : 16; }
 
 template <int F, int MT, int SP, int PF>
-__global__ __launch_bounds__(direct_waves<MT>() * 64) void k_direct_gemm(const StreamArgs a) {
+__global__ __launch_bounds__((direct_waves<F, MT>() * 64)) void k_direct_gemm(const StreamArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8* smem = (lds_u8*)smem_generic;
     constexpr int RW = kDirectRows;
@@ -112,27 +112,28 @@ static hipError_t dispatch_rlt(StreamArgs a, hipStream_t st) {
 // Direct path: SP passes per ring slot, PF slots (pure tuning: the per-row
 // arithmetic does not depend on them).
 template <int F, int MT> struct DirectTune;
-template <int MT> struct DirectTune<QG_Q4_K, MT> { static constexpr int SP = 1, PF = MT <= 4 ? 2 : MT <= 8 ? 3 : 2; };
-template <int MT> struct DirectTune<QG_NVFP4, MT> { static constexpr int SP = 2, PF = 3; };
+template <int MT> struct DirectTune<QG_Q4_K, MT> { static constexpr int SP = 1, PF = 2; };
+template <int MT> struct DirectTune<QG_NVFP4, MT> { static constexpr int SP = 1, PF = 2; };
+template <int MT> struct DirectTune<QG_Q6_K, MT> { static constexpr int SP = 1, PF = 2; };
 
 template <int F, int MT>
 static hipError_t dispatch_direct(const StreamArgs& a, hipStream_t st) {
     const size_t lds = kDirectCounterBytes + direct_lds_bytes(F, MT, a.K);
     auto kern = k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF>;
     int fit = 0;
-    hipError_t e = kernel_residency((const void*)kern, lds, &fit, direct_waves<MT>() * 64);
+    hipError_t e = kernel_residency((const void*)kern, lds, &fit, direct_waves<F, MT>() * 64);
     if (e != hipSuccess) return e;
     constexpr int RW = kDirectRows;
     const long groups = (a.N + RW - 1) / RW;
     long grid = (long)num_cus() * fit;
     if (grid > groups) grid = groups;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(direct_waves<MT>() * 64), lds, st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(direct_waves<F, MT>() * 64), lds, st, a);
     return hipGetLastError();
 }
 
 template <int F>
 static hipError_t dispatch_mt(const StreamArgs& a, int mt, hipStream_t st) {
-    if constexpr (F == QG_Q4_K || F == QG_NVFP4) {
+    if constexpr (F == QG_Q4_K || F == QG_Q6_K || F == QG_NVFP4) {
         if (direct_eligible(F, a.K)) {
             switch (mt) {
                 case 1: return dispatch_direct<F, 1>(a, st);
@@ -143,7 +144,7 @@ static hipError_t dispatch_mt(const StreamArgs& a, int mt, hipStream_t st) {
             }
         }
     }
-    if constexpr (F != QG_Q4_K) {
+    if constexpr (F == QG_Q8_0 || F == QG_NVFP4) {
         switch (mt) {
             case 1: return dispatch_rlt<F, 1>(a, st);
             case 2: return dispatch_rlt<F, 2>(a, st);

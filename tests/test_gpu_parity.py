@@ -81,6 +81,7 @@ PRODUCT_CASES = [
     (qg.Q6_K, 99, 17408, 8), (qg.Q6_K, 333, 5120, 33),
     (qg.NVFP4, 1, 16, 1), (qg.NVFP4, 3, 48, 2), (qg.NVFP4, 1000, 5120, 1), (qg.NVFP4, 100, 17408, 1),
     (qg.NVFP4, 77, 592, 8), (qg.NVFP4, 200, 5120, 16), (qg.NVFP4, 51, 17408, 8),
+    (qg.NVFP4, 70, 96, 3), (qg.NVFP4, 33, 1056, 8),  # K % 64 == 32: row-buffer path
     # matrix-core path (NVFP4, M >= 32): ragged M and N tiles, K % 32 == 16 (half step)
     (qg.NVFP4, 200, 5120, 37), (qg.NVFP4, 130, 48, 33), (qg.NVFP4, 300, 1040, 130), (qg.NVFP4, 1000, 512, 64),
     (qg.NVFP4, 64, 16, 32),
