@@ -13,10 +13,12 @@
 //
 // Tiling: a 256-thread workgroup computes a BM x BN tile of y (activation rows
 // x weight rows); its four waves each own a (BM/2) x (BN/2) quarter as
-// (BM/64) x (BN/64) 32x32 accumulators.  K advances 32 values (two NVFP4
+// (BM/64) x (BN/64) 32x32 accumulators.  K advances 64 values (four NVFP4
 // blocks) per step through two LDS buffers: while the matrix cores work on
-// one, the next step's activations and codes are in flight from memory and
-// are then decoded into the other.
+// one, the next step is decoded into the other, and the loads of the steps
+// after it are already in flight in a register ring several steps deep.
+#include <type_traits>
+
 #include "qg_internal.h"
 
 namespace qg {
@@ -24,9 +26,19 @@ namespace qg {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kMfmaKStep = 32;
-constexpr int kMfmaRowBytes = 80;  // one tile row: 32 bf16 (64 B) + 16 B padding (conflict-free fragment reads)
+constexpr int kMfmaKStep = 64;
+constexpr int kMfmaRowBytes = 144;  // one tile row: 64 bf16 (128 B) + 16 B padding (conflict-free fragment reads)
 constexpr int kMfmaThreads = 256;
+constexpr int kMfmaStages = 2;  // K steps of loads in flight (an even number)
+
+// f(std::integral_constant<int, i>{}) for i = 0 .. N-1, unrolled.
+template <int N, int I = 0, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
 
 __device__ __forceinline__ uint32_t bf16_pair_from_exact(float lo, float hi) {
     // lo, hi are exact in bf16: their top 16 bits are the bf16 encodings.
@@ -68,7 +80,7 @@ struct MfmaArgs {
 template <int BM, int BN>
 __global__ __launch_bounds__(kMfmaThreads) void k_mfma_nvfp4(const MfmaArgs a) {
     constexpr int FM = BM / 64, FN = BN / 64;          // 32x32 fragments per wave
-    constexpr int XCH = BM * 4 / kMfmaThreads;         // 16-byte activation chunks per thread per step
+    constexpr int XCH = BM * 8 / kMfmaThreads;         // 16-byte activation chunks per thread per step
     constexpr int TILE_X = BM * kMfmaRowBytes, TILE_W = BN * kMfmaRowBytes;
     __shared__ __attribute__((aligned(16))) uint8_t smem_generic[2 * (TILE_X + TILE_W)];
     lds_u8* smem = (lds_u8*)smem_generic;
@@ -80,45 +92,60 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mfma_nvfp4(const MfmaArgs a) {
     const int nsteps = (K + kMfmaKStep - 1) / kMfmaKStep;
     const int64_t crow = K / 2, srow = K / 16;
 
-    // Per-thread staging of one step: activation chunks and one NVFP4 block.
-    u32x4 xr[XCH];
-    uint32_t wc0 = 0, wc1 = 0, wsb = 0;
+    // Per-thread register staging of one K step (activation chunks and one
+    // NVFP4 block), in a ring of kMfmaStages steps: the loads of step s + 1 +
+    // kMfmaStages - 1 are issued while step s is on the matrix cores, so the
+    // memory latency is covered by several steps of work.
+    constexpr int D = kMfmaStages;
+    u32x4 xr[D][XCH];
+    u32x4 wc[D];
+    uint32_t wsb[D];
     const int wr = tid >> 1, wh = tid & 1;  // weight tile row and block half owned by this thread
     const bool w_owner = tid < BN * 2;
 
-    auto load = [&](int s) {
+    auto load = [&](int s, auto stage_tag) {
+        constexpr int j = decltype(stage_tag)::value;
         const int k0 = s * kMfmaKStep;
 #pragma unroll
         for (int c = 0; c < XCH; ++c) {
             const int i = tid + c * kMfmaThreads;
-            const int r = i >> 2, q = i & 3;
+            const int r = i >> 3, q = i & 7;
             const int m = m0 + r, k = k0 + q * 8;
-            xr[c] = u32x4{0u, 0u, 0u, 0u};
-            if (m < M && k < K) xr[c] = ld_global128(a.x + (size_t)m * a.ldx + k);
+            xr[j][c] = u32x4{0u, 0u, 0u, 0u};
+            if (m < M && k < K) xr[j][c] = ld_global128(a.x + (size_t)m * a.ldx + k);
         }
-        wc0 = wc1 = wsb = 0;
-        const int n = n0 + wr, kb = k0 + wh * 16;
+        wc[j] = u32x4{0u, 0u, 0u, 0u};
+        wsb[j] = 0;
+        const int n = n0 + wr, kb = k0 + wh * 32;  // 32 values = two NVFP4 blocks
         if (w_owner && n < N && kb < K) {
-            const u32x2 c = *(const QG_GLOBAL u32x2*)(uintptr_t)(a.codes + (size_t)n * crow + kb / 2);
-            wc0 = c.x;
-            wc1 = c.y;
-            wsb = *(const QG_GLOBAL uint8_t*)(uintptr_t)(a.scales + (size_t)n * srow + kb / 16);
+            if (kb + 16 < K) {
+                wc[j] = ld_global128(a.codes + (size_t)n * crow + kb / 2);
+                wsb[j] = *(const QG_GLOBAL uint16_t*)(uintptr_t)(a.scales + (size_t)n * srow + kb / 16);
+            } else {  // the row's last block alone (K % 32 == 16)
+                const u32x2 c = *(const QG_GLOBAL u32x2*)(uintptr_t)(a.codes + (size_t)n * crow + kb / 2);
+                wc[j] = u32x4{c.x, c.y, 0u, 0u};
+                wsb[j] = *(const QG_GLOBAL uint8_t*)(uintptr_t)(a.scales + (size_t)n * srow + kb / 16);
+            }
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](int buf, auto stage_tag) {
+        constexpr int j = decltype(stage_tag)::value;
         lds_u8* tx = smem + buf * (TILE_X + TILE_W);
         lds_u8* tw = tx + TILE_X;
 #pragma unroll
         for (int c = 0; c < XCH; ++c) {
             const int i = tid + c * kMfmaThreads;
-            *(lds_u32x4*)(tx + (i >> 2) * kMfmaRowBytes + (i & 3) * 16) = xr[c];
+            *(lds_u32x4*)(tx + (i >> 3) * kMfmaRowBytes + (i & 7) * 16) = xr[j][c];
         }
         if (w_owner) {
-            uint32_t o[8];
-            decode_nvfp4_block_bf16(wc0, wc1, e4m3_to_f32<0>(wsb), o);
-            lds_u8* p = tw + wr * kMfmaRowBytes + wh * 32;
+            uint32_t o[8], o2[8];
+            decode_nvfp4_block_bf16(wc[j].x, wc[j].y, e4m3_to_f32<0>(wsb[j]), o);
+            decode_nvfp4_block_bf16(wc[j].z, wc[j].w, e4m3_to_f32<1>(wsb[j]), o2);
+            lds_u8* p = tw + wr * kMfmaRowBytes + wh * 64;
             *(lds_u32x4*)p = u32x4{o[0], o[1], o[2], o[3]};
             *(lds_u32x4*)(p + 16) = u32x4{o[4], o[5], o[6], o[7]};
+            *(lds_u32x4*)(p + 32) = u32x4{o2[0], o2[1], o2[2], o2[3]};
+            *(lds_u32x4*)(p + 48) = u32x4{o2[4], o2[5], o2[6], o2[7]};
         }
     };
 
@@ -128,17 +155,12 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mfma_nvfp4(const MfmaArgs a) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    load(0);
-    store(0);
-    __syncthreads();
     const int frow = lane & 31, fcol = (lane >> 5) * 16;
-    for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nsteps) load(s + 1);
+    auto mma = [&](int buf) {
         const lds_u8* tx = smem + buf * (TILE_X + TILE_W);
         const lds_u8* tw = tx + TILE_X;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < kMfmaKStep / 16; ++kk) {
             bf16x8_t fa[FM], fb[FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i)
@@ -152,8 +174,29 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mfma_nvfp4(const MfmaArgs a) {
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
-        if (s + 1 < nsteps) store(buf ^ 1);
-        __syncthreads();
+    };
+
+    // prologue: steps 0 .. D-1 in flight, step 0 in LDS, step D into the freed stage
+    static_for<D>([&](auto j) {
+        if (decltype(j)::value < nsteps) load(decltype(j)::value, j);
+    });
+    store(0, std::integral_constant<int, 0>{});
+    if (D < nsteps) load(D, std::integral_constant<int, 0>{});
+    __syncthreads();
+    for (int s0 = 0; s0 < nsteps; s0 += D) {
+        static_for<D>([&](auto jt) {
+            constexpr int j = decltype(jt)::value;
+            constexpr int nj = (j + 1) % D;
+            const int s = s0 + j;
+            if (s < nsteps) {
+                mma(j & 1);  // s0 is a multiple of D (even), so s & 1 == j & 1
+                if (s + 1 < nsteps) {
+                    store((j + 1) & 1, std::integral_constant<int, nj>{});
+                    if (s + 1 + D < nsteps) load(s + 1 + D, std::integral_constant<int, nj>{});
+                }
+                __syncthreads();
+            }
+        });
     }
 
     const uint8_t* gb = a.gbytes;
