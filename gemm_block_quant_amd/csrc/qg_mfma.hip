@@ -29,7 +29,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kMfmaKStep = 64;
 constexpr int kMfmaRowBytes = 144;  // one tile row: 64 bf16 (128 B) + 16 B padding (conflict-free fragment reads)
 constexpr int kMfmaThreads = 256;
-constexpr int kMfmaStages = 2;  // K steps of loads in flight (an even number)
+constexpr int kMfmaStages = 4;  // K steps of loads in flight (an even number)
 
 // f(std::integral_constant<int, i>{}) for i = 0 .. N-1, unrolled.
 template <int N, int I = 0, class Fn>
@@ -103,6 +103,9 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mfma_nvfp4(const MfmaArgs a) {
     const int wr = tid >> 1, wh = tid & 1;  // weight tile row and block half owned by this thread
     const bool w_owner = tid < BN * 2;
 
+    // Loads are branch-free (clamped addresses, results selected afterwards):
+    // a load under a branch makes the compiler wait for every outstanding load
+    // before the next use, which would void the prefetch.
     auto load = [&](int s, auto stage_tag) {
         constexpr int j = decltype(stage_tag)::value;
         const int k0 = s * kMfmaKStep;
@@ -111,22 +114,21 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mfma_nvfp4(const MfmaArgs a) {
             const int i = tid + c * kMfmaThreads;
             const int r = i >> 3, q = i & 7;
             const int m = m0 + r, k = k0 + q * 8;
-            xr[j][c] = u32x4{0u, 0u, 0u, 0u};
-            if (m < M && k < K) xr[j][c] = ld_global128(a.x + (size_t)m * a.ldx + k);
+            const bool ok = m < M && k < K;
+            const u32x4 v = ld_global128(a.x + (ok ? (size_t)m * a.ldx + k : 0));
+            xr[j][c] = ok ? v : u32x4{0u, 0u, 0u, 0u};
         }
-        wc[j] = u32x4{0u, 0u, 0u, 0u};
-        wsb[j] = 0;
-        const int n = n0 + wr, kb = k0 + wh * 32;  // 32 values = two NVFP4 blocks
-        if (w_owner && n < N && kb < K) {
-            if (kb + 16 < K) {
-                wc[j] = ld_global128(a.codes + (size_t)n * crow + kb / 2);
-                wsb[j] = *(const QG_GLOBAL uint16_t*)(uintptr_t)(a.scales + (size_t)n * srow + kb / 16);
-            } else {  // the row's last block alone (K % 32 == 16)
-                const u32x2 c = *(const QG_GLOBAL u32x2*)(uintptr_t)(a.codes + (size_t)n * crow + kb / 2);
-                wc[j] = u32x4{c.x, c.y, 0u, 0u};
-                wsb[j] = *(const QG_GLOBAL uint8_t*)(uintptr_t)(a.scales + (size_t)n * srow + kb / 16);
-            }
-        }
+        // 32 values = two NVFP4 blocks of row n; a row whose K % 32 == 16 ends
+        // with a single block, whose neighbour bytes (inside the tensor) are
+        // read and dropped
+        const int n = n0 + wr, kb = k0 + wh * 32;
+        const bool ok = w_owner && n < N && kb < K;
+        const bool two = kb + 16 < K;
+        const size_t nn = ok ? (size_t)n : 0, kk = ok ? (size_t)kb : 0;
+        const u32x4 cw = ld_global128(a.codes + nn * crow + kk / 2);
+        const uint32_t sw = *(const QG_GLOBAL uint16_t*)(uintptr_t)(a.scales + nn * srow + kk / 16);
+        wc[j] = ok ? (two ? cw : u32x4{cw.x, cw.y, 0u, 0u}) : u32x4{0u, 0u, 0u, 0u};
+        wsb[j] = ok ? (two ? sw : (sw & 0xffu)) : 0u;
     };
     auto store = [&](int buf, auto stage_tag) {
         constexpr int j = decltype(stage_tag)::value;
@@ -177,27 +179,35 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mfma_nvfp4(const MfmaArgs a) {
     };
 
     // prologue: steps 0 .. D-1 in flight, step 0 in LDS, step D into the freed stage
-    static_for<D>([&](auto j) {
-        if (decltype(j)::value < nsteps) load(decltype(j)::value, j);
-    });
+    static_for<D>([&](auto j) { load(min((int)decltype(j)::value, nsteps - 1), j); });
     store(0, std::integral_constant<int, 0>{});
-    if (D < nsteps) load(D, std::integral_constant<int, 0>{});
+    load(min(D, nsteps - 1), std::integral_constant<int, 0>{});
     __syncthreads();
-    for (int s0 = 0; s0 < nsteps; s0 += D) {
+    // main loop over whole groups of D steps: no branches, so the compiler
+    // waits only for the loads each store needs
+    int s0 = 0;
+    for (; s0 + D < nsteps; s0 += D) {
         static_for<D>([&](auto jt) {
             constexpr int j = decltype(jt)::value;
             constexpr int nj = (j + 1) % D;
             const int s = s0 + j;
-            if (s < nsteps) {
-                mma(j & 1);  // s0 is a multiple of D (even), so s & 1 == j & 1
-                if (s + 1 < nsteps) {
-                    store((j + 1) & 1, std::integral_constant<int, nj>{});
-                    if (s + 1 + D < nsteps) load(s + 1 + D, std::integral_constant<int, nj>{});
-                }
-                __syncthreads();
-            }
+            mma(j & 1);  // s0 is a multiple of D (even), so s & 1 == j & 1
+            store((j + 1) & 1, std::integral_constant<int, nj>{});
+            load(min(s + 1 + D, nsteps - 1), std::integral_constant<int, nj>{});  // (past the end: a harmless reload)
+            __syncthreads();
         });
     }
+    // the last (up to D) steps
+    static_for<D>([&](auto jt) {
+        constexpr int j = decltype(jt)::value;
+        constexpr int nj = (j + 1) % D;
+        const int s = s0 + j;
+        if (s < nsteps) {
+            mma(j & 1);
+            if (s + 1 < nsteps) store((j + 1) & 1, std::integral_constant<int, nj>{});
+            __syncthreads();
+        }
+    });
 
     const uint8_t* gb = a.gbytes;
     const uint32_t gbits = (uint32_t)gb[0] | ((uint32_t)gb[1] << 8) | ((uint32_t)gb[2] << 16) | ((uint32_t)gb[3] << 24);
