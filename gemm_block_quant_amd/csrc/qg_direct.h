@@ -443,26 +443,64 @@ struct XStage {
 // Activation row slot a lane writes its result for: its unit slot.
 __device__ __forceinline__ int direct_out_slot(int lane) { return lane >> 2; }
 
-// One wave streams row groups handed out by next_group() (a row-group index,
-// or a negative value when there are none left) of mv; row group rg is rows
-// 4 rg .. 4 rg + 3 (rows >= N idle), lane l serving row l % 4.  A row is P
-// passes of 16 units, SP passes per ring slot, PF slots in flight; the ring
-// always holds the next PF slots of work, refilled as soon as a slot is
-// decoded.  Lane l with slot s = l / 4 < cnt writes y[yrow * ldy + n] for
+// K segments of a row: a row of P passes is cut into S segments of PS passes
+// (the last one shorter).  The cut depends only on (format, N, K) and the
+// device's CU count, never on the number of activation rows, so every output
+// keeps one arithmetic: the segment sums are added in segment order.  Rows
+// are split only when there are too few row groups to occupy the waves.
+struct Segments {
+    int S, PS;
+};
+// Rows are split only while a CU has fewer than this many row groups.
+constexpr int kDirectSegRgsMax = 16;
+inline Segments direct_segments(int fmt, int64_t N, int K, int cus) {
+    const int P = (K / 64 + kDirectSlots - 1) / kDirectSlots;
+    const int64_t groups = (N + kDirectRows - 1) / kDirectRows;
+    const int64_t per_cu = (groups + cus - 1) / cus;
+    int S = 1;
+    if (per_cu < kDirectSegRgsMax) S = (int)((48 + per_cu - 1) / per_cu);
+    if (S > P) S = P;
+    if (S < 1) S = 1;
+    const int PS = (P + S - 1) / S;
+    (void)fmt;
+    return Segments{(P + PS - 1) / PS, PS};
+}
+
+// LDS of the segment sums for `rgs` row groups (none when rows are not split).
+inline size_t direct_seg_lds_bytes(int S, int rgs, int mt) {
+    return S > 1 ? ((size_t)rgs * 4 + 15) / 16 * 16 + (size_t)rgs * kDirectRows * mt * 4 : 0;
+}
+
+// Ordered accumulation of the segment sums of a workgroup's row groups in
+// LDS: total[(rg_local * 4 + row) * MTMAX + m] and progress[rg_local] (the
+// number of segments already added).  Both start at zero.
+struct SegLds {
+    lds_f32* total;
+    QG_LDS int* progress;
+    int mtmax;
+};
+
+// One wave streams work items handed out by next_item() (an item index local
+// to the workgroup, or a negative value when there are none left): item t is
+// segment t % S of row group rg_base + t / S of mv; row group rg is rows
+// 4 rg .. 4 rg + 3 (rows >= N idle), lane l serving row l % 4.  A segment is
+// up to PS passes of 16 units, SP passes per ring slot, PF slots in flight;
+// the ring always holds the next PF slots of work, refilled as soon as a slot
+// is decoded.  Lane l with slot s = l / 4 < cnt writes y[yrow * ldy + n] for
 // activation row s (yrow given for that slot).  between() runs once, after
 // the first PF slots are in flight (the activation staging: a workgroup
 // barrier inside, so every wave of the workgroup must call this function).
 template <int F, int MT, int SP, int PF, class Next, class Between>
 __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int K, const lds_u8* xl,
-                                                   const lds_f32* xs, Next next_group, float* y, int64_t ldy,
-                                                   int64_t yrow, int cnt, Between between) {
+                                                   const lds_f32* xs, Next next_item, int rg_base, Segments sg,
+                                                   SegLds sl, float* y, int64_t ldy, int64_t yrow, int cnt,
+                                                   Between between) {
     using D = Direct<F>;
     constexpr int RW = kDirectRows, G = kDirectSlots;
     const int lane = threadIdx.x & 63;
     const int grp = lane & 3, slot = lane >> 2;
     const int U = D::units_per_row(K);
     const int P = (U + G - 1) / G;
-    const int nseg = (P + SP - 1) / SP;
     const typename D::Lane L = D::lane_consts(lane);
     const int ub = direct_unit_bytes(F);
     const int mgb = direct_mg_bytes(F, K);
@@ -481,30 +519,46 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
     }
 
     uint32_t R[PF][SP][D::REGS];
-    int slot_g[PF], slot_s[PF];  // row group and segment held by each slot (group < 0: none)
+    // per slot: item (< 0: none), first pass, and whether it ends the item
+    int slot_t[PF], slot_p[PF];
+    bool slot_last[PF];
 
-    int cur_g = next_group(), cur_s = 0;
-    // Issues the next segment of work into a slot; with no work left it loads
-    // unit 0 of row 0 (every path issues the same loads).
-    auto issue = [&](uint32_t (&r)[SP][D::REGS], int& sg, int& ss) {
-        const bool live = cur_g >= 0;
-        sg = cur_g;
-        ss = cur_s;
+    // current item and its pass cursor
+    int cur_t = next_item(), cur_p = 0, cur_end = 0;
+    auto item_range = [&](int t, int& p0, int& p1) {
+        const int s = t % sg.S;
+        p0 = s * sg.PS;
+        p1 = min(P, p0 + sg.PS);
+    };
+    if (cur_t >= 0) item_range(cur_t, cur_p, cur_end);
+    // Issues the next SP passes of work into a slot; with no work left it
+    // loads unit 0 of row 0 (every path issues the same loads).
+    auto issue = [&](uint32_t (&r)[SP][D::REGS], int& st, int& sp, bool& slast) {
+        const bool live = cur_t >= 0;
+        st = cur_t;
+        sp = cur_p;
         int n = 0;
         if (live) {
-            n = RW * cur_g + grp;
-            if (n >= N) n = RW * cur_g;  // idle row of the group: duplicate the group's first row
+            const int rg = rg_base + cur_t / sg.S;
+            n = RW * rg + grp;
+            if (n >= N) n = RW * rg;  // idle row of the group: duplicate the group's first row
         }
         const uint8_t* rc = mv.w0 + (size_t)n * mv.rb0;
         const uint8_t* rs = F == QG_NVFP4 ? mv.w1 + (size_t)n * mv.rb1 : nullptr;
 #pragma unroll
         for (int p = 0; p < SP; ++p) {
-            const int u = ((live ? cur_s : 0) * SP + p) * G + slot;
-            D::load(r[p], rc, rs, u < U ? u : 0);
+            const int pass = live ? cur_p + p : 0;
+            const int u = pass * G + slot;
+            D::load(r[p], rc, rs, (live && pass < cur_end && u < U) ? u : 0);
         }
-        if (live && ++cur_s == nseg) {
-            cur_s = 0;
-            cur_g = next_group();
+        slast = false;
+        if (live) {
+            cur_p += SP;
+            if (cur_p >= cur_end) {
+                slast = true;
+                cur_t = next_item();
+                if (cur_t >= 0) item_range(cur_t, cur_p, cur_end);
+            }
         }
     };
 
@@ -512,16 +566,19 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.f;
 
-    auto process = [&](const uint32_t (&r)[SP][D::REGS], int sg, int ss) {
+    auto process = [&](const uint32_t (&r)[SP][D::REGS], int t, int p0, bool last) {
+        int pe, pend;
+        item_range(t, pe, pend);
 #pragma unroll
         for (int p = 0; p < SP; ++p) {
-            const int u = (ss * SP + p) * G + slot;
-            const bool live = u < U;
+            const int u = (p0 + p) * G + slot;
+            const bool live = p0 + p < pend && u < U;
             const int ux = live ? u : 0;
             D::template decode<MT>(r[p], L, ux, live, xa_lane + (size_t)ux * ub, mgb, xs, xs_mg, acc);
         }
-        if (ss == nseg - 1) {
-            const int n = RW * sg + grp;
+        if (last) {
+            const int rgl = t / sg.S, s = t % sg.S;
+            const int n = RW * (rg_base + rgl) + grp;
             float mine = 0.f;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
@@ -529,19 +586,38 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
                 if (slot == m) mine = tot;
                 acc[m] = 0.f;
             }
-            if (F == QG_NVFP4) mine *= gscale;
-            if (slot < cnt && n < N) st_global_f32(y + yrow * ldy + n, mine);
+            if (sg.S > 1) {
+                // add this segment after the ones before it, in segment order
+                // (the oldest unfinished item never waits, so this ends; the
+                // bound only guarantees that every wave exits)
+                QG_LDS int* prog = sl.progress + rgl;
+                for (int spin = 0; spin < (1 << 22); ++spin) {
+                    if (__hip_atomic_load(prog, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == s) break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                lds_f32* tp = sl.total + (size_t)(rgl * RW + grp) * sl.mtmax + (slot < MT ? slot : 0);
+                if (slot < MT) {
+                    const float sum = s == 0 ? mine : *tp + mine;
+                    *tp = sum;
+                    mine = sum;
+                }
+                __hip_atomic_store(prog, s + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            if (s == sg.S - 1) {
+                if (F == QG_NVFP4) mine *= gscale;
+                if (slot < cnt && n < N) st_global_f32(y + yrow * ldy + n, mine);
+            }
         }
     };
 
 #pragma unroll
-    for (int sl = 0; sl < PF; ++sl) issue(R[sl], slot_g[sl], slot_s[sl]);
+    for (int k = 0; k < PF; ++k) issue(R[k], slot_t[k], slot_p[k], slot_last[k]);
     between();
-    while (slot_g[0] >= 0) {
+    while (slot_t[0] >= 0) {
 #pragma unroll
-        for (int sl = 0; sl < PF; ++sl) {
-            if (slot_g[sl] >= 0) process(R[sl], slot_g[sl], slot_s[sl]);
-            issue(R[sl], slot_g[sl], slot_s[sl]);
+        for (int k = 0; k < PF; ++k) {
+            if (slot_t[k] >= 0) process(R[k], slot_t[k], slot_p[k], slot_last[k]);
+            issue(R[k], slot_t[k], slot_p[k], slot_last[k]);
         }
     }
 }

@@ -12,7 +12,8 @@ constexpr int kDirectCounterBytes = 16;
 
 // LDS one launch needs for `mt` activation rows.
 size_t stream_lds_bytes(int fmt, int K, int mt) {
-    if (direct_eligible(fmt, K)) return kDirectCounterBytes + direct_lds_bytes(fmt, mt, K);
+    if (direct_eligible(fmt, K))
+        return kDirectCounterBytes + direct_lds_bytes(fmt, mt, K) + direct_seg_lds_bytes(2, kDirectSegRgsMax, mt);  // (worst case)
     return gemv_lds_bytes(mt, K, choose_cpl(fmt, K), fmt == QG_NVFP4 ? 1 : 0);
 }
 
@@ -38,10 +39,10 @@ __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
 }
 
 // Direct path: one 16-wave workgroup per CU.  Workgroup b owns an equal
-// contiguous share of the row groups and its waves take them one at a time
-// from a counter in LDS, so every CU finishes within about one row group of
-// the others.  The order in which waves take rows does not change any row's
-// arithmetic.
+// contiguous share of the row groups; its waves take (row group, K segment)
+// items one at a time from a counter in LDS, so every CU finishes within
+// about one item of the others.  The order in which waves take items does not
+// change any row's arithmetic.
 // 16 waves per workgroup; 8 where the accumulators of many activation rows
 // need more registers than 4 waves per SIMD allow.
 template <int F, int MT> constexpr int direct_waves() { return MT >= 16 || (F == QG_Q6_K && MT >= 8) ? 8 : 16; }
@@ -60,21 +61,30 @@ __global__ __launch_bounds__((direct_waves<F, MT>() * 64)) void k_direct_gemm(co
     const int groups = (a.N + RW - 1) / RW;
     const int per = (groups + gridDim.x - 1) / gridDim.x;
     const int g0 = blockIdx.x * per, g1 = min(groups, g0 + per);
+    const Segments sg{a.seg_S > 0 ? a.seg_S : 1, a.seg_PS > 0 ? a.seg_PS : 1};
+    const int items = (g1 > g0 ? g1 - g0 : 0) * sg.S;
+    // segment sums after the activations: progress[per], then total[per][4][MT]
+    SegLds sl;
+    sl.progress = (QG_LDS int*)(xl + direct_lds_bytes(F, MT, K));
+    sl.total = (lds_f32*)((lds_u8*)sl.progress + ((size_t)per * 4 + 15) / 16 * 16);
+    sl.mtmax = MT;
     if (threadIdx.x == 0) *counter = 0;
-    auto next_group = [&]() {
+    if (sg.S > 1)
+        for (int i = threadIdx.x; i < per; i += blockDim.x) sl.progress[i] = 0;
+    auto next_item = [&]() {
         int t = 0;
         if (lane == 0) t = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         t = __builtin_amdgcn_readfirstlane(t);
-        return g0 + t < g1 ? g0 + t : -1;
+        return t < items ? t : -1;
     };
     MatView mv = {a.w0, a.rb0, a.w1, a.rb1, a.gbytes};
     const int64_t yrow = a.yrow[li < a.M ? li : 0];
     auto row_of = [&](int m) { return a.xrow[m]; };
     XStage<F, MT, 2> xst;
     xst.issue(a.x, a.ldx, a.M, K, row_of);
-    __syncthreads();  // the counter is initialised before any wave takes work
+    __syncthreads();  // the counter and progress are initialised before any wave takes work
     auto between = [&] { xst.commit(xl, xs, a.x, a.ldx, a.M, K, row_of); };
-    wave_stream_direct<F, MT, SP, PF>(mv, a.N, K, xl, xs, next_group, a.y, a.ldy, yrow, a.M, between);
+    wave_stream_direct<F, MT, SP, PF>(mv, a.N, K, xl, xs, next_item, g0, sg, sl, a.y, a.ldy, yrow, a.M, between);
 }
 
 // Persistent grid: as many 4-wave workgroups as can be resident at once (by
@@ -117,16 +127,27 @@ template <int MT> struct DirectTune<QG_NVFP4, MT> { static constexpr int SP = 1,
 template <int MT> struct DirectTune<QG_Q6_K, MT> { static constexpr int SP = 1, PF = 2; };
 
 template <int F, int MT>
-static hipError_t dispatch_direct(const StreamArgs& a, hipStream_t st) {
-    const size_t lds = kDirectCounterBytes + direct_lds_bytes(F, MT, a.K);
+static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
+    const Segments sg = direct_segments(F, a.N, a.K, num_cus());
+    a.seg_S = sg.S;
+    a.seg_PS = sg.PS;
     auto kern = k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF>;
-    int fit = 0;
-    hipError_t e = kernel_residency((const void*)kern, lds, &fit, direct_waves<F, MT>() * 64);
-    if (e != hipSuccess) return e;
     constexpr int RW = kDirectRows;
     const long groups = (a.N + RW - 1) / RW;
-    long grid = (long)num_cus() * fit;
-    if (grid > groups) grid = groups;
+    // grid from the residency without the segment sums, then their LDS for the
+    // resulting share of row groups (and the residency again)
+    size_t lds = kDirectCounterBytes + direct_lds_bytes(F, MT, a.K);
+    long grid = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+        int fit = 0;
+        hipError_t e = kernel_residency((const void*)kern, lds, &fit, direct_waves<F, MT>() * 64);
+        if (e != hipSuccess) return e;
+        grid = (long)num_cus() * fit;
+        if (grid > groups) grid = groups;
+        const long per = (groups + grid - 1) / grid;
+        lds = kDirectCounterBytes + direct_lds_bytes(F, MT, a.K) + direct_seg_lds_bytes(sg.S, (int)per, MT);
+    }
+    if (lds > (size_t)kLdsBytes) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(direct_waves<F, MT>() * 64), lds, st, a);
     return hipGetLastError();
 }

@@ -171,19 +171,28 @@ __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32
             constexpr int MT = decltype(mt_tag)::value;
             if constexpr (DIRECT) {
                 constexpr int RW = kDirectRows;
+                // rpc is a multiple of RW, so row groups never straddle chunks; the
+                // workgroup's waves take its (row group, K segment) items round robin
+                const Segments sg{a.seg_S > 0 ? a.seg_S : 1, a.seg_PS > 0 ? a.seg_PS : 1};
+                const int rg0 = n_begin / RW, rgs = (n_end - n_begin + RW - 1) / RW;
+                SegLds sl;
+                sl.progress = (QG_LDS int*)(xl + direct_lds_bytes(F, MTMAX, K));
+                sl.total = (lds_f32*)((lds_u8*)sl.progress + ((size_t)rgs * 4 + 15) / 16 * 16);
+                sl.mtmax = MT;
+                if (sg.S > 1)
+                    for (int i = threadIdx.x; i < rgs; i += blockDim.x) sl.progress[i] = 0;
                 XStage<F, MT, 1> xst;
                 xst.issue(a.x, a.ldx, cnt, K, row_of);
                 auto between = [&] { xst.commit(xl, xs, a.x, a.ldx, cnt, K, row_of); };
-                // rpc is a multiple of RW, so row groups never straddle chunks; the
-                // workgroup's waves take its groups round robin
-                int next = n_begin / RW + wid;
-                const int gend = (n_end + RW - 1) / RW;
-                auto next_group = [&]() {
-                    const int g = next;
+                const int items = rgs * sg.S;
+                int next = wid;
+                auto next_item = [&]() {
+                    const int t = next;
                     next += kWavesPerBlock;
-                    return g < gend ? g : -1;
+                    return t < items ? t : -1;
                 };
-                wave_stream_direct<F, MT, SP, PF>(mv, n_end, K, xl, xs, next_group, a.y, a.ldy, yrow, cnt, between);
+                wave_stream_direct<F, MT, SP, PF>(mv, n_end, K, xl, xs, next_item, rg0, sg, sl, a.y, a.ldy, yrow,
+                                                  cnt, between);
             } else {
                 auto stage = [&] { stage_x<MT, kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of); };
                 wave_stream<F, MT, CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf, rowbuf_s,
@@ -204,9 +213,12 @@ size_t grouped_workspace_bytes(int64_t E, int64_t M) {
     return (size_t)((ints * 4 + 15) / 16 * 16);
 }
 
+// lds: the kernel's LDS; seg_mt > 0: rows are split into K segments whose sums
+// take LDS per row group of a chunk (chunks then hold at most 16 row groups).
 template <class Kern>
 static hipError_t launch_grouped_one(Kern kern, size_t lds, const StreamArgs& a, const int32_t* ws, int64_t E,
-                                     int64_t M, int64_t estride0, int64_t estride1, hipStream_t st) {
+                                     int64_t M, int64_t estride0, int64_t estride1, hipStream_t st,
+                                     int seg_mt = 0) {
     int fit = 0;
     hipError_t e = kernel_residency((const void*)kern, lds, &fit);
     if (e != hipSuccess) return e;
@@ -219,7 +231,10 @@ static hipError_t launch_grouped_one(Kern kern, size_t lds, const StreamArgs& a,
     if (nchunks < 1) nchunks = 1;
     int rpc = (int)((a.N + nchunks - 1) / nchunks);
     rpc = (rpc + 3) & ~3;  // a multiple of every rows-per-wave (1, 2, 4)
+    const bool split = seg_mt > 0 && a.seg_S > 1;
+    if (split && rpc > 4 * kDirectSegRgsMax) rpc = 4 * kDirectSegRgsMax;
     nchunks = (a.N + rpc - 1) / rpc;
+    if (split) lds += direct_seg_lds_bytes(a.seg_S, rpc / 4, seg_mt);
     hipLaunchKernelGGL(kern, dim3((unsigned)(S * nchunks)), dim3(256), lds, st, a, ws, E, M, rpc, (int)nchunks,
                        estride0, estride1);
     return hipGetLastError();
@@ -230,9 +245,13 @@ static hipError_t grouped_paths(StreamArgs a, const int32_t* ws, int64_t E, int6
                                 hipStream_t st) {
     if constexpr (F == QG_Q4_K || F == QG_Q6_K || F == QG_NVFP4) {
         if (direct_eligible(F, a.K)) {
+            const Segments sg = direct_segments(F, a.N, a.K, num_cus());
+            a.seg_S = sg.S;
+            a.seg_PS = sg.PS;
             const size_t lds = direct_lds_bytes(F, MTMAX, a.K);
             constexpr int SP = 1, PF = 3;
-            return launch_grouped_one(k_grouped<F, MTMAX, true, 1, 0, SP, PF>, lds, a, ws, E, M, es0, es1, st);
+            return launch_grouped_one(k_grouped<F, MTMAX, true, 1, 0, SP, PF>, lds, a, ws, E, M, es0, es1, st,
+                                      MTMAX);
         }
     }
     if constexpr (F == QG_Q8_0 || F == QG_NVFP4) {

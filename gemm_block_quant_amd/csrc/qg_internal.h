@@ -17,7 +17,8 @@ struct StreamArgs {
     int64_t rb1;         // NVFP4: scale bytes per row
     const uint8_t* gbytes;  // NVFP4: device address of the matrix's fp32 tensor scale (any alignment)
     int N, K;
-    int seg_blocks, nseg;  // filled by the dispatcher
+    int seg_blocks, nseg;  // row-buffer path: filled by the dispatcher
+    int seg_S, seg_PS;     // direct path: K segments per row and passes per segment
     const uint16_t* x;   // activations (bf16 bits); row m of this pass is x + xrow[m] * ldx
     int64_t ldx;
     float* y;            // output; row m of this pass is y + yrow[m] * ldy
