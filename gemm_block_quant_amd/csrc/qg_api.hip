@@ -146,7 +146,7 @@ qg_status quant_gemm(const void* w, qg_format fmt, int64_t N, int64_t K, int64_t
                    ? QG_OK
                    : QG_EHIP;
     }
-    const int rows = stream_rows_per_pass(fmt, (int)K, (int)(M < 16 ? M : 16));
+    const int rows = stream_rows_per_pass(fmt, N, (int)K, (int)(M < 16 ? M : 16));
     if (rows <= 0) return QG_ESHAPE;
     a.x = x;
     a.ldx = K;

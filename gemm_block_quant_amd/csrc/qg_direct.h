@@ -480,9 +480,16 @@ struct SegLds {
     int mtmax;
 };
 
+// The K range whose activations are staged in LDS: segments [s_lo, s_lo + ns)
+// of every row, i.e. units [u0, u0 + KL / 64).  One phase covers the whole row
+// unless the activations of all rows do not fit in LDS at once.
+struct Phase {
+    int s_lo, ns, u0, KL;
+};
+
 // One wave streams work items handed out by next_item() (an item index local
 // to the workgroup, or a negative value when there are none left): item t is
-// segment t % S of row group rg_base + t / S of mv; row group rg is rows
+// segment ph.s_lo + t % ph.ns of row group rg_base + t / ph.ns of mv; row group rg is rows
 // 4 rg .. 4 rg + 3 (rows >= N idle), lane l serving row l % 4.  A segment is
 // up to PS passes of 16 units, SP passes per ring slot, PF slots in flight;
 // the ring always holds the next PF slots of work, refilled as soon as a slot
@@ -493,8 +500,8 @@ struct SegLds {
 template <int F, int MT, int SP, int PF, class Next, class Between>
 __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int K, const lds_u8* xl,
                                                    const lds_f32* xs, Next next_item, int rg_base, Segments sg,
-                                                   SegLds sl, float* y, int64_t ldy, int64_t yrow, int cnt,
-                                                   Between between) {
+                                                   Phase ph, SegLds sl, float* y, int64_t ldy, int64_t yrow,
+                                                   int cnt, Between between) {
     using D = Direct<F>;
     constexpr int RW = kDirectRows, G = kDirectSlots;
     const int lane = threadIdx.x & 63;
@@ -503,8 +510,8 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
     const int P = (U + G - 1) / G;
     const typename D::Lane L = D::lane_consts(lane);
     const int ub = direct_unit_bytes(F);
-    const int mgb = direct_mg_bytes(F, K);
-    const int xs_mg = direct_xs_mg(F, K);
+    const int mgb = direct_mg_bytes(F, ph.KL);
+    const int xs_mg = direct_xs_mg(F, ph.KL);
     // A-operand row slot of this lane: lane % 4 (slots >= MT read slot 0: their
     // products land in result rows nobody uses)
     const int aslot = (lane & 3) < MT ? (lane & 3) : 0;
@@ -526,7 +533,7 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
     // current item and its pass cursor
     int cur_t = next_item(), cur_p = 0, cur_end = 0;
     auto item_range = [&](int t, int& p0, int& p1) {
-        const int s = t % sg.S;
+        const int s = ph.s_lo + t % ph.ns;
         p0 = s * sg.PS;
         p1 = min(P, p0 + sg.PS);
     };
@@ -539,7 +546,7 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
         sp = cur_p;
         int n = 0;
         if (live) {
-            const int rg = rg_base + cur_t / sg.S;
+            const int rg = rg_base + cur_t / ph.ns;
             n = RW * rg + grp;
             if (n >= N) n = RW * rg;  // idle row of the group: duplicate the group's first row
         }
@@ -573,11 +580,13 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
         for (int p = 0; p < SP; ++p) {
             const int u = (p0 + p) * G + slot;
             const bool live = p0 + p < pend && u < U;
-            const int ux = live ? u : 0;
+            // activations of this phase are staged from unit ph.u0 on (a multiple of
+            // 16, so the bank rotation u % 4 is unchanged)
+            const int ux = live ? u - ph.u0 : 0;
             D::template decode<MT>(r[p], L, ux, live, xa_lane + (size_t)ux * ub, mgb, xs, xs_mg, acc);
         }
         if (last) {
-            const int rgl = t / sg.S, s = t % sg.S;
+            const int rgl = t / ph.ns, s = ph.s_lo + t % ph.ns;
             const int n = RW * (rg_base + rgl) + grp;
             float mine = 0.f;
 #pragma unroll

@@ -8,9 +8,32 @@
 namespace qg {
 
 // The direct kernel's LDS starts with its row-group counter.
-constexpr int kDirectCounterBytes = 16;
+constexpr int kDirectCounterBytes = 64;  // item counters of up to 16 K phases
 
 // LDS one launch needs for `mt` activation rows.
+// Direct path: LDS of one launch with K staged in `nph` phases, for a share of
+// `rgs` row groups.
+static size_t direct_launch_lds(int fmt, int K, int mt, Segments sg, int nph, int64_t rgs) {
+    const int seg_per_ph = (sg.S + nph - 1) / nph;
+    const int U = K / 64;
+    const int KLmax = (U < seg_per_ph * sg.PS * kDirectSlots ? U : seg_per_ph * sg.PS * kDirectSlots) * 64;
+    return kDirectCounterBytes + direct_lds_bytes(fmt, mt, KLmax) + direct_seg_lds_bytes(sg.S, (int)rgs, mt);
+}
+
+// Fewest K phases (at most 16, each a whole number of segments) whose staged
+// activations fit in LDS; 0 when none does.
+static int direct_phases(int fmt, int64_t N, int K, int mt) {
+    const int cus = num_cus();
+    const Segments sg = direct_segments(fmt, N, K, cus);
+    const int64_t groups = (N + kDirectRows - 1) / kDirectRows;
+    // largest share of row groups a workgroup gets (the grid holds at least
+    // min(cus, groups) workgroups)
+    const int64_t rgs = groups > cus ? (groups + cus - 1) / cus : 1;
+    for (int nph = 1; nph <= sg.S && nph <= kDirectCounterBytes / 4; ++nph)
+        if (direct_launch_lds(fmt, K, mt, sg, nph, rgs) <= (size_t)kLdsBytes) return nph;
+    return 0;
+}
+
 size_t stream_lds_bytes(int fmt, int K, int mt) {
     if (direct_eligible(fmt, K))
         return kDirectCounterBytes + direct_lds_bytes(fmt, mt, K) + direct_seg_lds_bytes(2, kDirectSegRgsMax, mt);  // (worst case)
@@ -53,38 +76,57 @@ __global__ __launch_bounds__((direct_waves<F, MT>() * 64)) void k_direct_gemm(co
     lds_u8* smem = (lds_u8*)smem_generic;
     constexpr int RW = kDirectRows;
     const int K = a.K;
-    QG_LDS int* counter = (QG_LDS int*)smem;
+    const Segments sg{a.seg_S > 0 ? a.seg_S : 1, a.seg_PS > 0 ? a.seg_PS : 1};
+    const int nph = a.phases > 0 ? a.phases : 1;
+    const int seg_per_ph = (sg.S + nph - 1) / nph;
+    const int U = K / 64;
+    // LDS: one item counter per phase, then the activations of the longest
+    // phase and their sums, then the segment sums
+    const int KLmax = min(U, seg_per_ph * sg.PS * kDirectSlots) * 64;
+    QG_LDS int* counters = (QG_LDS int*)smem;
     lds_u8* xl = smem + kDirectCounterBytes;
-    lds_f32* xs = (lds_f32*)(xl + (size_t)direct_mg(MT) * direct_mg_bytes(F, K));
+    lds_f32* xs = (lds_f32*)(xl + (size_t)direct_mg(MT) * direct_mg_bytes(F, KLmax));
     const int lane = threadIdx.x & 63;
     const int li = direct_out_slot(lane);
     const int groups = (a.N + RW - 1) / RW;
     const int per = (groups + gridDim.x - 1) / gridDim.x;
     const int g0 = blockIdx.x * per, g1 = min(groups, g0 + per);
-    const Segments sg{a.seg_S > 0 ? a.seg_S : 1, a.seg_PS > 0 ? a.seg_PS : 1};
-    const int items = (g1 > g0 ? g1 - g0 : 0) * sg.S;
+    const int rgs = g1 > g0 ? g1 - g0 : 0;
     // segment sums after the activations: progress[per], then total[per][4][MT]
     SegLds sl;
-    sl.progress = (QG_LDS int*)(xl + direct_lds_bytes(F, MT, K));
+    sl.progress = (QG_LDS int*)(xl + direct_lds_bytes(F, MT, KLmax));
     sl.total = (lds_f32*)((lds_u8*)sl.progress + ((size_t)per * 4 + 15) / 16 * 16);
     sl.mtmax = MT;
-    if (threadIdx.x == 0) *counter = 0;
+    if (threadIdx.x < kDirectCounterBytes / 4) counters[threadIdx.x] = 0;
     if (sg.S > 1)
         for (int i = threadIdx.x; i < per; i += blockDim.x) sl.progress[i] = 0;
-    auto next_item = [&]() {
-        int t = 0;
-        if (lane == 0) t = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        t = __builtin_amdgcn_readfirstlane(t);
-        return t < items ? t : -1;
-    };
     MatView mv = {a.w0, a.rb0, a.w1, a.rb1, a.gbytes};
     const int64_t yrow = a.yrow[li < a.M ? li : 0];
     auto row_of = [&](int m) { return a.xrow[m]; };
-    XStage<F, MT, 2> xst;
-    xst.issue(a.x, a.ldx, a.M, K, row_of);
-    __syncthreads();  // the counter and progress are initialised before any wave takes work
-    auto between = [&] { xst.commit(xl, xs, a.x, a.ldx, a.M, K, row_of); };
-    wave_stream_direct<F, MT, SP, PF>(mv, a.N, K, xl, xs, next_item, g0, sg, sl, a.y, a.ldy, yrow, a.M, between);
+    for (int p = 0; p < nph; ++p) {
+        Phase ph;
+        ph.s_lo = p * seg_per_ph;
+        ph.ns = min(sg.S, ph.s_lo + seg_per_ph) - ph.s_lo;
+        ph.u0 = ph.s_lo * sg.PS * kDirectSlots;
+        ph.KL = (min(U, (ph.s_lo + ph.ns) * sg.PS * kDirectSlots) - ph.u0) * 64;
+        const int items = rgs * ph.ns;
+        QG_LDS int* counter = counters + p;
+        auto next_item = [&]() {
+            int t = 0;
+            if (lane == 0) t = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            t = __builtin_amdgcn_readfirstlane(t);
+            return t < items ? t : -1;
+        };
+        const uint16_t* xp = a.x + (size_t)ph.u0 * 64;
+        XStage<F, MT, 2> xst;
+        xst.issue(xp, a.ldx, a.M, ph.KL, row_of);
+        // the counters and progress are initialised, and every wave is done with
+        // the previous phase's activations, before any wave goes on
+        __syncthreads();
+        auto between = [&] { xst.commit(xl, xs, xp, a.ldx, a.M, ph.KL, row_of); };
+        wave_stream_direct<F, MT, SP, PF>(mv, a.N, K, xl, xs, next_item, g0, sg, ph, sl, a.y, a.ldy, yrow, a.M,
+                                          between);
+    }
 }
 
 // Persistent grid: as many 4-wave workgroups as can be resident at once (by
@@ -131,12 +173,14 @@ static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
     const Segments sg = direct_segments(F, a.N, a.K, num_cus());
     a.seg_S = sg.S;
     a.seg_PS = sg.PS;
+    a.phases = direct_phases(F, a.N, a.K, MT);
+    if (a.phases <= 0) return hipErrorInvalidValue;
     auto kern = k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF>;
     constexpr int RW = kDirectRows;
     const long groups = (a.N + RW - 1) / RW;
-    // grid from the residency without the segment sums, then their LDS for the
-    // resulting share of row groups (and the residency again)
-    size_t lds = kDirectCounterBytes + direct_lds_bytes(F, MT, a.K);
+    // grid from the residency, then the LDS for the resulting share of row
+    // groups (and the residency again)
+    size_t lds = direct_launch_lds(F, a.K, MT, sg, a.phases, 1);
     long grid = 0;
     for (int pass = 0; pass < 2; ++pass) {
         int fit = 0;
@@ -145,7 +189,7 @@ static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
         grid = (long)num_cus() * fit;
         if (grid > groups) grid = groups;
         const long per = (groups + grid - 1) / grid;
-        lds = kDirectCounterBytes + direct_lds_bytes(F, MT, a.K) + direct_seg_lds_bytes(sg.S, (int)per, MT);
+        lds = direct_launch_lds(F, a.K, MT, sg, a.phases, per);
     }
     if (lds > (size_t)kLdsBytes) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(direct_waves<F, MT>() * 64), lds, st, a);
@@ -182,12 +226,14 @@ static int mt_for(int m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 
 // Activation rows one pass of the streaming kernel can take: the largest of
 // 16, 8, 4, 2, 1 (capped by M) whose LDS needs fit in 160 KB.  0 when not
 // even one row fits.
-int stream_rows_per_pass(int fmt, int K, int M) {
+int stream_rows_per_pass(int fmt, int64_t N, int K, int M) {
     const int cands[5] = {16, 8, 4, 2, 1};
     for (int i = 0; i < 5; ++i) {
         const int mt = cands[i];
         if (mt > 1 && mt / 2 >= M) continue;  // a smaller instantiation already covers M
-        if (stream_lds_bytes(fmt, K, mt) <= (size_t)kLdsBytes) return mt < M ? mt : M;
+        const bool fits = direct_eligible(fmt, K) ? direct_phases(fmt, N, K, mt) > 0
+                                                  : stream_lds_bytes(fmt, K, mt) <= (size_t)kLdsBytes;
+        if (fits) return mt < M ? mt : M;
     }
     return 0;
 }

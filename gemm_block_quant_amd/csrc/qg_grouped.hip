@@ -184,15 +184,16 @@ __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32
                 XStage<F, MT, 1> xst;
                 xst.issue(a.x, a.ldx, cnt, K, row_of);
                 auto between = [&] { xst.commit(xl, xs, a.x, a.ldx, cnt, K, row_of); };
-                const int items = rgs * sg.S;
+                const int items = rgs * sg.S;  // one phase: the whole row
                 int next = wid;
                 auto next_item = [&]() {
                     const int t = next;
                     next += kWavesPerBlock;
                     return t < items ? t : -1;
                 };
-                wave_stream_direct<F, MT, SP, PF>(mv, n_end, K, xl, xs, next_item, rg0, sg, sl, a.y, a.ldy, yrow,
-                                                  cnt, between);
+                const Phase ph{0, sg.S, 0, K};
+                wave_stream_direct<F, MT, SP, PF>(mv, n_end, K, xl, xs, next_item, rg0, sg, ph, sl, a.y, a.ldy,
+                                                  yrow, cnt, between);
             } else {
                 auto stage = [&] { stage_x<MT, kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of); };
                 wave_stream<F, MT, CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf, rowbuf_s,

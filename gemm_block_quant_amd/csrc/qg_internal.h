@@ -19,6 +19,7 @@ struct StreamArgs {
     int N, K;
     int seg_blocks, nseg;  // row-buffer path: filled by the dispatcher
     int seg_S, seg_PS;     // direct path: K segments per row and passes per segment
+    int phases;            // direct path: K phases of staged activations (1: the whole row)
     const uint16_t* x;   // activations (bf16 bits); row m of this pass is x + xrow[m] * ldx
     int64_t ldx;
     float* y;            // output; row m of this pass is y + yrow[m] * ldy
@@ -29,7 +30,7 @@ struct StreamArgs {
 };
 
 hipError_t launch_stream_gemm(int fmt, StreamArgs a, hipStream_t st);
-int stream_rows_per_pass(int fmt, int K, int M);
+int stream_rows_per_pass(int fmt, int64_t N, int K, int M);
 size_t stream_lds_bytes(int fmt, int K, int mt);
 
 // Grouped-expert product: bucketing + streaming over the distinct experts.
