@@ -497,12 +497,20 @@ struct Phase {
 // activation row s (yrow given for that slot).  between() runs once, after
 // the first PF slots are in flight (the activation staging: a workgroup
 // barrier inside, so every wave of the workgroup must call this function).
-template <int F, int MT, int SP, int PF, class Next, class Between>
+// SEG false: the caller has one segment per row and one phase over all of K
+// (sg and ph are then ignored).
+template <int F, int MT, int SP, int PF, bool SEG, class Next, class Between>
 __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int K, const lds_u8* xl,
                                                    const lds_f32* xs, Next next_item, int rg_base, Segments sg,
                                                    Phase ph, SegLds sl, float* y, int64_t ldy, int64_t yrow,
                                                    int cnt, Between between) {
     using D = Direct<F>;
+    if (!SEG) {
+        // one segment per row, one phase: constants the compiler can fold
+        sg.S = 1;
+        sg.PS = (D::units_per_row(K) + kDirectSlots - 1) / kDirectSlots;
+        ph = Phase{0, 1, 0, K};
+    }
     constexpr int RW = kDirectRows, G = kDirectSlots;
     const int lane = threadIdx.x & 63;
     const int grp = lane & 3, slot = lane >> 2;
@@ -526,27 +534,40 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
     }
 
     uint32_t R[PF][SP][D::REGS];
-    // per slot: item (< 0: none), first pass, and whether it ends the item
-    int slot_t[PF], slot_p[PF];
+    // Per ring slot: local row group of its item (< 0: none), segment, first
+    // pass, end pass of the segment, and whether the slot ends the item.
+    int slot_g[PF], slot_s[PF], slot_p[PF], slot_e[PF];
     bool slot_last[PF];
 
-    // current item and its pass cursor
-    int cur_t = next_item(), cur_p = 0, cur_end = 0;
-    auto item_range = [&](int t, int& p0, int& p1) {
-        const int s = ph.s_lo + t % ph.ns;
-        p0 = s * sg.PS;
-        p1 = min(P, p0 + sg.PS);
+    // current item: local row group, segment, pass cursor and end pass
+    int cur_g = -1, cur_s = 0, cur_p = 0, cur_end = 0;
+    auto fetch = [&]() {
+        const int t = next_item();
+        cur_g = -1;
+        if (t >= 0) {
+            int q = t, r = 0;
+            if (ph.ns > 1) {
+                q = t / ph.ns;
+                r = t - q * ph.ns;
+            }
+            cur_g = q;
+            cur_s = ph.s_lo + r;
+            cur_p = cur_s * sg.PS;
+            cur_end = min(P, cur_p + sg.PS);
+        }
     };
-    if (cur_t >= 0) item_range(cur_t, cur_p, cur_end);
+    fetch();
     // Issues the next SP passes of work into a slot; with no work left it
     // loads unit 0 of row 0 (every path issues the same loads).
-    auto issue = [&](uint32_t (&r)[SP][D::REGS], int& st, int& sp, bool& slast) {
-        const bool live = cur_t >= 0;
-        st = cur_t;
+    auto issue = [&](uint32_t (&r)[SP][D::REGS], int& sgi, int& ss, int& sp, int& se, bool& slast) {
+        const bool live = cur_g >= 0;
+        sgi = cur_g;
+        ss = cur_s;
         sp = cur_p;
+        se = cur_end;
         int n = 0;
         if (live) {
-            const int rg = rg_base + cur_t / ph.ns;
+            const int rg = rg_base + cur_g;
             n = RW * rg + grp;
             if (n >= N) n = RW * rg;  // idle row of the group: duplicate the group's first row
         }
@@ -563,8 +584,7 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
             cur_p += SP;
             if (cur_p >= cur_end) {
                 slast = true;
-                cur_t = next_item();
-                if (cur_t >= 0) item_range(cur_t, cur_p, cur_end);
+                fetch();
             }
         }
     };
@@ -573,9 +593,7 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.f;
 
-    auto process = [&](const uint32_t (&r)[SP][D::REGS], int t, int p0, bool last) {
-        int pe, pend;
-        item_range(t, pe, pend);
+    auto process = [&](const uint32_t (&r)[SP][D::REGS], int rgl, int s, int p0, int pend, bool last) {
 #pragma unroll
         for (int p = 0; p < SP; ++p) {
             const int u = (p0 + p) * G + slot;
@@ -586,7 +604,6 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
             D::template decode<MT>(r[p], L, ux, live, xa_lane + (size_t)ux * ub, mgb, xs, xs_mg, acc);
         }
         if (last) {
-            const int rgl = t / ph.ns, s = ph.s_lo + t % ph.ns;
             const int n = RW * (rg_base + rgl) + grp;
             float mine = 0.f;
 #pragma unroll
@@ -620,13 +637,13 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
     };
 
 #pragma unroll
-    for (int k = 0; k < PF; ++k) issue(R[k], slot_t[k], slot_p[k], slot_last[k]);
+    for (int k = 0; k < PF; ++k) issue(R[k], slot_g[k], slot_s[k], slot_p[k], slot_e[k], slot_last[k]);
     between();
-    while (slot_t[0] >= 0) {
+    while (slot_g[0] >= 0) {
 #pragma unroll
         for (int k = 0; k < PF; ++k) {
-            if (slot_t[k] >= 0) process(R[k], slot_t[k], slot_p[k], slot_last[k]);
-            issue(R[k], slot_t[k], slot_p[k], slot_last[k]);
+            if (slot_g[k] >= 0) process(R[k], slot_g[k], slot_s[k], slot_p[k], slot_e[k], slot_last[k]);
+            issue(R[k], slot_g[k], slot_s[k], slot_p[k], slot_e[k], slot_last[k]);
         }
     }
 }

@@ -70,16 +70,18 @@ __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
 // need more registers than 4 waves per SIMD allow.
 template <int F, int MT> constexpr int direct_waves() { return MT >= 16 || (F == QG_Q6_K && MT >= 8) ? 8 : 16; }
 
-template <int F, int MT, int SP, int PF>
+// SEG false: one K segment and one phase (the launch guarantees it).
+template <int F, int MT, int SP, int PF, bool SEG>
 __global__ __launch_bounds__((direct_waves<F, MT>() * 64)) void k_direct_gemm(const StreamArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8* smem = (lds_u8*)smem_generic;
     constexpr int RW = kDirectRows;
     const int K = a.K;
-    const Segments sg{a.seg_S > 0 ? a.seg_S : 1, a.seg_PS > 0 ? a.seg_PS : 1};
-    const int nph = a.phases > 0 ? a.phases : 1;
-    const int seg_per_ph = (sg.S + nph - 1) / nph;
     const int U = K / 64;
+    const Segments sg = SEG ? Segments{a.seg_S > 0 ? a.seg_S : 1, a.seg_PS > 0 ? a.seg_PS : 1}
+                            : Segments{1, (U + kDirectSlots - 1) / kDirectSlots};
+    const int nph = SEG && a.phases > 0 ? a.phases : 1;
+    const int seg_per_ph = (sg.S + nph - 1) / nph;
     // LDS: one item counter per phase, then the activations of the longest
     // phase and their sums, then the segment sums
     const int KLmax = min(U, seg_per_ph * sg.PS * kDirectSlots) * 64;
@@ -98,7 +100,7 @@ __global__ __launch_bounds__((direct_waves<F, MT>() * 64)) void k_direct_gemm(co
     sl.total = (lds_f32*)((lds_u8*)sl.progress + ((size_t)per * 4 + 15) / 16 * 16);
     sl.mtmax = MT;
     if (threadIdx.x < kDirectCounterBytes / 4) counters[threadIdx.x] = 0;
-    if (sg.S > 1)
+    if (SEG && sg.S > 1)
         for (int i = threadIdx.x; i < per; i += blockDim.x) sl.progress[i] = 0;
     MatView mv = {a.w0, a.rb0, a.w1, a.rb1, a.gbytes};
     const int64_t yrow = a.yrow[li < a.M ? li : 0];
@@ -124,8 +126,8 @@ __global__ __launch_bounds__((direct_waves<F, MT>() * 64)) void k_direct_gemm(co
         // the previous phase's activations, before any wave goes on
         __syncthreads();
         auto between = [&] { xst.commit(xl, xs, xp, a.ldx, a.M, ph.KL, row_of); };
-        wave_stream_direct<F, MT, SP, PF>(mv, a.N, K, xl, xs, next_item, g0, sg, ph, sl, a.y, a.ldy, yrow, a.M,
-                                          between);
+        wave_stream_direct<F, MT, SP, PF, SEG>(mv, a.N, K, xl, xs, next_item, g0, sg, ph, sl, a.y, a.ldy, yrow,
+                                               a.M, between);
     }
 }
 
@@ -175,7 +177,8 @@ static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
     a.seg_PS = sg.PS;
     a.phases = direct_phases(F, a.N, a.K, MT);
     if (a.phases <= 0) return hipErrorInvalidValue;
-    auto kern = k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF>;
+    auto kern = sg.S > 1 || a.phases > 1 ? k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF, true>
+                                         : k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF, false>;
     constexpr int RW = kDirectRows;
     const long groups = (a.N + RW - 1) / RW;
     // grid from the residency, then the LDS for the resulting share of row

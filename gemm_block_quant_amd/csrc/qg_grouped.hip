@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32
                     return t < items ? t : -1;
                 };
                 const Phase ph{0, sg.S, 0, K};
-                wave_stream_direct<F, MT, SP, PF>(mv, n_end, K, xl, xs, next_item, rg0, sg, ph, sl, a.y, a.ldy,
+                wave_stream_direct<F, MT, SP, PF, true>(mv, n_end, K, xl, xs, next_item, rg0, sg, ph, sl, a.y, a.ldy,
                                                   yrow, cnt, between);
             } else {
                 auto stage = [&] { stage_x<MT, kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of); };

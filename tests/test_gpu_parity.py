@@ -100,10 +100,13 @@ def test_product_band(fmt, N, K, M):
     assert_band(y, y_ref, bound, "fmt %d N %d K %d M %d" % (fmt, N, K, M))
 
 
-@pytest.mark.parametrize("fmt,K", [(qg.Q8_0, 1024), (qg.Q4_K, 5120), (qg.Q6_K, 17408), (qg.NVFP4, 5120)])
-def test_rows_match_decode_bitwise_and_repeat(fmt, K):
+@pytest.mark.parametrize("fmt,N,K", [(qg.Q8_0, 300, 1024), (qg.Q4_K, 300, 5120), (qg.Q6_K, 300, 17408),
+                                     (qg.NVFP4, 300, 5120),
+                                     # tall: up to 8 rows take the whole-row-group kernel, 16 the direct one
+                                     (qg.Q4_K, 16385, 5120), (qg.NVFP4, 16387, 5120)])
+def test_rows_match_decode_bitwise_and_repeat(fmt, N, K):
     """Row m of M = 8 (and M = 16) equals the M = 1 result bit for bit; runs repeat."""
-    N, M = 300, 16
+    M = 16
     w, x = make_case(fmt, N, K, M, seed=55)
     wd, xd = dev_bytes(w), dev_x(x)
     y16 = qg.quant_gemm(wd, fmt, N, K, M, xd).cpu().numpy()
@@ -131,7 +134,9 @@ def test_zero_activations_and_zero_weights():
 FULL = [
     # the workload shapes: Q8_0 1024x1024; Q4_K fused gate+up; Q6_K down and LM head; NVFP4 both MLP shapes
     (qg.Q8_0, 1024, 1024, 1),
-    (qg.Q4_K, 2 * 17408, 5120, 1),
+    (qg.Q4_K, 2 * 17408, 5120, 1), (qg.Q4_K, 2 * 17408, 5120, 8),
+    # tall with a ragged last row group (whole-row-group kernel)
+    (qg.Q4_K, 16385, 5120, 3), (qg.NVFP4, 16387, 5120, 5),
     (qg.Q6_K, 5120, 17408, 1), (qg.Q6_K, 5120, 17408, 8),
     (qg.Q6_K, 248320, 5120, 1), (qg.Q6_K, 248320, 5120, 8),
     (qg.NVFP4, 17408, 5120, 1), (qg.NVFP4, 17408, 5120, 8),
