@@ -107,12 +107,22 @@ template <> struct Direct<QG_Q4_K> {
         return L;
     }
     __device__ __host__ static int units_per_row(int K) { return (K / 256) * 4; }
-    __device__ static void load(uint32_t (&r)[REGS], const uint8_t* row, const uint8_t*, int u) {
-        const uint8_t* blk = row + 144 * (u >> 2);
-        const uint8_t* q = blk + 16 + 32 * (u & 3);
+    // Bytes of one pass (16 units = 4 super-blocks) of a row.
+    static constexpr int PASS0 = 4 * 144, PASS1 = 0;
+    // Offsets from the start of a pass's stretch of the row: code bytes of
+    // the unit (a) and its super-block header (b).
+    struct Offs {
+        uint32_t a, b;
+    };
+    __device__ static Offs slot_offs(int s) {
+        return Offs{144u * (uint32_t)(s >> 2) + 16u + 32u * (uint32_t)(s & 3), 144u * (uint32_t)(s >> 2)};
+    }
+    __device__ static Offs shift(const Offs& o, uint32_t r0, uint32_t) { return Offs{o.a + r0, o.b + r0}; }
+    __device__ static Offs pick(bool c, const Offs& x, const Offs& y) { return Offs{c ? x.a : y.a, c ? x.b : y.b}; }
+    __device__ static void load_at(uint32_t (&r)[REGS], const uint8_t* b0, const uint8_t*, const Offs& o) {
         // Plain (cached) loads: the three loads of a lane touch the same lines as
         // those of its neighbours, and non-temporal loads fetched them again.
-        const u32x4 qa = ld_global128(q), qb = ld_global128(q + 16), h = ld_global128(blk);
+        const u32x4 qa = ld_global128(b0 + o.a), qb = ld_global128(b0 + o.a + 16), h = ld_global128(b0 + o.b);
         r[0] = qa.x; r[1] = qa.y; r[2] = qa.z; r[3] = qa.w;
         r[4] = qb.x; r[5] = qb.y; r[6] = qb.z; r[7] = qb.w;
         r[8] = h.x; r[9] = h.y; r[10] = h.z; r[11] = h.w;
@@ -194,11 +204,20 @@ template <> struct Direct<QG_NVFP4> {
     struct Lane {};
     __device__ static Lane lane_consts(int) { return Lane{}; }
     __device__ __host__ static int units_per_row(int K) { return K / 64; }
-    __device__ static void load(uint32_t (&r)[REGS], const uint8_t* row_codes, const uint8_t* row_scales, int u) {
-        const u32x4 q0 = ld_stream128(row_codes + 32 * u), q1 = ld_stream128(row_codes + 32 * u + 16);
+    // Bytes of one pass (16 units) of a row: codes, scales.
+    static constexpr int PASS0 = 16 * 32, PASS1 = 16 * 4;
+    // Offsets from the start of a pass's stretch: codes (a), scales (b).
+    struct Offs {
+        uint32_t a, b;
+    };
+    __device__ static Offs slot_offs(int s) { return Offs{32u * (uint32_t)s, 4u * (uint32_t)s}; }
+    __device__ static Offs shift(const Offs& o, uint32_t r0, uint32_t r1) { return Offs{o.a + r0, o.b + r1}; }
+    __device__ static Offs pick(bool c, const Offs& x, const Offs& y) { return Offs{c ? x.a : y.a, c ? x.b : y.b}; }
+    __device__ static void load_at(uint32_t (&r)[REGS], const uint8_t* b0, const uint8_t* b1, const Offs& o) {
+        const u32x4 q0 = ld_stream128(b0 + o.a), q1 = ld_stream128(b0 + o.a + 16);
         r[0] = q0.x; r[1] = q0.y; r[2] = q0.z; r[3] = q0.w;
         r[4] = q1.x; r[5] = q1.y; r[6] = q1.z; r[7] = q1.w;
-        r[8] = __builtin_nontemporal_load((const QG_GLOBAL uint32_t*)(uintptr_t)(row_scales + 4 * u));
+        r[8] = __builtin_nontemporal_load((const QG_GLOBAL uint32_t*)(uintptr_t)(b1 + o.b));
     }
     template <int MT>
     __device__ static void decode(const uint32_t (&r)[REGS], const Lane&, int u, bool live, const lds_u8* xa,
@@ -262,18 +281,34 @@ template <> struct Direct<QG_Q6_K> {
     };
     __device__ static Lane lane_consts(int lane) { return Lane{8u * (uint32_t)((lane >> 2) & 1)}; }
     __device__ __host__ static int units_per_row(int K) { return (K / 256) * 4; }
-    __device__ static void load(uint32_t (&r)[REGS], const uint8_t* row, const uint8_t*, int u) {
-        const uint8_t* blk = row + 210 * (u >> 2);
-        const int h = (u >> 1) & 1, t = u & 1;
-        const u32x4 qa = ld_global128_a2(blk + 64 * h + 16 * t);
-        const u32x4 qb = ld_global128_a2(blk + 64 * h + 32 + 16 * t);
-        const u32x4 qh = ld_global128_a2(blk + 128 + 32 * h + 16 * t);
-        const u32x2 sc = ld_global64_a2(blk + 192 + 8 * h);
+    // Bytes of one pass (16 units = 4 blocks) of a row.
+    static constexpr int PASS0 = 4 * 210, PASS1 = 0;
+    // Offsets from the start of a pass's stretch: low-nibble codes (a; the
+    // second half at a + 32), high bits (b), sub-scales (c), block start (d;
+    // the fp16 scale at d + 208).
+    struct Offs {
+        uint32_t a, b, c, d;
+    };
+    __device__ static Offs slot_offs(int s) {
+        const uint32_t blk = 210u * (uint32_t)(s >> 2), h = (uint32_t)(s >> 1) & 1u, t = (uint32_t)s & 1u;
+        return Offs{blk + 64u * h + 16u * t, blk + 128u + 32u * h + 16u * t, blk + 192u + 8u * h, blk};
+    }
+    __device__ static Offs shift(const Offs& o, uint32_t r0, uint32_t) {
+        return Offs{o.a + r0, o.b + r0, o.c + r0, o.d + r0};
+    }
+    __device__ static Offs pick(bool c, const Offs& x, const Offs& y) {
+        return Offs{c ? x.a : y.a, c ? x.b : y.b, c ? x.c : y.c, c ? x.d : y.d};
+    }
+    __device__ static void load_at(uint32_t (&r)[REGS], const uint8_t* b0, const uint8_t*, const Offs& o) {
+        const u32x4 qa = ld_global128_a2(b0 + o.a);
+        const u32x4 qb = ld_global128_a2(b0 + o.a + 32);
+        const u32x4 qh = ld_global128_a2(b0 + o.b);
+        const u32x2 sc = ld_global64_a2(b0 + o.c);
         r[0] = qa.x; r[1] = qa.y; r[2] = qa.z; r[3] = qa.w;
         r[4] = qb.x; r[5] = qb.y; r[6] = qb.z; r[7] = qb.w;
         r[8] = qh.x; r[9] = qh.y; r[10] = qh.z; r[11] = qh.w;
         r[12] = sc.x; r[13] = sc.y;
-        r[14] = ld_global16(blk + 208);
+        r[14] = ld_global16(b0 + o.d + 208);
     }
     template <int MT>
     __device__ static void decode(const uint32_t (&r)[REGS], const Lane& L, int u, bool live, const lds_u8* xa,
@@ -505,21 +540,18 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
                                                    Phase ph, SegLds sl, float* y, int64_t ldy, int64_t yrow,
                                                    int cnt, Between between) {
     using D = Direct<F>;
-    if (!SEG) {
-        // one segment per row, one phase: constants the compiler can fold
-        sg.S = 1;
-        sg.PS = (D::units_per_row(K) + kDirectSlots - 1) / kDirectSlots;
-        ph = Phase{0, 1, 0, K};
-    }
     constexpr int RW = kDirectRows, G = kDirectSlots;
     const int lane = threadIdx.x & 63;
     const int grp = lane & 3, slot = lane >> 2;
     const int U = D::units_per_row(K);
     const int P = (U + G - 1) / G;
+    // segments and phase (compile-time one segment, one phase when !SEG)
+    const int S = SEG ? sg.S : 1, PS = SEG ? sg.PS : P;
+    const int NS = SEG ? ph.ns : 1, SLO = SEG ? ph.s_lo : 0, U0 = SEG ? ph.u0 : 0, KL = SEG ? ph.KL : K;
     const typename D::Lane L = D::lane_consts(lane);
     const int ub = direct_unit_bytes(F);
-    const int mgb = direct_mg_bytes(F, ph.KL);
-    const int xs_mg = direct_xs_mg(F, ph.KL);
+    const int mgb = direct_mg_bytes(F, KL);
+    const int xs_mg = direct_xs_mg(F, KL);
     // A-operand row slot of this lane: lane % 4 (slots >= MT read slot 0: their
     // products land in result rows nobody uses)
     const int aslot = (lane & 3) < MT ? (lane & 3) : 0;
@@ -539,45 +571,62 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
     int slot_g[PF], slot_s[PF], slot_p[PF], slot_e[PF];
     bool slot_last[PF];
 
-    // current item: local row group, segment, pass cursor and end pass
+    // Load addresses: a uniform base per (row group, pass) and per-lane
+    // offsets fixed for the whole run (unit slot, row of the group), so a pass
+    // costs no per-lane address arithmetic.  On a last, partial pass (U not a
+    // multiple of 16) slots past the row's end read a live slot of that pass.
+    const typename D::Offs o_slot = D::slot_offs(slot);
+    const int live_last = U - (P - 1) * G;  // live slots of the last pass, 1..16
+    const typename D::Offs o_last = D::slot_offs(slot < live_last ? slot : slot % live_last);
+    const uint32_t lrow0 = (uint32_t)grp * (uint32_t)mv.rb0;
+    const uint32_t lrow1 = F == QG_NVFP4 ? (uint32_t)grp * (uint32_t)mv.rb1 : 0u;
+
+    // current item: local row group, segment, pass cursor and end pass; its
+    // row group's bases and this lane's offsets (rows past N read the group's
+    // first row).  With no work left the bases stay those of the last item
+    // (initially row 0), so every load stays in the matrix.
     int cur_g = -1, cur_s = 0, cur_p = 0, cur_end = 0;
+    const uint8_t *cur_b0 = mv.w0, *cur_b1 = mv.w1;
+    typename D::Offs cur_o = o_slot, cur_ol = o_last;
     auto fetch = [&]() {
         const int t = next_item();
         cur_g = -1;
         if (t >= 0) {
             int q = t, r = 0;
-            if (ph.ns > 1) {
-                q = t / ph.ns;
-                r = t - q * ph.ns;
+            if (NS > 1) {
+                q = t / NS;
+                r = t - q * NS;
             }
             cur_g = q;
-            cur_s = ph.s_lo + r;
-            cur_p = cur_s * sg.PS;
-            cur_end = min(P, cur_p + sg.PS);
+            cur_s = SLO + r;
+            cur_p = cur_s * PS;
+            cur_end = min(P, cur_p + PS);
+            const int rg = rg_base + q;
+            cur_b0 = mv.w0 + (size_t)(RW * rg) * mv.rb0;
+            cur_b1 = F == QG_NVFP4 ? mv.w1 + (size_t)(RW * rg) * mv.rb1 : nullptr;
+            const bool real = RW * rg + grp < N;
+            cur_o = D::shift(o_slot, real ? lrow0 : 0u, real ? lrow1 : 0u);
+            cur_ol = D::shift(o_last, real ? lrow0 : 0u, real ? lrow1 : 0u);
         }
     };
     fetch();
-    // Issues the next SP passes of work into a slot; with no work left it
-    // loads unit 0 of row 0 (every path issues the same loads).
+    // Issues the next SP passes of work into a slot (with no work left, loads
+    // that stay in one line: every path issues the same loads).
     auto issue = [&](uint32_t (&r)[SP][D::REGS], int& sgi, int& ss, int& sp, int& se, bool& slast) {
         const bool live = cur_g >= 0;
         sgi = cur_g;
         ss = cur_s;
         sp = cur_p;
         se = cur_end;
-        int n = 0;
-        if (live) {
-            const int rg = rg_base + cur_g;
-            n = RW * rg + grp;
-            if (n >= N) n = RW * rg;  // idle row of the group: duplicate the group's first row
-        }
-        const uint8_t* rc = mv.w0 + (size_t)n * mv.rb0;
-        const uint8_t* rs = F == QG_NVFP4 ? mv.w1 + (size_t)n * mv.rb1 : nullptr;
 #pragma unroll
         for (int p = 0; p < SP; ++p) {
-            const int pass = live ? cur_p + p : 0;
-            const int u = pass * G + slot;
-            D::load(r[p], rc, rs, (live && pass < cur_end && u < U) ? u : 0);
+            // passes past the item's end (SP > 1) repeat its first pass
+            const int pass = !live ? 0 : (cur_p + p < cur_end ? cur_p + p : cur_p);
+            const bool partial = (pass + 1) * G > U;
+            // no work: every lane loads the first bytes of the last row group
+            // (one line; nothing streams for a dead slot)
+            D::load_at(r[p], cur_b0 + (size_t)pass * D::PASS0, cur_b1 + (size_t)pass * D::PASS1,
+                       D::pick(live, D::pick(partial, cur_ol, cur_o), typename D::Offs{}));
         }
         slast = false;
         if (live) {
@@ -598,9 +647,9 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
         for (int p = 0; p < SP; ++p) {
             const int u = (p0 + p) * G + slot;
             const bool live = p0 + p < pend && u < U;
-            // activations of this phase are staged from unit ph.u0 on (a multiple of
+            // activations of this phase are staged from unit U0 on (a multiple of
             // 16, so the bank rotation u % 4 is unchanged)
-            const int ux = live ? u - ph.u0 : 0;
+            const int ux = live ? u - U0 : 0;
             D::template decode<MT>(r[p], L, ux, live, xa_lane + (size_t)ux * ub, mgb, xs, xs_mg, acc);
         }
         if (last) {
@@ -612,7 +661,7 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
                 if (slot == m) mine = tot;
                 acc[m] = 0.f;
             }
-            if (sg.S > 1) {
+            if (S > 1) {
                 // add this segment after the ones before it, in segment order
                 // (the oldest unfinished item never waits, so this ends; the
                 // bound only guarantees that every wave exits)
@@ -629,7 +678,7 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
                 }
                 __hip_atomic_store(prog, s + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
-            if (s == sg.S - 1) {
+            if (s == S - 1) {
                 if (F == QG_NVFP4) mine *= gscale;
                 if (slot < cnt && n < N) st_global_f32(y + yrow * ldy + n, mine);
             }
