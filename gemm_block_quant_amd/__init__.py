@@ -64,6 +64,8 @@ def lib():
     L.quant_dequantize_stacked.restype = i32
     L.quant_status_string.argtypes = [i32]
     L.quant_status_string.restype = ctypes.c_char_p
+    L.quant_read_probe.argtypes = [vp, sz, vp, vp]
+    L.quant_read_probe.restype = i32
     _lib = L
     return L
 
@@ -189,3 +191,12 @@ def quant_dequantize_stacked(w, fmt: int, E: int, N: int, K: int, out=None, stre
                                         _dev_ptr(out, "out", 4 * E * N * K), _stream(stream))
     _check(st, "quant_dequantize_stacked")
     return out
+
+
+def quant_read_probe(buf, sink, stream=None):
+    """Plain streaming read of every byte of the device tensor `buf` (a
+    measurement reference, not part of the product path); `sink` is a device
+    int32/uint32 tensor of at least one element."""
+    nbytes = buf.numel() * buf.element_size()
+    st = lib().quant_read_probe(_dev_ptr(buf, "buf", nbytes), nbytes, _dev_ptr(sink, "sink", 4), _stream(stream))
+    _check(st, "quant_read_probe")

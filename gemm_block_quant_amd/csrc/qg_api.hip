@@ -103,6 +103,26 @@ hipError_t kernel_residency(const void* fn, size_t lds, int* per_cu, int block) 
     return hipSuccess;
 }
 
+// Plain streaming read (measurement reference): every 16-byte granule of the
+// buffer once, non-temporal, eight loads in flight per thread, grid-stride.
+__global__ __launch_bounds__(256) void k_read_probe(const u32x4* __restrict__ p, size_t n16, uint32_t* sink) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load((const QG_GLOBAL u32x4*)(p + i + u * stride));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 v = __builtin_nontemporal_load((const QG_GLOBAL u32x4*)(p + i));
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9E3779B9u) *sink = acc;  // keeps the loads; practically never taken
+}
+
 }  // namespace qg
 
 extern "C" {
@@ -207,6 +227,20 @@ qg_status quant_dequantize_stacked(const void* w, qg_format fmt, int64_t E, int6
 
 qg_status quant_dequantize(const void* w, qg_format fmt, int64_t rows, int64_t K, float* out, void* stream) {
     return quant_dequantize_stacked(w, fmt, 1, rows, K, out, stream);
+}
+
+qg_status quant_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink) return QG_EINVAL;
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return QG_EALIGN;
+    if (bytes % 16) return QG_ESHAPE;
+    if (bytes == 0) return QG_OK;
+    const size_t n16 = bytes / 16;
+    size_t grid = (size_t)qg::num_cus() * 64;  // 64 workgroups per CU: the fastest shape measured
+    const size_t need = (n16 + 255) / 256;
+    if (grid > need) grid = need;
+    hipLaunchKernelGGL(qg::k_read_probe, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
+                       (const qg::u32x4*)buf, n16, sink);
+    return from_hip(hipGetLastError());
 }
 
 }  // extern "C"

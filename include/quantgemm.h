@@ -143,6 +143,17 @@ qg_status quant_dequantize_stacked(const void* w, qg_format fmt, int64_t E, int6
 /* Static description of a status code; never NULL. */
 const char* quant_status_string(qg_status s);
 
+/* Measurement reference, not part of the product path: a plain streaming read
+ * of `bytes` bytes at `buf` (each 16-byte granule once, non-temporal loads),
+ * the achievable-bandwidth ceiling the streaming kernels are compared with
+ * ("Qwen3.8-27B on one Tenstorrent P150", section "4. Measuring the ceiling,
+ * and lots of dead ends": a validated read microbenchmark as the ceiling).
+ * buf: device, 16-byte aligned; bytes: a multiple of 16 (0 is a no-op);
+ * sink: one device uint32, written only in the (practically impossible) case
+ * that the xor of all words equals 0x9E3779B9.  Asynchronous on `stream`.
+ * Errors: QG_EINVAL (null), QG_EALIGN, QG_ESHAPE (bytes % 16), QG_EHIP. */
+qg_status quant_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -86,6 +86,17 @@ def test_validation_rejects_before_launch():
     assert deq(FAKE_W, qg.Q6_K, 0, 256, FAKE_Y, None) == qg.QG_OK
 
 
+def test_read_probe_validation():
+    probe = _raw("quant_read_probe")
+    sink = ctypes.c_void_p(0x600000)
+    assert probe(None, 1024, sink, None) == qg.QG_EINVAL
+    assert probe(FAKE_W, 1024, None, None) == qg.QG_EINVAL
+    assert probe(ctypes.c_void_p(0x100008), 1024, sink, None) == qg.QG_EALIGN
+    assert probe(FAKE_W, 1024, ctypes.c_void_p(0x600002), None) == qg.QG_EALIGN
+    assert probe(FAKE_W, 1000, sink, None) == qg.QG_ESHAPE
+    assert probe(FAKE_W, 0, sink, None) == qg.QG_OK
+
+
 def test_grouped_validation():
     grouped = _raw("quant_grouped_gemm")
     E, N, K, M = 4, 8, 256, 3

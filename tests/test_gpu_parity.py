@@ -120,6 +120,18 @@ def test_rows_match_decode_bitwise_and_repeat(fmt, N, K):
     assert same_bits(again, y16)
 
 
+def test_read_probe_runs_and_writes_nothing():
+    """The streaming-read reference reads every granule (odd sizes included) and
+    leaves the sink alone for data whose per-thread xor cannot be the sentinel."""
+    import torch
+    for nbytes in (16, 4096 + 16, (1 << 20) + 48):
+        buf = torch.full((nbytes // 4,), 1.0, dtype=torch.float32, device="cuda")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        qg.quant_read_probe(buf, sink)
+        torch.cuda.synchronize()
+        assert int(sink.item()) == 0
+
+
 def test_zero_activations_and_zero_weights():
     fmt, N, K = qg.Q4_K, 64, 512
     w, x = make_case(fmt, N, K, 1, seed=3)
