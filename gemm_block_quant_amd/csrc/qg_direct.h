@@ -486,14 +486,17 @@ __device__ __forceinline__ int direct_out_slot(int lane) { return lane >> 2; }
 struct Segments {
     int S, PS;
 };
-// Rows are split only while a CU has fewer than this many row groups.
+// Rows are split only while a CU has fewer than this many row groups (one
+// per wave of a 16-wave workgroup); then into as many segments as keep the
+// items of a CU within its 16 waves (5 row groups per CU: 3 segments, 15
+// items -- measured fastest on the 5120 x 17408 shapes against 2, 4, 5, 9).
 constexpr int kDirectSegRgsMax = 16;
 inline Segments direct_segments(int fmt, int64_t N, int K, int cus) {
     const int P = (K / 64 + kDirectSlots - 1) / kDirectSlots;
     const int64_t groups = (N + kDirectRows - 1) / kDirectRows;
     const int64_t per_cu = (groups + cus - 1) / cus;
     int S = 1;
-    if (per_cu < kDirectSegRgsMax) S = (int)((48 + per_cu - 1) / per_cu);
+    if (per_cu < kDirectSegRgsMax) S = (int)(kDirectSegRgsMax / per_cu);
     if (S > P) S = P;
     if (S < 1) S = 1;
     const int PS = (P + S - 1) / S;
