@@ -37,7 +37,7 @@
  * Exactness: every DEQ below is evaluated in fp64, where it is exact (the
  * operands carry at most 30 significant bits in total), and then rounded once
  * to fp32 (round to nearest even, the C default).  Q8_0 and Q6_K products are
- * already exact in fp32; Q4_K and NVFP4 round exactly once.
+ * already exact in fp32; Q4_K, Q5_K and NVFP4 round exactly once.
  */
 #include <math.h>
 #include <stdint.h>
@@ -47,7 +47,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_Q8_0 = 1, ORC_Q4_K = 2, ORC_Q6_K = 3, ORC_NVFP4 = 4 };
+enum { ORC_Q8_0 = 1, ORC_Q4_K = 2, ORC_Q6_K = 3, ORC_NVFP4 = 4, ORC_Q5_K = 5 };
 
 /* ---------- scalar decoders written from the number-format definitions ---------- */
 
@@ -98,20 +98,23 @@ long long orc_block_values(int fmt) {
     case ORC_Q4_K: return 256;
     case ORC_Q6_K: return 256;
     case ORC_NVFP4: return 16;
+    case ORC_Q5_K: return 256;
     default: return 0;
     }
 }
 
 /* Q8_0: fp16 d + 32 int8 = 34 B.  Q4_K: fp16 d + fp16 dmin + 12 scale bytes +
- * 128 nibble bytes = 144 B.  Q6_K: 128 low-nibble bytes + 64 high-bit bytes +
- * 16 int8 sub-scales + fp16 d = 210 B.  NVFP4: 8 code bytes + 1 E4M3 scale
- * byte per 16 values (the 4-byte fp32 tensor scale is counted per tensor). */
+ * 128 nibble bytes = 144 B.  Q5_K: as Q4_K plus 32 bytes of fifth bits =
+ * 176 B.  Q6_K: 128 low-nibble bytes + 64 high-bit bytes + 16 int8
+ * sub-scales + fp16 d = 210 B.  NVFP4: 8 code bytes + 1 E4M3 scale byte per
+ * 16 values (the 4-byte fp32 tensor scale is counted per tensor). */
 long long orc_block_bytes(int fmt) {
     switch (fmt) {
     case ORC_Q8_0: return 34;
     case ORC_Q4_K: return 144;
     case ORC_Q6_K: return 210;
     case ORC_NVFP4: return 9;
+    case ORC_Q5_K: return 176;
     default: return 0;
     }
 }
@@ -160,6 +163,41 @@ static void orc_deq_q4_k(const uint8_t* blk, float* out) {
         for (int l = 0; l < 32; ++l) {
             uint8_t byte = Q[32 * g + l];
             int q = hi ? (byte >> 4) : (byte & 15);
+            out[32 * j + l] = (float)(d * sc * q - dmin * m);
+        }
+    }
+}
+
+/* Q5_K super-block of 256 values in 8 sub-blocks of 32 (the 27B model's
+ * packing carries 48 Q5_K tensors and the packed-word grouped kernels still
+ * owe the format -- vllm.cpp issue #3030 "BACKEND-TENSTORRENT-KEEPQUANT",
+ * paragraph "Re-anchor (scope item 1 replaced)"; the byte layout is the GGUF
+ * convention, like Q4_K's):
+ *   [0,2) d fp16, [2,4) dmin fp16, [4,16) S[0..11] scales/mins packed as in
+ *   Q4_K, [16,48) H[0..31] fifth bits, [48,176) Q[0..127] nibbles.
+ * Value 64g+l (g in 0..3, l in 0..31) is the low nibble of Q[32g+l] plus 16
+ * times bit 2g of H[l]; value 64g+32+l is the high nibble of the same byte
+ * plus 16 times bit 2g+1 of H[l].  So the code q of sub-block j, position l
+ * takes its fifth bit from bit j of H[l].
+ * w = d*sc_j*q - dmin*m_j (q in 0..31), rounded once to fp32. */
+static void orc_deq_q5_k(const uint8_t* blk, float* out) {
+    double d = orc_fp16(orc_le16(blk)), dmin = orc_fp16(orc_le16(blk + 2));
+    const uint8_t* S = blk + 4;
+    const uint8_t* H = blk + 16;
+    const uint8_t* Q = blk + 48;
+    for (int j = 0; j < 8; ++j) {
+        int sc, m;
+        if (j < 4) {
+            sc = S[j] & 63;
+            m = S[j + 4] & 63;
+        } else {
+            sc = (S[j + 4] & 15) | ((S[j - 4] >> 6) << 4);
+            m = (S[j + 4] >> 4) | ((S[j] >> 6) << 4);
+        }
+        int g = j / 2, hi = j % 2;
+        for (int l = 0; l < 32; ++l) {
+            uint8_t byte = Q[32 * g + l];
+            int q = (hi ? (byte >> 4) : (byte & 15)) | (((H[l] >> j) & 1) << 4);
             out[32 * j + l] = (float)(d * sc * q - dmin * m);
         }
     }
@@ -232,6 +270,7 @@ static void orc_deq_row(int fmt, const uint8_t* w, long long E, long long N, lon
         float* o = out + b * qk;
         if (fmt == ORC_Q8_0) orc_deq_q8_0(blk, o);
         else if (fmt == ORC_Q4_K) orc_deq_q4_k(blk, o);
+        else if (fmt == ORC_Q5_K) orc_deq_q5_k(blk, o);
         else orc_deq_q6_k(blk, o);
     }
 }

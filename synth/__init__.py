@@ -13,6 +13,7 @@ hidden 5,120 / MLP 17,408 / vocab 248,320 and the 288-expert, 4096x2048 MoE):
   Q8_0  : q uniform int8 in [-127, 127]; d = fp16(|N(0,1)| * 0.01)
   Q4_K  : 4-bit codes and 6-bit scales/mins uniform (all 12 scale bytes and 128
           code bytes uniform); d, dmin = fp16(0.01 * (0.5 + U)) per super-block
+  Q5_K  : as Q4_K, with the 32 fifth-bit bytes uniform (5-bit codes uniform)
   Q6_K  : 6-bit codes uniform (ql, qh bytes uniform); int8 sub-scales uniform in
           [-128, 127]; d = fp16(|N(0,1)| * 0.01)
   NVFP4 : code bytes uniform (each E2M1 nibble uniform over 16 values); block
@@ -25,9 +26,9 @@ from __future__ import annotations
 
 import numpy as np
 
-Q8_0, Q4_K, Q6_K, NVFP4 = 1, 2, 3, 4
-QK = {Q8_0: 32, Q4_K: 256, Q6_K: 256, NVFP4: 16}
-BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210}
+Q8_0, Q4_K, Q6_K, NVFP4, Q5_K = 1, 2, 3, 4, 5
+QK = {Q8_0: 32, Q4_K: 256, Q6_K: 256, NVFP4: 16, Q5_K: 256}
+BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210, Q5_K: 176}
 
 
 def rng(config_seed: int, tensor_id: int) -> np.random.Generator:
@@ -54,6 +55,14 @@ def q8_0(g: np.random.Generator, rows: int, K: int) -> np.ndarray:
 def q4_k(g: np.random.Generator, rows: int, K: int) -> np.ndarray:
     nb = rows * (K // 256)
     buf = _random_bytes(g, nb * 144).reshape(nb, 144)
+    buf[:, 0:2] = _fp16_bytes(0.01 * (0.5 + g.random(nb)))
+    buf[:, 2:4] = _fp16_bytes(0.01 * (0.5 + g.random(nb)))
+    return buf.reshape(-1)
+
+
+def q5_k(g: np.random.Generator, rows: int, K: int) -> np.ndarray:
+    nb = rows * (K // 256)
+    buf = _random_bytes(g, nb * 176).reshape(nb, 176)
     buf[:, 0:2] = _fp16_bytes(0.01 * (0.5 + g.random(nb)))
     buf[:, 2:4] = _fp16_bytes(0.01 * (0.5 + g.random(nb)))
     return buf.reshape(-1)
@@ -91,6 +100,8 @@ def weights(fmt: int, g: np.random.Generator, rows: int, K: int, E: int = 1) -> 
         return q4_k(g, rows, K)
     if fmt == Q6_K:
         return q6_k(g, rows, K)
+    if fmt == Q5_K:
+        return q5_k(g, rows, K)
     if fmt == NVFP4:
         return nvfp4(g, rows, K, E)
     raise ValueError("unknown format %r" % fmt)

@@ -93,6 +93,21 @@ def enc_q4_k(d_bits, dmin_bits, sc, mn, q):
     return bytes(b)
 
 
+def enc_q5_k(d_bits, dmin_bits, sc, mn, q):
+    """sc, mn: 8 six-bit values; q: 256 five-bit codes in value order.  The low
+    four bits go where Q4_K keeps its nibbles (28 bytes further on); bit 4 of
+    the code of sub-block j, position l is bit j of byte 16 + l."""
+    b = bytearray(enc_q4_k(d_bits, dmin_bits, sc, mn, [v & 15 for v in q]))
+    nib = bytes(b[16:144])
+    b = bytearray(176)
+    b[0:16] = enc_q4_k(d_bits, dmin_bits, sc, mn, [0] * 256)[0:16]
+    b[48:176] = nib
+    for j in range(8):
+        for l in range(32):
+            b[16 + l] |= ((q[32 * j + l] >> 4) & 1) << j
+    return bytes(b)
+
+
 def enc_q6_k(d_bits, s, q):
     """s: 16 int8 sub-scales; q: 256 six-bit codes in value order."""
     b = bytearray(210)
@@ -138,10 +153,12 @@ def test_block_sizes_match_pages():
     assert oracle.block_bytes(oracle.Q6_K) == f["q6_k_block_bytes"]
     assert -(-oracle.block_bytes(oracle.Q8_0) // 4) == f["q8_0_block_words"]
     assert -(-oracle.block_bytes(oracle.Q6_K) // 4) == f["q6_k_block_words"]
-    # Q4_K: 2 + 2 + 12 + 128 bytes; NVFP4: 8 code bytes + 1 scale byte per 16 values
+    # Q4_K: 2 + 2 + 12 + 128 bytes; Q5_K adds one bit per value (32 bytes);
+    # NVFP4: 8 code bytes + 1 scale byte per 16 values
     assert oracle.block_bytes(oracle.Q4_K) == 2 + 2 + 12 + 256 // 2
+    assert oracle.block_bytes(oracle.Q5_K) == 2 + 2 + 12 + 256 // 8 + 256 // 2
     assert oracle.block_bytes(oracle.NVFP4) == 16 // 2 + 1
-    assert [oracle.block_values(t) for t in (1, 2, 3, 4)] == [32, 256, 256, 16]
+    assert [oracle.block_values(t) for t in (1, 2, 3, 4, 5)] == [32, 256, 256, 16, 256]
 
 
 def test_packed_totals_match_pages():
@@ -268,6 +285,42 @@ def test_q4_k_scale_layout_every_code():
     assert np.array_equal(w.reshape(-1), np.array(expect, np.float32))
 
 
+def test_q5_k_exact():
+    g = np.random.default_rng(15)
+    nb = 28
+    blocks, expect = [], []
+    for i in range(nb):
+        db = _rand_f16_bits(g, SPECIALS[i % len(SPECIALS)])
+        mb = _rand_f16_bits(g, SPECIALS[(i // 2) % len(SPECIALS)])
+        sc = [int(v) for v in g.integers(0, 64, 8)]
+        mn = [int(v) for v in g.integers(0, 64, 8)]
+        if i == 1:
+            sc, mn = [63] * 8, [63] * 8
+        q = [int(v) for v in g.integers(0, 32, 256)]
+        if i == 2:
+            q = [31, 16] * 128
+        blocks.append(enc_q5_k(db, mb, sc, mn, q))
+        d, dmin = f16_value(db), f16_value(mb)
+        for v in range(256):
+            j = v // 32
+            expect.append(rn32(d * sc[j] * q[v] - dmin * mn[j]))
+    w = oracle.dequant_rows(oracle.Q5_K, as_u8(b"".join(blocks)), 1, nb, 256)
+    assert same_values(w.reshape(-1), np.array(expect, np.float32))
+
+
+def test_q5_k_fifth_bit_every_position():
+    """A code of 16 (only the fifth bit set) at each of the 256 positions in turn,
+    with d = sc = 1 and no min: the dequantized block is 16 at that position only."""
+    one = f16_bits(1.0)
+    blocks = []
+    for v in range(256):
+        q = [0] * 256
+        q[v] = 16
+        blocks.append(enc_q5_k(one, one, [1] * 8, [0] * 8, q))
+    w = oracle.dequant_rows(oracle.Q5_K, as_u8(b"".join(blocks)), 1, 256, 256)
+    assert np.array_equal(w, 16.0 * np.eye(256, dtype=np.float32))
+
+
 def test_q6_k_exact():
     g = np.random.default_rng(13)
     nb = 21
@@ -320,6 +373,10 @@ def test_generator_fields_in_range():
     w4 = synth.weights(synth.Q4_K, synth.rng(2, 0), 16, 512).reshape(-1, 144)
     d4 = w4[:, 0:2].copy().view(np.float16).astype(np.float64)
     assert (d4 >= 0.005 - 1e-6).all() and (d4 <= 0.015 + 1e-5).all()
+    w5 = synth.weights(synth.Q5_K, synth.rng(6, 0), 16, 512)
+    assert w5.size == oracle.packed_bytes(oracle.Q5_K, 1, 16, 512)
+    d5 = w5.reshape(-1, 176)[:, 0:4].copy().view(np.float16).astype(np.float64)
+    assert (d5 >= 0.005 - 1e-6).all() and (d5 <= 0.015 + 1e-5).all()
     nv = synth.weights(synth.NVFP4, synth.rng(4, 0), 32, 256)
     assert nv.size == oracle.packed_bytes(oracle.NVFP4, 1, 32, 256)
     gsc = nv[-4:].view(np.float32)[0]
@@ -332,7 +389,7 @@ def _bf16_to_f64(xb):
     return (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-@pytest.mark.parametrize("fmt,K", [(1, 1024), (2, 1024), (3, 768), (4, 512)])
+@pytest.mark.parametrize("fmt,K", [(1, 1024), (2, 1024), (3, 768), (4, 512), (5, 768)])
 def test_gemm_matches_numpy_fp64(fmt, K):
     N, M = 67, 3
     w = synth.weights(fmt, synth.rng(5, 0), N, K)
@@ -384,6 +441,11 @@ def test_gemm_one_hot_and_integer_sums():
     w4 = as_u8(enc_q4_k(one, one, [1] * 8, [0] * 8, q))
     y, b = oracle.gemm(oracle.Q4_K, w4, 1, 256, np.full((1, 256), 0x3F80, np.uint16))
     assert y[0, 0] == sum(q) == b[0, 0]
+    # Q5_K likewise: y = sum of the five-bit codes
+    q5 = [int(v) for v in g.integers(0, 32, 256)]
+    w5 = as_u8(enc_q5_k(one, one, [1] * 8, [0] * 8, q5))
+    y, b = oracle.gemm(oracle.Q5_K, w5, 1, 256, np.full((1, 256), 0x3F80, np.uint16))
+    assert y[0, 0] == sum(q5) == b[0, 0]
     # x = 0: y = 0 and bound = 0
     y, b = oracle.gemm(oracle.Q4_K, w4, 1, 256, np.zeros((1, 256), np.uint16))
     assert y[0, 0] == 0 and b[0, 0] == 0
