@@ -15,6 +15,7 @@ int64_t block_values(int fmt) {
     switch (fmt) {
         case QG_Q8_0: return 32;
         case QG_Q4_K: return 256;
+        case QG_Q5_K: return 256;
         case QG_Q6_K: return 256;
         case QG_NVFP4: return 16;
         default: return 0;
@@ -25,6 +26,7 @@ int64_t block_bytes(int fmt) {
     switch (fmt) {
         case QG_Q8_0: return 34;
         case QG_Q4_K: return 144;
+        case QG_Q5_K: return 176;
         case QG_Q6_K: return 210;
         default: return 0;
     }

@@ -5,6 +5,7 @@
 // exact up to a single rounding to nearest even:
 //   Q8_0  w = d * q                         (exact)
 //   Q4_K  w = (d * sc) * q - dmin * m       (both products exact, one rounding)
+//   Q5_K  the same, with 5-bit codes
 //   Q6_K  w = (d * s) * (q - 32)            (exact)
 //   NVFP4 w = (e2m1 * e4m3) * g             (first product exact, one rounding)
 // Block sizes: Q8_0 34 bytes and Q6_K 210 bytes (vllm.cpp issue #3030,
@@ -55,6 +56,29 @@ __global__ __launch_bounds__(256) void k_dequant_block(int fmt, const uint8_t* _
             for (int l = 0; l < 32; ++l) {
                 const uint32_t byte = Q[32 * g + l];
                 const uint32_t q = hi ? (byte >> 4) : (byte & 15u);
+                o[32 * j + l] = ds * (float)q - mm;
+            }
+        }
+    } else if (fmt == QG_Q5_K) {
+        const uint8_t* p = w + blk * 176;
+        const float d = f16_to_f32(ld_u16(p)), dmin = f16_to_f32(ld_u16(p + 2));
+        const uint8_t* S = p + 4;
+        const uint8_t* H = p + 16;
+        const uint8_t* Q = p + 48;
+        for (int j = 0; j < 8; ++j) {
+            uint32_t sc, m;
+            if (j < 4) {
+                sc = S[j] & 63u;
+                m = S[j + 4] & 63u;
+            } else {
+                sc = (S[j + 4] & 15u) | ((uint32_t)(S[j - 4] >> 6) << 4);
+                m = (S[j + 4] >> 4) | ((uint32_t)(S[j] >> 6) << 4);
+            }
+            const float ds = d * (float)sc, mm = dmin * (float)m;
+            const int g = j >> 1, hi = j & 1;
+            for (int l = 0; l < 32; ++l) {
+                const uint32_t byte = Q[32 * g + l];
+                const uint32_t q = (hi ? (byte >> 4) : (byte & 15u)) | ((((uint32_t)H[l] >> j) & 1u) << 4);
                 o[32 * j + l] = ds * (float)q - mm;
             }
         }

@@ -193,6 +193,116 @@ template <> struct Direct<QG_Q4_K> {
     }
 };
 
+// Q5_K: Q4_K with a fifth code bit.  Unit u of a row = quarter g = u % 4 of
+// super-block u / 4: code bytes [48 + 32g, 48 + 32g + 32) (low nibbles:
+// sub-block 2g, high: 2g + 1), the 32 fifth-bit bytes H at [16, 48) (bit 2g of
+// H[l] for the low nibble of position l, bit 2g + 1 for the high one) and the
+// 16-byte header.  The codes go to the matrix cores as exact bf16 128 + q
+// (q <= 31), with the sums of Q4_K.
+template <> struct Direct<QG_Q5_K> {
+    static constexpr int UV = 64;
+    static constexpr int REGS = 20;
+    static constexpr bool SUMS = true;
+    struct Lane {
+        Direct<QG_Q4_K>::Lane s;  // scale and min extraction (as Q4_K)
+        uint32_t hsh;             // 2g: the fifth bits of sub-block 2g
+    };
+    __device__ static Lane lane_consts(int lane) {
+        return Lane{Direct<QG_Q4_K>::lane_consts(lane), 2u * (uint32_t)((lane >> 2) & 3)};
+    }
+    __device__ __host__ static int units_per_row(int K) { return (K / 256) * 4; }
+    // Bytes of one pass (16 units = 4 super-blocks) of a row.
+    static constexpr int PASS0 = 4 * 176, PASS1 = 0;
+    // Offsets from the start of a pass's stretch: the unit's code bytes (a),
+    // its super-block's fifth-bit bytes (b) and header (c).
+    struct Offs {
+        uint32_t a, b, c;
+    };
+    __device__ static Offs slot_offs(int s) {
+        const uint32_t blk = 176u * (uint32_t)(s >> 2);
+        return Offs{blk + 48u + 32u * (uint32_t)(s & 3), blk + 16u, blk};
+    }
+    __device__ static Offs shift(const Offs& o, uint32_t r0, uint32_t) { return Offs{o.a + r0, o.b + r0, o.c + r0}; }
+    __device__ static Offs pick(bool c, const Offs& x, const Offs& y) {
+        return Offs{c ? x.a : y.a, c ? x.b : y.b, c ? x.c : y.c};
+    }
+    __device__ static void load_at(uint32_t (&r)[REGS], const uint8_t* b0, const uint8_t*, const Offs& o) {
+        const u32x4 qa = ld_global128(b0 + o.a), qb = ld_global128(b0 + o.a + 16);
+        const u32x4 h0 = ld_global128(b0 + o.b), h1 = ld_global128(b0 + o.b + 16);
+        const u32x4 hd = ld_global128(b0 + o.c);
+        r[0] = qa.x; r[1] = qa.y; r[2] = qa.z; r[3] = qa.w;
+        r[4] = qb.x; r[5] = qb.y; r[6] = qb.z; r[7] = qb.w;
+        r[8] = h0.x; r[9] = h0.y; r[10] = h0.z; r[11] = h0.w;
+        r[12] = h1.x; r[13] = h1.y; r[14] = h1.z; r[15] = h1.w;
+        r[16] = hd.x; r[17] = hd.y; r[18] = hd.z; r[19] = hd.w;
+    }
+    template <int MT>
+    __device__ static void decode(const uint32_t (&r)[REGS], const Lane& LL, int u, bool live, const lds_u8* xa,
+                                  int xmg_bytes, const lds_f32* xs, int xs_mg, float (&acc)[MT]) {
+        constexpr int MG = (MT + 3) / 4;
+        const Direct<QG_Q4_K>::Lane& L = LL.s;
+        const uint32_t y = r[17], z = r[18], w = r[19];
+        const uint32_t as = L.hi4 ? w : y, am = L.hi4 ? w : z;
+        const uint32_t sc0 = __builtin_amdgcn_ubfe(as, L.off, L.wa) | (__builtin_amdgcn_ubfe(y, L.off + 6, L.wb) << 4);
+        const uint32_t sc1 =
+            __builtin_amdgcn_ubfe(as, L.off + 8, L.wa) | (__builtin_amdgcn_ubfe(y, L.off + 14, L.wb) << 4);
+        const uint32_t m0 = __builtin_amdgcn_ubfe(am, L.oam, L.wa) | (__builtin_amdgcn_ubfe(z, L.off + 6, L.wb) << 4);
+        const uint32_t m1 =
+            __builtin_amdgcn_ubfe(am, L.oam + 8, L.wa) | (__builtin_amdgcn_ubfe(z, L.off + 14, L.wb) << 4);
+        const float d = f16_to_f32(r[16]), dmin = f16_to_f32(r[16] >> 16);
+        const float a0 = d * (float)sc0, a1 = d * (float)sc1;
+        const float b0 = -fmaf(dmin, (float)m0, 128.f * a0);
+        const float b1 = -fmaf(dmin, (float)m1, 128.f * a1);
+
+        f32x4_t c0[MG], c1[MG];
+#pragma unroll
+        for (int g = 0; g < MG; ++g) c0[g] = c1[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int rot = u & 3;
+#pragma unroll
+        for (int rp = 0; rp < 4; ++rp) {
+            // values 8rp..8rp+7 of each sub-block: code dwords 2rp, 2rp+1 and the
+            // fifth-bit bytes of the same positions (H dwords 2rp, 2rp+1), moved
+            // to bit 0 of each byte for sub-block 2g and bit 1 for 2g+1
+            const uint32_t e0 = r[8 + 2 * rp] >> LL.hsh, e1 = r[8 + 2 * rp + 1] >> LL.hsh;
+            const uint32_t l0 = (r[2 * rp] & 0x0F0F0F0Fu) | ((e0 << 4) & 0x10101010u);
+            const uint32_t l1 = (r[2 * rp + 1] & 0x0F0F0F0Fu) | ((e1 << 4) & 0x10101010u);
+            const uint32_t h0 = ((r[2 * rp] >> 4) & 0x0F0F0F0Fu) | ((e0 << 3) & 0x10101010u);
+            const uint32_t h1 = ((r[2 * rp + 1] >> 4) & 0x0F0F0F0Fu) | ((e1 << 3) & 0x10101010u);
+            const uint32_t bl0 = bias128_pair(l0, kSelB0B1), bl1 = bias128_pair(l0, kSelB2B3);
+            const uint32_t bl2 = bias128_pair(l1, kSelB0B1), bl3 = bias128_pair(l1, kSelB2B3);
+            const uint32_t bh0 = bias128_pair(h0, kSelB0B1), bh1 = bias128_pair(h0, kSelB2B3);
+            const uint32_t bh2 = bias128_pair(h1, kSelB0B1), bh3 = bias128_pair(h1, kSelB2B3);
+#pragma unroll
+            for (int g = 0; g < MG; ++g) {
+                const u32x4 xl = lds_ld128(xa + g * xmg_bytes + ((rp ^ rot) * 4 * 16));
+                const u32x4 xh = lds_ld128(xa + g * xmg_bytes + (((4 + rp) ^ rot) * 4 * 16));
+                c0[g] = mfma4(xl.x, xl.y, bl0, bl1, c0[g]);
+                c1[g] = mfma4(xh.x, xh.y, bh0, bh1, c1[g]);
+                c0[g] = mfma4(xl.z, xl.w, bl2, bl3, c0[g]);
+                c1[g] = mfma4(xh.z, xh.w, bh2, bh3, c1[g]);
+            }
+        }
+        if (live) {
+#pragma unroll
+            for (int g = 0; g < MG; ++g) {
+                const f32x4_t s0 = *(const QG_LDS f32x4_t*)(xs + (size_t)g * xs_mg + 8 * u);
+                const f32x4_t s1 = *(const QG_LDS f32x4_t*)(xs + (size_t)g * xs_mg + 8 * u + 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (4 * g + i < MT) {
+                        float a = acc[4 * g + i];
+                        a = fmaf(a0, c0[g][i], a);
+                        a = fmaf(b0, s0[i], a);
+                        a = fmaf(a1, c1[g][i], a);
+                        a = fmaf(b1, s1[i], a);
+                        acc[4 * g + i] = a;
+                    }
+                }
+            }
+        }
+    }
+};
+
 // NVFP4 (K a multiple of 64).  Unit u of a row = code bytes [32u, 32u + 32)
 // (values 64u + [0,64), blocks 4u .. 4u + 3) and the four E4M3 scales of
 // those blocks (one 4-byte load).  sum w x = g * sum_b s_b * sum c x; g is
@@ -378,9 +488,11 @@ template <> struct Direct<QG_Q6_K> {
 __host__ __device__ constexpr int direct_uv(int) { return 64; }
 __host__ __device__ constexpr int direct_mg(int mt) { return (mt + 3) / 4; }
 __host__ __device__ constexpr int direct_units(int K) { return K / 64; }
-// Activation sub-blocks (one scale, one sum) per unit: Q4_K 2 x 32 values,
+// Activation sub-blocks (one scale, one sum) per unit: Q4_K and Q5_K 2 x 32 values,
 // Q6_K 4 x 16 values; NVFP4 needs no sums.
-__host__ __device__ constexpr int direct_sub(int fmt) { return fmt == QG_Q4_K ? 2 : fmt == QG_Q6_K ? 4 : 0; }
+__host__ __device__ constexpr int direct_sub(int fmt) {
+    return fmt == QG_Q4_K || fmt == QG_Q5_K ? 2 : fmt == QG_Q6_K ? 4 : 0;
+}
 // Bytes of one unit for one group of 4 activation rows.
 __host__ __device__ constexpr int direct_unit_bytes(int) { return 8 * 4 * 16; }
 // Bytes of one group of 4 activation rows (all units).
@@ -701,7 +813,7 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
 }
 
 inline bool direct_eligible(int fmt, int K) {
-    return fmt == QG_Q4_K || fmt == QG_Q6_K || (fmt == QG_NVFP4 && K % 64 == 0);
+    return fmt == QG_Q4_K || fmt == QG_Q5_K || fmt == QG_Q6_K || (fmt == QG_NVFP4 && K % 64 == 0);
 }
 
 }  // namespace qg

@@ -68,7 +68,9 @@ __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
 // change any row's arithmetic.
 // 16 waves per workgroup; 8 where the accumulators of many activation rows
 // need more registers than 4 waves per SIMD allow.
-template <int F, int MT> constexpr int direct_waves() { return MT >= 16 || (F == QG_Q6_K && MT >= 8) ? 8 : 16; }
+template <int F, int MT> constexpr int direct_waves() {
+    return MT >= 16 || ((F == QG_Q6_K || F == QG_Q5_K) && MT >= 8) ? 8 : 16;
+}
 
 // SEG false: one K segment and one phase (the launch guarantees it).
 template <int F, int MT, int SP, int PF, bool SEG>
@@ -167,6 +169,7 @@ static hipError_t dispatch_rlt(StreamArgs a, hipStream_t st) {
 // arithmetic does not depend on them).
 template <int F, int MT> struct DirectTune;
 template <int MT> struct DirectTune<QG_Q4_K, MT> { static constexpr int SP = 1, PF = 2; };
+template <int MT> struct DirectTune<QG_Q5_K, MT> { static constexpr int SP = 1, PF = 2; };
 template <int MT> struct DirectTune<QG_NVFP4, MT> { static constexpr int SP = 1, PF = 2; };
 template <int MT> struct DirectTune<QG_Q6_K, MT> { static constexpr int SP = 1, PF = 2; };
 
@@ -201,7 +204,7 @@ static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
 
 template <int F>
 static hipError_t dispatch_mt(const StreamArgs& a, int mt, hipStream_t st) {
-    if constexpr (F == QG_Q4_K || F == QG_Q6_K || F == QG_NVFP4) {
+    if constexpr (F == QG_Q4_K || F == QG_Q5_K || F == QG_Q6_K || F == QG_NVFP4) {
         if (direct_eligible(F, a.K)) {
             switch (mt) {
                 case 1: return dispatch_direct<F, 1>(a, st);
@@ -246,6 +249,7 @@ hipError_t launch_stream_gemm(int fmt, StreamArgs a, hipStream_t st) {
     switch (fmt) {
         case QG_Q8_0: return dispatch_mt<QG_Q8_0>(a, mt, st);
         case QG_Q4_K: return dispatch_mt<QG_Q4_K>(a, mt, st);
+        case QG_Q5_K: return dispatch_mt<QG_Q5_K>(a, mt, st);
         case QG_Q6_K: return dispatch_mt<QG_Q6_K>(a, mt, st);
         default: return dispatch_mt<QG_NVFP4>(a, mt, st);
     }

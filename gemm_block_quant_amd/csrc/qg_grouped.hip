@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
 }
 
 // Grouped streaming kernel.  MTMAX: activation rows per pass (LDS sized for
-// it); DIRECT: register-direct streaming (Q4_K, Q6_K, NVFP4 with K % 64 == 0) with SP
+// it); DIRECT: register-direct streaming (Q4_K, Q5_K, Q6_K, NVFP4 with K % 64 == 0) with SP
 // passes per ring slot, else the LDS row-buffer path with CPL/CPLS chunks.
 template <int F, int MTMAX, bool DIRECT, int CPL, int CPLS, int SP, int PF>
 __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32_t* __restrict__ ws, int64_t E,
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32
                                                  int64_t estride1) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8* smem = (lds_u8*)smem_generic;
-    constexpr bool kSums = F == QG_Q4_K || F == QG_Q6_K;
+    constexpr bool kSums = F == QG_Q4_K || F == QG_Q5_K || F == QG_Q6_K;
     const int K = a.K;
     const int slot = blockIdx.x / nchunks, chunk = blockIdx.x % nchunks;
     const int nslots = ws[0];
@@ -244,7 +244,7 @@ static hipError_t launch_grouped_one(Kern kern, size_t lds, const StreamArgs& a,
 template <int F, int MTMAX>
 static hipError_t grouped_paths(StreamArgs a, const int32_t* ws, int64_t E, int64_t M, int64_t es0, int64_t es1,
                                 hipStream_t st) {
-    if constexpr (F == QG_Q4_K || F == QG_Q6_K || F == QG_NVFP4) {
+    if constexpr (F == QG_Q4_K || F == QG_Q5_K || F == QG_Q6_K || F == QG_NVFP4) {
         if (direct_eligible(F, a.K)) {
             const Segments sg = direct_segments(F, a.N, a.K, num_cus());
             a.seg_S = sg.S;
@@ -309,6 +309,7 @@ hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int6
     switch (fmt) {
         case QG_Q8_0: return grouped_mt<QG_Q8_0>(a, mtmax, ws, E, M, estride0, estride1, st);
         case QG_Q4_K: return grouped_mt<QG_Q4_K>(a, mtmax, ws, E, M, estride0, estride1, st);
+        case QG_Q5_K: return grouped_mt<QG_Q5_K>(a, mtmax, ws, E, M, estride0, estride1, st);
         case QG_Q6_K: return grouped_mt<QG_Q6_K>(a, mtmax, ws, E, M, estride0, estride1, st);
         default: return grouped_mt<QG_NVFP4>(a, mtmax, ws, E, M, estride0, estride1, st);
     }

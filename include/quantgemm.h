@@ -40,6 +40,12 @@
  *  - QG_Q4_K (QK = 256, 144 bytes): fp16 d, fp16 dmin, 12 bytes of packed
  *    6-bit sub-block scales sc[8] and mins m[8], 128 bytes of 4-bit codes.
  *    w = d * sc_j * q - dmin * m_j for sub-block j of 32 values.
+ *  - QG_Q5_K (QK = 256, 176 bytes): fp16 d, fp16 dmin, the 12 scale bytes of
+ *    Q4_K, 32 bytes H of fifth bits, 128 bytes of 4-bit codes laid out as in
+ *    Q4_K; the code of sub-block j at position l gets bit j of H[l] as its
+ *    fifth bit (q in 0..31).  w = d * sc_j * q - dmin * m_j.  (The 27B
+ *    artefact carries Q5_K tensors that the packed-word kernels still owe:
+ *    vllm.cpp issue #3030, paragraph "Re-anchor (scope item 1 replaced)".)
  *  - QG_Q6_K (QK = 256, 210 bytes): 128 bytes low nibbles, 64 bytes high
  *    2-bit pairs, 16 int8 sub-scales (one per 16 values), fp16 d.
  *    w = d * s * (q - 32).
@@ -74,7 +80,7 @@
 extern "C" {
 #endif
 
-typedef enum { QG_Q8_0 = 1, QG_Q4_K = 2, QG_Q6_K = 3, QG_NVFP4 = 4 } qg_format;
+typedef enum { QG_Q8_0 = 1, QG_Q4_K = 2, QG_Q6_K = 3, QG_NVFP4 = 4, QG_Q5_K = 5 } qg_format;
 
 typedef enum {
     QG_OK = 0,

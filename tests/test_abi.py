@@ -107,7 +107,7 @@ def test_grouped_validation():
     args = lambda **kw: [kw.get("w", FAKE_W), kw.get("fmt", qg.Q4_K), kw.get("E", E), N, K, kw.get("M", M), FAKE_X,
                          kw.get("ids", ids), FAKE_Y, kw.get("ws", ws), kw.get("wsb", wsb), None]
     assert grouped(*args(E=0)) == qg.QG_ESHAPE
-    assert grouped(*args(fmt=5)) == qg.QG_EFORMAT
+    assert grouped(*args(fmt=6)) == qg.QG_EFORMAT
     assert grouped(*args(ws=None)) == qg.QG_EWORKSPACE
     assert grouped(*args(wsb=wsb - 1)) == qg.QG_EWORKSPACE
     assert grouped(*args(ws=ctypes.c_void_p(0x400004))) == qg.QG_EALIGN

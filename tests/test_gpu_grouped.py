@@ -17,7 +17,7 @@ def _ids_dev(ids):
 
 @pytest.mark.parametrize("fmt,E,N,K,M", [
     (qg.Q4_K, 5, 100, 512, 12), (qg.Q6_K, 4, 77, 768, 9), (qg.Q8_0, 6, 50, 1024, 20),
-    (qg.NVFP4, 3, 64, 592, 7), (qg.Q4_K, 40, 130, 2048, 37),
+    (qg.NVFP4, 3, 64, 592, 7), (qg.Q4_K, 40, 130, 2048, 37), (qg.Q5_K, 6, 90, 1024, 15),
 ])
 def test_grouped_band_and_invalid_rows(fmt, E, N, K, M):
     w = synth.weights(fmt, synth.rng(21, 0), E * N, K, E=E)
@@ -34,7 +34,7 @@ def test_grouped_band_and_invalid_rows(fmt, E, N, K, M):
     assert_band(y[~bad], y_ref[~bad], bound[~bad], "grouped fmt %d" % fmt)
 
 
-@pytest.mark.parametrize("fmt,K", [(qg.Q4_K, 4096), (qg.NVFP4, 5120), (qg.Q6_K, 2048)])
+@pytest.mark.parametrize("fmt,K", [(qg.Q4_K, 4096), (qg.NVFP4, 5120), (qg.Q6_K, 2048), (qg.Q5_K, 2048)])
 def test_grouped_e1_is_dense_bitwise(fmt, K):
     N, M = 257, 11
     w = synth.weights(fmt, synth.rng(22, 0), N, K)

@@ -20,6 +20,7 @@ pytestmark = pytest.mark.gpu
 DEQ_SHAPES = [
     (qg.Q8_0, 37, 96), (qg.Q8_0, 5, 1024),
     (qg.Q4_K, 13, 512), (qg.Q4_K, 3, 5120),
+    (qg.Q5_K, 7, 512), (qg.Q5_K, 3, 5120),
     (qg.Q6_K, 11, 768), (qg.Q6_K, 2, 17408),
     (qg.NVFP4, 9, 48), (qg.NVFP4, 17, 5120),
 ]
@@ -42,13 +43,13 @@ def _with_specials(fmt, w, N, K):
             w[sc0 + i] = s
         w[0] = 0x08  # codes -0 and +0
         return w
-    bb = {qg.Q8_0: 34, qg.Q4_K: 144, qg.Q6_K: 210}[fmt]
-    doff = {qg.Q8_0: 0, qg.Q4_K: 0, qg.Q6_K: 208}[fmt]
+    bb = {qg.Q8_0: 34, qg.Q4_K: 144, qg.Q5_K: 176, qg.Q6_K: 210}[fmt]
+    doff = {qg.Q8_0: 0, qg.Q4_K: 0, qg.Q5_K: 0, qg.Q6_K: 208}[fmt]
     nblk = w.size // bb
     for i, bits in enumerate([0x0000, 0x0001, 0x03FF, 0x7BFF, 0x8000 | 0x2E66, 0x0400]):
         if i < nblk:
             _put_f16(w, i * bb + doff, bits)
-    if fmt == qg.Q4_K and nblk > 2:
+    if fmt in (qg.Q4_K, qg.Q5_K) and nblk > 2:
         _put_f16(w, 2 * bb + 2, 0x0001)  # subnormal dmin
     if fmt == qg.Q6_K and nblk > 1:
         w[bb + 192: bb + 208] = 0x80  # sub-scales -128
@@ -77,6 +78,8 @@ PRODUCT_CASES = [
     (qg.Q8_0, 1, 32, 1), (qg.Q8_0, 300, 1024, 1), (qg.Q8_0, 1000, 2048, 3), (qg.Q8_0, 129, 4192, 8),
     (qg.Q4_K, 1, 256, 1), (qg.Q4_K, 5, 512, 2), (qg.Q4_K, 1000, 5120, 1), (qg.Q4_K, 777, 5120, 8),
     (qg.Q4_K, 257, 1792, 16), (qg.Q4_K, 130, 17408, 1), (qg.Q4_K, 64, 17408, 17),
+    (qg.Q5_K, 1, 256, 1), (qg.Q5_K, 5, 512, 2), (qg.Q5_K, 1000, 5120, 1), (qg.Q5_K, 777, 5120, 8),
+    (qg.Q5_K, 257, 1792, 16), (qg.Q5_K, 130, 17408, 1), (qg.Q5_K, 64, 17408, 17), (qg.Q5_K, 33, 4096, 3),
     (qg.Q6_K, 1, 256, 1), (qg.Q6_K, 3, 768, 4), (qg.Q6_K, 1000, 5120, 1), (qg.Q6_K, 150, 17408, 1),
     (qg.Q6_K, 99, 17408, 8), (qg.Q6_K, 333, 5120, 33),
     (qg.NVFP4, 1, 16, 1), (qg.NVFP4, 3, 48, 2), (qg.NVFP4, 1000, 5120, 1), (qg.NVFP4, 100, 17408, 1),
@@ -101,7 +104,7 @@ def test_product_band(fmt, N, K, M):
 
 
 @pytest.mark.parametrize("fmt,N,K", [(qg.Q8_0, 300, 1024), (qg.Q4_K, 300, 5120), (qg.Q6_K, 300, 17408),
-                                     (qg.NVFP4, 300, 5120),
+                                     (qg.NVFP4, 300, 5120), (qg.Q5_K, 300, 5120),
                                      # tall: up to 8 rows take the whole-row-group kernel, 16 the direct one
                                      (qg.Q4_K, 16385, 5120), (qg.NVFP4, 16387, 5120)])
 def test_rows_match_decode_bitwise_and_repeat(fmt, N, K):
@@ -149,6 +152,8 @@ FULL = [
     (qg.Q4_K, 2 * 17408, 5120, 1), (qg.Q4_K, 2 * 17408, 5120, 8),
     # tall with a ragged last row group (whole-row-group kernel)
     (qg.Q4_K, 16385, 5120, 3), (qg.NVFP4, 16387, 5120, 5),
+    # Q5_K at the fused gate+up shape
+    (qg.Q5_K, 2 * 17408, 5120, 1), (qg.Q5_K, 2 * 17408, 5120, 8),
     (qg.Q6_K, 5120, 17408, 1), (qg.Q6_K, 5120, 17408, 8),
     (qg.Q6_K, 248320, 5120, 1), (qg.Q6_K, 248320, 5120, 8),
     (qg.NVFP4, 17408, 5120, 1), (qg.NVFP4, 17408, 5120, 8),
@@ -159,7 +164,7 @@ FULL = [
 
 @pytest.mark.parametrize("fmt,N,K,M", FULL)
 def test_full_size_sampled(fmt, N, K, M):
-    seed = {qg.Q8_0: 1, qg.Q4_K: 2, qg.Q6_K: 3, qg.NVFP4: 4}[fmt]
+    seed = {qg.Q8_0: 1, qg.Q4_K: 2, qg.Q6_K: 3, qg.NVFP4: 4, qg.Q5_K: 6}[fmt]
     w = synth.weights(fmt, synth.rng(seed, 0), N, K)
     x = synth.x_bf16(synth.rng(seed, 1), M, K)
     wd, xd = dev_bytes(w), dev_x(x)
