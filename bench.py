@@ -55,8 +55,11 @@ def workloads():
         "q8_0_1024": Workload("Q8_0 GEMV 1024x1024", qg.Q8_0, 1024, 1024, 1, 1),
         "q4k_gateup": Workload("Q4_K fused gate+up GEMV, N=34816 K=5120", qg.Q4_K, 2 * 17408, 5120, 1, 2),
         "q4k_gateup_m8": Workload("Q4_K fused gate+up, N=34816 K=5120", qg.Q4_K, 2 * 17408, 5120, 8, 2),
+        "q4k_gateup_m512": Workload("Q4_K fused gate+up prefill, N=34816 K=5120", qg.Q4_K, 2 * 17408, 5120, 512, 2),
         "q5k_gateup": Workload("Q5_K fused gate+up GEMV, N=34816 K=5120", qg.Q5_K, 2 * 17408, 5120, 1, 6),
         "q5k_gateup_m8": Workload("Q5_K fused gate+up, N=34816 K=5120", qg.Q5_K, 2 * 17408, 5120, 8, 6),
+        "q5k_gateup_m512": Workload("Q5_K fused gate+up prefill, N=34816 K=5120", qg.Q5_K, 2 * 17408, 5120, 512,
+                                    6),
         "q6k_down_m1": Workload("Q6_K down-proj, N=5120 K=17408", qg.Q6_K, 5120, 17408, 1, 3),
         "q6k_down_m8": Workload("Q6_K down-proj, N=5120 K=17408", qg.Q6_K, 5120, 17408, 8, 3),
         "q6k_head_m1": Workload("Q6_K LM head, N=248320 K=5120", qg.Q6_K, 248320, 5120, 1, 3),

@@ -17,28 +17,11 @@
 // blocks) per step through two LDS buffers: while the matrix cores work on
 // one, the next step is decoded into the other, and the loads of the steps
 // after it are already in flight in a register ring several steps deep.
-#include <type_traits>
-
-#include "qg_internal.h"
+#include "qg_mfma.h"
 
 namespace qg {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr int kMfmaKStep = 64;
-constexpr int kMfmaRowBytes = 144;  // one tile row: 64 bf16 (128 B) + 16 B padding (conflict-free fragment reads)
-constexpr int kMfmaThreads = 256;
 constexpr int kMfmaStages = 4;  // K steps of loads in flight (an even number)
-
-// f(std::integral_constant<int, i>{}) for i = 0 .. N-1, unrolled.
-template <int N, int I = 0, class Fn>
-__device__ __forceinline__ void static_for(Fn&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<N, I + 1>(f);
-    }
-}
 
 __device__ __forceinline__ uint32_t bf16_pair_from_exact(float lo, float hi) {
     // lo, hi are exact in bf16: their top 16 bits are the bf16 encodings.

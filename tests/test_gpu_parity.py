@@ -88,6 +88,11 @@ PRODUCT_CASES = [
     # matrix-core path (NVFP4, M >= 32): ragged M and N tiles, K % 32 == 16 (half step)
     (qg.NVFP4, 200, 5120, 37), (qg.NVFP4, 130, 48, 33), (qg.NVFP4, 300, 1040, 130), (qg.NVFP4, 1000, 512, 64),
     (qg.NVFP4, 64, 16, 32),
+    # matrix-core path (Q4_K, Q5_K, M >= 32): ragged tiles, K of one super-block,
+    # 64 x 64 and 128 x 64 tiles (the latter once the tile count covers the CUs)
+    (qg.Q4_K, 200, 5120, 37), (qg.Q4_K, 130, 256, 33), (qg.Q4_K, 300, 1280, 130), (qg.Q4_K, 1000, 512, 64),
+    (qg.Q4_K, 4100, 768, 450),
+    (qg.Q5_K, 200, 5120, 37), (qg.Q5_K, 64, 256, 32), (qg.Q5_K, 300, 1792, 130), (qg.Q5_K, 4100, 768, 450),
 ]
 
 
@@ -159,6 +164,7 @@ FULL = [
     (qg.NVFP4, 17408, 5120, 1), (qg.NVFP4, 17408, 5120, 8),
     (qg.NVFP4, 5120, 17408, 1), (qg.NVFP4, 5120, 17408, 8),
     (qg.NVFP4, 17408, 5120, 512), (qg.NVFP4, 5120, 17408, 512),
+    (qg.Q4_K, 2 * 17408, 5120, 512), (qg.Q5_K, 2 * 17408, 5120, 512),
 ]
 
 
@@ -176,11 +182,11 @@ def test_full_size_sampled(fmt, N, K, M):
     assert_band(y[:, cols], y_ref, bound, "full fmt %d N %d K %d M %d" % (fmt, N, K, M))
 
 
-def test_mfma_rows_independent_of_tiling_and_repeat():
-    """NVFP4 with M >= 32: each output is one fixed fp32 accumulation over K, so
-    the rows of a 37-row call equal those rows of a 512-row call (other tile
-    shapes and grid) bit for bit, and runs repeat."""
-    fmt, N, K = qg.NVFP4, 1000, 1040
+@pytest.mark.parametrize("fmt,N,K", [(qg.NVFP4, 1000, 1040), (qg.Q4_K, 4100, 768), (qg.Q5_K, 4100, 768)])
+def test_mfma_rows_independent_of_tiling_and_repeat(fmt, N, K):
+    """M >= 32 on the matrix cores: each output is one fixed fp32 accumulation
+    over K, so the rows of a 37-row call equal those rows of a 512-row call
+    (other tile shapes and grid) bit for bit, and runs repeat."""
     w, x = make_case(fmt, N, K, 512, seed=77)
     wd, xd = dev_bytes(w), dev_x(x)
     y512 = qg.quant_gemm(wd, fmt, N, K, 512, xd).cpu().numpy()
