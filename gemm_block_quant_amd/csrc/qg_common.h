@@ -103,6 +103,7 @@ __device__ __forceinline__ u32x4 ld_stream128(const uint8_t* p) {
 
 // Ordinary global 16-byte load / 4-byte store through the global address space.
 __device__ __forceinline__ u32x4 ld_global128(const void* p) { return *(const QG_GLOBAL u32x4*)(uintptr_t)p; }
+__device__ __forceinline__ u32x2 ld_global64(const void* p) { return *(const QG_GLOBAL u32x2*)(uintptr_t)p; }
 // 16 / 8 / 2 bytes at a 2-byte aligned address.
 __device__ __forceinline__ u32x4 ld_global128_a2(const void* p) {
     const u32x4_a2 v = *(const QG_GLOBAL u32x4_a2*)(uintptr_t)p;

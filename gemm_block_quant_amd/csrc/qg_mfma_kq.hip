@@ -61,13 +61,14 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
     const int K = a.K, M = a.M, N = a.N;
     const int nsteps = K / kMfmaKStep;  // K is a multiple of 256
 
-    // Register ring: activation chunks and this thread's weight piece (half a
-    // quarter super-block of one row: 16 code bytes, the 16-byte header and,
-    // for Q5_K, the 16 fifth-bit bytes of the same positions).
+    // Register ring: activation chunks and this thread's weight piece (a
+    // quarter of one row's 32 code bytes for the step, the row's 16-byte
+    // header and, for Q5_K, the 8 fifth-bit bytes of the same positions).
+    static_assert(BN * 4 == kMfmaThreads, "four threads per weight row");
     u32x4 xr[D][XCH];
-    u32x4 wq[D], wh[D], wf[D];
-    const int wr = tid >> 1, wpart = tid & 1;  // weight tile row and half owned by this thread
-    const bool w_owner = tid < BN * 2;
+    u32x4 wh[D];
+    u32x2 wq[D], wf[D];
+    const int wr = tid >> 2, wpart = tid & 3;  // weight tile row and quarter owned by this thread
 
     // Branch-free loads (clamped addresses, results selected afterwards): a
     // load under a branch makes the compiler wait for every outstanding load.
@@ -84,12 +85,11 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
             xr[j][c] = ok ? v : u32x4{0u, 0u, 0u, 0u};
         }
         const int n = n0 + wr;
-        const bool ok = w_owner && n < N;
-        const uint8_t* blk = a.w + (ok ? (size_t)n : 0) * a.rb + (size_t)(s >> 2) * G::BB;
+        const uint8_t* blk = a.w + (n < N ? (size_t)n : 0) * a.rb + (size_t)(s >> 2) * G::BB;
         const int g = s & 3;
-        wq[j] = ld_global128(blk + G::CODES + 32 * g + 16 * wpart);
+        wq[j] = ld_global64(blk + G::CODES + 32 * g + 8 * wpart);
         wh[j] = ld_global128(blk);
-        if constexpr (G::HIGH >= 0) wf[j] = ld_global128(blk + G::HIGH + 16 * wpart);
+        if constexpr (G::HIGH >= 0) wf[j] = ld_global64(blk + G::HIGH + 8 * wpart);
     };
     auto store = [&](int buf, int s, auto stage_tag) {
         constexpr int j = decltype(stage_tag)::value;
@@ -102,79 +102,56 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
             const int i = tid + c * kMfmaThreads;
             const int r = i >> 3, q = i & 7;
             *(lds_u32x4*)(tx + r * kMfmaRowBytes + q * 16) = xr[j][c];
-            // sum of this chunk's 8 values, then over the 4 chunks of the
-            // sub-block (lanes with the same i >> 2: a fixed butterfly order)
-            const uint32_t v[4] = {xr[j][c].x, xr[j][c].y, xr[j][c].z, xr[j][c].w};
-            float p = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                p += bf16_to_f32(v[e]);
-                p += bf16_to_f32(v[e] >> 16);
-            }
-            p += __shfl_xor(p, 1, 64);
-            p += __shfl_xor(p, 2, 64);
+            // sum of this chunk's 8 values (pairs dotted with (1, 1)), then over
+            // the 4 chunks of the sub-block: lanes xor 1, then xor 2 of a quad
+            // (element copies first: a bit cast of a vector element reads element 0)
+            const uint32_t e0 = xr[j][c].x, e1 = xr[j][c].y, e2 = xr[j][c].z, e3 = xr[j][c].w;
+            float p = dot2bf(e0, kBf16Ones, 0.f);
+            p = dot2bf(e1, kBf16Ones, p);
+            p = dot2bf(e2, kBf16Ones, p);
+            p = dot2bf(e3, kBf16Ones, p);
+            p += __builtin_amdgcn_update_dpp(0.f, p, kDppQuadXor1, 0xF, 0xF, false);
+            p += __builtin_amdgcn_update_dpp(0.f, p, kDppQuadXor2, 0xF, 0xF, false);
             if ((q & 3) == 0) txs[(q >> 2) * BM + r] = p;
         }
-        if (w_owner) {
-            // codes: bytes [16 part, 16 part + 16) of quarter g: low nibbles are
-            // positions 16 part .. + 15 of sub-block 2g, high nibbles of 2g + 1
-            const uint32_t cw[4] = {wq[j].x, wq[j].y, wq[j].z, wq[j].w};
-            uint32_t fw[4] = {0u, 0u, 0u, 0u};
-            const int g = s & 3;
-            if constexpr (G::HIGH >= 0) {
-                fw[0] = wf[j].x >> (2 * g);
-                fw[1] = wf[j].y >> (2 * g);
-                fw[2] = wf[j].z >> (2 * g);
-                fw[3] = wf[j].w >> (2 * g);
+        // codes: bytes [8 part, 8 part + 8) of quarter g; low nibbles are
+        // positions 8 part .. + 7 of sub-block 2g, high nibbles of 2g + 1
+        const int g = s & 3;
+        uint32_t l0 = wq[j].x & 0x0F0F0F0Fu, l1 = wq[j].y & 0x0F0F0F0Fu;
+        uint32_t h0 = (wq[j].x >> 4) & 0x0F0F0F0Fu, h1 = (wq[j].y >> 4) & 0x0F0F0F0Fu;
+        if constexpr (G::HIGH >= 0) {
+            // fifth bit of sub-block 2g + t at bit 2g + t of each H byte
+            const uint32_t f0 = wf[j].x >> (2 * g), f1 = wf[j].y >> (2 * g);
+            l0 |= (f0 << 4) & 0x10101010u;
+            l1 |= (f1 << 4) & 0x10101010u;
+            h0 |= (f0 << 3) & 0x10101010u;
+            h1 |= (f1 << 3) & 0x10101010u;
+        }
+        lds_u8* pw = tw + wr * kMfmaRowBytes;
+        *(lds_u32x4*)(pw + 16 * wpart) =
+            u32x4{bias128_pair(l0, kSelB0B1), bias128_pair(l0, kSelB2B3), bias128_pair(l1, kSelB0B1),
+                  bias128_pair(l1, kSelB2B3)};
+        *(lds_u32x4*)(pw + 64 + 16 * wpart) =
+            u32x4{bias128_pair(h0, kSelB0B1), bias128_pair(h0, kSelB2B3), bias128_pair(h1, kSelB0B1),
+                  bias128_pair(h1, kSelB2B3)};
+        if (wpart < 2) {
+            // 6-bit scale and min of sub-block jb = 2g + part (Q4_K packing over
+            // S[0..3], S[4..7], S[8..11]: jb < 4 whole in S[jb], S[jb + 4];
+            // jb >= 4 low bits in S[jb + 4], top bits in S[jb - 4] and S[jb])
+            const uint32_t S0 = wh[j].y, S1 = wh[j].z, S2 = wh[j].w;
+            const uint32_t o = 8u * (uint32_t)((2 * g + wpart) & 3);
+            uint32_t sc, m;
+            if (g < 2) {
+                sc = __builtin_amdgcn_ubfe(S0, o, 6);
+                m = __builtin_amdgcn_ubfe(S1, o, 6);
+            } else {
+                sc = __builtin_amdgcn_ubfe(S2, o, 4) | (__builtin_amdgcn_ubfe(S0, o + 6, 2) << 4);
+                m = __builtin_amdgcn_ubfe(S2, o + 4, 4) | (__builtin_amdgcn_ubfe(S1, o + 6, 2) << 4);
             }
-            uint32_t lo[8], hi[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t l = cw[e] & 0x0F0F0F0Fu, h = (cw[e] >> 4) & 0x0F0F0F0Fu;
-                if constexpr (G::HIGH >= 0) {
-                    l |= (fw[e] << 4) & 0x10101010u;
-                    h |= (fw[e] << 3) & 0x10101010u;
-                }
-                lo[2 * e] = bias128_pair(l, kSelB0B1);
-                lo[2 * e + 1] = bias128_pair(l, kSelB2B3);
-                hi[2 * e] = bias128_pair(h, kSelB0B1);
-                hi[2 * e + 1] = bias128_pair(h, kSelB2B3);
-            }
-            lds_u8* p = tw + wr * kMfmaRowBytes;
-            *(lds_u32x4*)(p + 32 * wpart) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-            *(lds_u32x4*)(p + 32 * wpart + 16) = u32x4{lo[4], lo[5], lo[6], lo[7]};
-            *(lds_u32x4*)(p + 64 + 32 * wpart) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-            *(lds_u32x4*)(p + 64 + 32 * wpart + 16) = u32x4{hi[4], hi[5], hi[6], hi[7]};
-            if (wpart == 0) {
-                // 6-bit scale and min of sub-blocks 2g and 2g + 1 (packing of
-                // Q4_K: j < 4 whole in S[j], S[j + 4]; j >= 4 low bits in
-                // S[j + 4], top bits in S[j - 4] and S[j])
-                // S[0..3], S[4..7], S[8..11]; sub-block jb = 4 h + jj reads byte jj
-                // of them (field offsets depend on g only: no indexed arrays)
-                const uint32_t S0 = wh[j].y, S1 = wh[j].z, S2 = wh[j].w;
-                float sc2[2], mn2[2];
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int jb = 2 * g + t;
-                    const uint32_t o = 8u * (uint32_t)(jb & 3);
-                    uint32_t sc, m;
-                    if (jb < 4) {
-                        sc = __builtin_amdgcn_ubfe(S0, o, 6);
-                        m = __builtin_amdgcn_ubfe(S1, o, 6);
-                    } else {
-                        sc = __builtin_amdgcn_ubfe(S2, o, 4) | (__builtin_amdgcn_ubfe(S0, o + 6, 2) << 4);
-                        m = __builtin_amdgcn_ubfe(S2, o + 4, 4) | (__builtin_amdgcn_ubfe(S1, o + 6, 2) << 4);
-                    }
-                    sc2[t] = (float)sc;
-                    mn2[t] = (float)m;
-                }
-                const float d = f16_to_f32(wh[j].x), dmin = f16_to_f32(wh[j].x >> 16);
-                const float s0 = d * sc2[0], s1 = d * sc2[1];
-                *(lds_u32x4*)((lds_u8*)ts + wr * 16) =
-                    u32x4{__builtin_bit_cast(uint32_t, s0), __builtin_bit_cast(uint32_t, s1),
-                          __builtin_bit_cast(uint32_t, -fmaf(dmin, mn2[0], 128.f * s0)),
-                          __builtin_bit_cast(uint32_t, -fmaf(dmin, mn2[1], 128.f * s1))};
-            }
+            const float d = f16_to_f32(wh[j].x), dmin = f16_to_f32(wh[j].x >> 16);
+            const float sv = d * (float)sc;
+            ts[wr * 4 + wpart] = sv;
+            ts[wr * 4 + 2 + wpart] = -fmaf(dmin, (float)m, 128.f * sv);
         }
     };
 
