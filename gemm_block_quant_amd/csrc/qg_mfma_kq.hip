@@ -70,26 +70,30 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
     u32x2 wq[D], wf[D];
     const int wr = tid >> 2, wpart = tid & 3;  // weight tile row and quarter owned by this thread
 
-    // Branch-free loads (clamped addresses, results selected afterwards): a
-    // load under a branch makes the compiler wait for every outstanding load.
+    // Per-thread row pointers, fixed for the whole K loop.  Rows past M or N
+    // read row M - 1 or row 0 instead: such rows feed only outputs that are
+    // never written, so no select is needed.
+    const uint16_t* xp[XCH];
+#pragma unroll
+    for (int c = 0; c < XCH; ++c) {
+        const int i = tid + c * kMfmaThreads;
+        xp[c] = a.x + (size_t)min(m0 + (i >> 3), M - 1) * a.ldx + (i & 7) * 8;
+    }
+    const uint8_t* wrow = a.w + (size_t)(n0 + wr < N ? n0 + wr : 0) * a.rb;
+    const uint8_t* wcode = wrow + G::CODES + 8 * wpart;
+    const uint8_t* whigh = wrow + (G::HIGH >= 0 ? G::HIGH : 0) + 8 * wpart;
+
+    // Loads without branches: a load under a branch makes the compiler wait
+    // for every outstanding load.
     auto load = [&](int s, auto stage_tag) {
         constexpr int j = decltype(stage_tag)::value;
         const int k0 = s * kMfmaKStep;
 #pragma unroll
-        for (int c = 0; c < XCH; ++c) {
-            const int i = tid + c * kMfmaThreads;
-            const int r = i >> 3, q = i & 7;
-            const int m = m0 + r, k = k0 + q * 8;
-            const bool ok = m < M;
-            const u32x4 v = ld_global128(a.x + (ok ? (size_t)m * a.ldx + k : 0));
-            xr[j][c] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-        }
-        const int n = n0 + wr;
-        const uint8_t* blk = a.w + (n < N ? (size_t)n : 0) * a.rb + (size_t)(s >> 2) * G::BB;
-        const int g = s & 3;
-        wq[j] = ld_global64(blk + G::CODES + 32 * g + 8 * wpart);
-        wh[j] = ld_global128(blk);
-        if constexpr (G::HIGH >= 0) wf[j] = ld_global64(blk + G::HIGH + 8 * wpart);
+        for (int c = 0; c < XCH; ++c) xr[j][c] = ld_global128(xp[c] + k0);
+        const size_t bo = (size_t)(s >> 2) * G::BB;
+        wq[j] = ld_global64(wcode + bo + 32 * (s & 3));
+        wh[j] = ld_global128(wrow + bo);
+        if constexpr (G::HIGH >= 0) wf[j] = ld_global64(whigh + bo);
     };
     auto store = [&](int buf, int s, auto stage_tag) {
         constexpr int j = decltype(stage_tag)::value;
