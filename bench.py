@@ -62,6 +62,7 @@ def workloads():
                                     6),
         "q6k_down_m1": Workload("Q6_K down-proj, N=5120 K=17408", qg.Q6_K, 5120, 17408, 1, 3),
         "q6k_down_m8": Workload("Q6_K down-proj, N=5120 K=17408", qg.Q6_K, 5120, 17408, 8, 3),
+        "q6k_down_m512": Workload("Q6_K down-proj prefill, N=5120 K=17408", qg.Q6_K, 5120, 17408, 512, 3),
         "q6k_head_m1": Workload("Q6_K LM head, N=248320 K=5120", qg.Q6_K, 248320, 5120, 1, 3),
         "q6k_head_m8": Workload("Q6_K LM head, N=248320 K=5120", qg.Q6_K, 248320, 5120, 8, 3),
         "nvfp4_up_m1": Workload("NVFP4 MLP, N=17408 K=5120", qg.NVFP4, 17408, 5120, 1, 4),

@@ -168,7 +168,7 @@ qg_status quant_gemm(const void* w, qg_format fmt, int64_t N, int64_t K, int64_t
                    ? QG_OK
                    : QG_EHIP;
     }
-    if ((fmt == QG_Q4_K || fmt == QG_Q5_K) && M >= kMfmaMinRows) {
+    if (M >= kMfmaMinRows && mfma_kquant_supported(fmt, (int)K)) {
         if (M > INT32_MAX) return QG_ESHAPE;
         return launch_mfma_kquant(fmt, (const uint8_t*)w, (int)N, (int)K, x, K, (int)M, y, N, (hipStream_t)stream) ==
                        hipSuccess

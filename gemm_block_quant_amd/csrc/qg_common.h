@@ -12,6 +12,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // global loads at any byte alignment).
 typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
 typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
+typedef uint32_t u32_a2 __attribute__((aligned(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -113,6 +114,7 @@ __device__ __forceinline__ u32x2 ld_global64_a2(const void* p) {
     const u32x2_a2 v = *(const QG_GLOBAL u32x2_a2*)(uintptr_t)p;
     return u32x2{v.x, v.y};
 }
+__device__ __forceinline__ uint32_t ld_global32_a2(const void* p) { return *(const QG_GLOBAL u32_a2*)(uintptr_t)p; }
 __device__ __forceinline__ uint32_t ld_global16(const void* p) { return *(const QG_GLOBAL uint16_t*)(uintptr_t)p; }
 __device__ __forceinline__ void st_global_f32(float* p, float v) { *(QG_GLOBAL float*)(uintptr_t)p = v; }
 

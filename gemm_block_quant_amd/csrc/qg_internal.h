@@ -43,8 +43,10 @@ hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int6
 constexpr int kMfmaMinRows = 32;
 hipError_t launch_mfma_nvfp4(const uint8_t* codes, const uint8_t* scales, const uint8_t* gbytes, int N, int K,
                              const uint16_t* x, int64_t ldx, int M, float* y, int64_t ldy, hipStream_t st);
-// Q4_K / Q5_K product for M >= kMfmaMinRows on the bf16 matrix cores (codes
-// as exact bf16, sub-block scales and mins in fp32).
+// Q4_K / Q5_K / Q6_K / Q8_0 product for M >= kMfmaMinRows on the bf16 matrix
+// cores (codes as exact bf16, sub-block scales and offsets in fp32), for the
+// formats and K that mfma_kquant_supported accepts.
+bool mfma_kquant_supported(int fmt, int K);
 hipError_t launch_mfma_kquant(int fmt, const uint8_t* w, int N, int K, const uint16_t* x, int64_t ldx, int M,
                               float* y, int64_t ldy, hipStream_t st);
 int num_cus();

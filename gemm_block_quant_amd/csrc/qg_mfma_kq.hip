@@ -1,74 +1,229 @@
-// qg_mfma_kq.hip -- Q4_K and Q5_K products for M >= 32 activation rows on the
-// bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
+// qg_mfma_kq.hip -- Q4_K, Q5_K, Q6_K and Q8_0 products for M >= 32 activation
+// rows on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
 //
 // Prefill must read each packed weight slab once for all rows rather than once
 // per few rows ("Qwen3.8-27B on one Tenstorrent P150", section "3. Porting the
 // 9B stack to 27B geometry": re-streaming the weights per 32 rows was the
-// prefill bug).  A dequantized K-quant weight d*sc*q - dmin*m is not exact in
-// bf16, but its code is: the tile holds bf16(128 + q) (q <= 31, exact), the
-// matrix cores form D = sum (128 + q) x over each 32-value sub-block in fp32,
-// and the sub-block's scale and min enter in fp32 afterwards:
-//   sum_k w x = s * D + t * X,  s = d * sc,  t = -(128 s + dmin * m),
-// X = sum of the sub-block's 32 activations (the factorisation of the decode
-// path, applied per 32 x 32 output block).
+// prefill bug).  A dequantized weight of these formats is not exact in bf16,
+// but inside one sub-block it is an affine function of an integer code that
+// is: w = s * v + t with v exact in bf16 and s, t fp32 per weight row and
+// sub-block.  The tile holds v, the matrix cores form D = sum v x over the
+// sub-block in fp32, and the scale and offset enter in fp32 afterwards:
+//   sum_k w x = s * D + t * X,   X = sum of the sub-block's activations.
+//   Q4_K, Q5_K (32 values): v = 128 + q, s = d sc, t = -(128 s + dmin m)
+//   Q6_K (16 values):       v = 128 + q, s = d sc, t = -160 s   (w = s (q - 32))
+//   Q8_0 (32 values):       v = q + 128 (the code as an unsigned byte),
+//                           s = d, t = -128 d
+// (the factorisation of the decode path, applied per 32 x 32 output block).
 //
-// Tiling as the NVFP4 tile kernel: a 256-thread workgroup computes a BM x BN
-// tile of y, four waves own (BM/2) x (BN/2) quarters as 32x32 accumulators; a
-// K step is 64 values (two sub-blocks, one quarter of a super-block) staged in
-// one of two LDS buffers: activations, their two sub-block sums per row, the
-// decoded codes, and per weight row (s, t) of both sub-blocks.  The loads of the
-// next steps run in a register ring several steps ahead.
+// Tiling: a 256-thread workgroup computes a BM x 64 tile of y, four waves own
+// (BM/2) x 32 quarters as 32x32 accumulators.  A K step is 64 values staged in
+// one of two LDS buffers: activations, their sub-block sums per row, the tile
+// values v, and per weight row (s, t) of each sub-block.  Four threads decode
+// each weight row.  The loads of the next steps run in a register ring.
 #include "qg_mfma.h"
 
 namespace qg {
 
-
 struct KqArgs {
     const uint16_t* x;  // bf16 [M, K], row stride ldx
     int64_t ldx;
-    const uint8_t* w;  // packed rows of K/256 super-blocks
+    const uint8_t* w;  // packed rows
     int64_t rb;        // bytes per weight row
     float* y;          // fp32 [M, N], row stride ldy
     int64_t ldy;
     int M, N, K;
 };
 
-template <int F> struct KqGeom;
-template <> struct KqGeom<QG_Q4_K> {
-    static constexpr int BB = 144, CODES = 16, HIGH = -1;
+// bf16 pair from the upper halves of two exactly representable fp32 values.
+__device__ __forceinline__ uint32_t bf16_pair_exact(float lo, float hi) {
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+}
+
+// Per-format pieces.  Each provides:
+//   SUB            values per sub-block (32 or 16); a step holds 64 / SUB
+//   Ring           registers one thread holds for one step
+//   x_step(s)      offset of step s's first activation (uniform)
+//   x_chunk(q)     offset of the step's 8-value chunk q (tile columns 8q..8q+7)
+//   load(wrow, s, part)               this thread's share of row wrow for step s
+//   decode(r, s, part, trow, srow)    tile values of the share into the LDS row
+//                                     trow, (s, t) of the row's sub-blocks into srow
+template <int F> struct KqFmt;
+
+// Q4_K / Q5_K: step s is quarter g = s & 3 of super-block s >> 2: sub-blocks
+// 2g (low nibbles of code bytes 32g..32g+31) and 2g + 1 (high nibbles).  Part
+// p decodes code bytes 8p..8p+7 of the quarter: positions 8p..8p+7 of both.
+template <int BB, int CODES, int HIGH> struct KqFmtK4 {
+    static constexpr int SUB = 32;
+    struct Ring {
+        u32x4 hdr;  // d, dmin, 12 scale bytes
+        u32x2 q;    // 8 code bytes
+        u32x2 f;    // Q5_K: the 8 fifth-bit bytes of the same positions
+    };
+    __device__ static int x_step(int s) { return 64 * s; }
+    __device__ static int x_chunk(int q) { return 8 * q; }
+    __device__ static Ring load(const uint8_t* wrow, int s, int part) {
+        const uint8_t* blk = wrow + (size_t)(s >> 2) * BB;
+        Ring r;
+        r.hdr = ld_global128(blk);
+        r.q = ld_global64(blk + CODES + 32 * (s & 3) + 8 * part);
+        if constexpr (HIGH >= 0) r.f = ld_global64(blk + HIGH + 8 * part);
+        return r;
+    }
+    __device__ static void decode(const Ring& r, int s, int part, lds_u8* trow, lds_f32* srow) {
+        const int g = s & 3;
+        uint32_t l0 = r.q.x & 0x0F0F0F0Fu, l1 = r.q.y & 0x0F0F0F0Fu;
+        uint32_t h0 = (r.q.x >> 4) & 0x0F0F0F0Fu, h1 = (r.q.y >> 4) & 0x0F0F0F0Fu;
+        if constexpr (HIGH >= 0) {
+            // fifth bit of sub-block 2g + t at bit 2g + t of each H byte
+            const uint32_t f0 = r.f.x >> (2 * g), f1 = r.f.y >> (2 * g);
+            l0 |= (f0 << 4) & 0x10101010u;
+            l1 |= (f1 << 4) & 0x10101010u;
+            h0 |= (f0 << 3) & 0x10101010u;
+            h1 |= (f1 << 3) & 0x10101010u;
+        }
+        *(lds_u32x4*)(trow + 16 * part) = u32x4{bias128_pair(l0, kSelB0B1), bias128_pair(l0, kSelB2B3),
+                                                bias128_pair(l1, kSelB0B1), bias128_pair(l1, kSelB2B3)};
+        *(lds_u32x4*)(trow + 64 + 16 * part) = u32x4{bias128_pair(h0, kSelB0B1), bias128_pair(h0, kSelB2B3),
+                                                     bias128_pair(h1, kSelB0B1), bias128_pair(h1, kSelB2B3)};
+        if (part < 2) {
+            // 6-bit scale and min of sub-block jb = 2g + part (packing over
+            // S[0..3], S[4..7], S[8..11]: jb < 4 whole in S[jb], S[jb + 4];
+            // jb >= 4 low bits in S[jb + 4], top bits in S[jb - 4] and S[jb])
+            const uint32_t S0 = r.hdr.y, S1 = r.hdr.z, S2 = r.hdr.w;
+            const uint32_t o = 8u * (uint32_t)((2 * g + part) & 3);
+            uint32_t sc, m;
+            if (g < 2) {
+                sc = __builtin_amdgcn_ubfe(S0, o, 6);
+                m = __builtin_amdgcn_ubfe(S1, o, 6);
+            } else {
+                sc = __builtin_amdgcn_ubfe(S2, o, 4) | (__builtin_amdgcn_ubfe(S0, o + 6, 2) << 4);
+                m = __builtin_amdgcn_ubfe(S2, o + 4, 4) | (__builtin_amdgcn_ubfe(S1, o + 6, 2) << 4);
+            }
+            const float d = f16_to_f32(r.hdr.x), dmin = f16_to_f32(r.hdr.x >> 16);
+            const float sv = d * (float)sc;
+            srow[part] = sv;
+            srow[2 + part] = -fmaf(dmin, (float)m, 128.f * sv);
+        }
+    }
 };
-template <> struct KqGeom<QG_Q5_K> {
-    static constexpr int BB = 176, CODES = 48, HIGH = 16;  // fifth bits at [16, 48)
+template <> struct KqFmt<QG_Q4_K> : KqFmtK4<144, 16, -1> {};
+template <> struct KqFmt<QG_Q5_K> : KqFmtK4<176, 48, 16> {};  // fifth bits at [16, 48)
+
+// Q8_0: step s is blocks 2s and 2s + 1 (34 bytes each: fp16 d, 32 int8 codes,
+// 2-byte aligned).  Part p decodes codes 16 (p & 1) .. + 15 of block 2s + p / 2.
+template <> struct KqFmt<QG_Q8_0> {
+    static constexpr int SUB = 32;
+    struct Ring {
+        u32x4 q;     // 16 codes
+        uint32_t d;  // fp16 d of the block
+    };
+    __device__ static int x_step(int s) { return 64 * s; }
+    __device__ static int x_chunk(int q) { return 8 * q; }
+    __device__ static Ring load(const uint8_t* wrow, int s, int part) {
+        const uint8_t* blk = wrow + (size_t)(2 * s + (part >> 1)) * 34;
+        Ring r;
+        r.q = ld_global128_a2(blk + 2 + 16 * (part & 1));
+        r.d = ld_global16(blk);
+        return r;
+    }
+    __device__ static void decode(const Ring& r, int s, int part, lds_u8* trow, lds_f32* srow) {
+        // v = q + 128: the code with its sign bit flipped, read unsigned (0..255, exact in bf16)
+        const uint32_t w0 = r.q.x ^ 0x80808080u, w1 = r.q.y ^ 0x80808080u, w2 = r.q.z ^ 0x80808080u,
+                       w3 = r.q.w ^ 0x80808080u;
+        const uint32_t w[4] = {w0, w1, w2, w3};
+        uint32_t o[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            o[2 * e] = bf16_pair_exact((float)(w[e] & 0xFFu), (float)((w[e] >> 8) & 0xFFu));
+            o[2 * e + 1] = bf16_pair_exact((float)((w[e] >> 16) & 0xFFu), (float)(w[e] >> 24));
+        }
+        *(lds_u32x4*)(trow + 32 * part) = u32x4{o[0], o[1], o[2], o[3]};
+        *(lds_u32x4*)(trow + 32 * part + 16) = u32x4{o[4], o[5], o[6], o[7]};
+        if ((part & 1) == 0) {
+            const float d = f16_to_f32(r.d);
+            srow[part >> 1] = d;
+            srow[2 + (part >> 1)] = -128.f * d;
+        }
+    }
+};
+
+// Q6_K (210 bytes, 2-byte aligned): value 128 n + 32 j + l of a super-block
+// (n < 2, j < 4, l < 32) has low bits in byte 64 n + l (j = 0, 2: low / high
+// nibble) or 64 n + 32 + l (j = 1, 3), high bits 2j..2j+1 of byte 128 + 32 n
+// + l, scale int8 at 192 + 8 n + 2 j + l / 16, d fp16 at 208.  Step s takes
+// n = (s >> 1) & 1 and l in [16 h, 16 h + 16), h = s & 1: its 64 values are
+// four sub-blocks of 16 (tile columns 16 j .. 16 j + 15 hold quadrant j), and
+// every code byte of the super-block is read by exactly one step.  Part p
+// decodes l = 16 h + 4 p .. + 3 of the four quadrants.
+template <> struct KqFmt<QG_Q6_K> {
+    static constexpr int SUB = 16;
+    struct Ring {
+        uint32_t qa, qb, qh;  // low-bit bytes (quadrants 0/2, 1/3) and high-bit bytes of 4 positions
+        u32x2 sc;             // scales 8n .. 8n + 7
+        uint32_t d;
+    };
+    __device__ static int x_step(int s) { return 256 * (s >> 2) + 128 * ((s >> 1) & 1) + 16 * (s & 1); }
+    __device__ static int x_chunk(int q) { return 32 * (q >> 1) + 8 * (q & 1); }
+    __device__ static Ring load(const uint8_t* wrow, int s, int part) {
+        const uint8_t* blk = wrow + (size_t)(s >> 2) * 210;
+        const int n = (s >> 1) & 1, l = 16 * (s & 1) + 4 * part;
+        Ring r;
+        r.qa = ld_global32_a2(blk + 64 * n + l);
+        r.qb = ld_global32_a2(blk + 64 * n + 32 + l);
+        r.qh = ld_global32_a2(blk + 128 + 32 * n + l);
+        r.sc = ld_global64_a2(blk + 192 + 8 * n);
+        r.d = ld_global16(blk + 208);
+        return r;
+    }
+    __device__ static void decode(const Ring& r, int s, int part, lds_u8* trow, lds_f32* srow) {
+        const uint32_t q0 = (r.qa & 0x0F0F0F0Fu) | ((r.qh << 4) & 0x30303030u);
+        const uint32_t q1 = (r.qb & 0x0F0F0F0Fu) | ((r.qh << 2) & 0x30303030u);
+        const uint32_t q2 = ((r.qa >> 4) & 0x0F0F0F0Fu) | (r.qh & 0x30303030u);
+        const uint32_t q3 = ((r.qb >> 4) & 0x0F0F0F0Fu) | ((r.qh >> 2) & 0x30303030u);
+        *(lds_u32x2*)(trow + 8 * part) = u32x2{bias128_pair(q0, kSelB0B1), bias128_pair(q0, kSelB2B3)};
+        *(lds_u32x2*)(trow + 32 + 8 * part) = u32x2{bias128_pair(q1, kSelB0B1), bias128_pair(q1, kSelB2B3)};
+        *(lds_u32x2*)(trow + 64 + 8 * part) = u32x2{bias128_pair(q2, kSelB0B1), bias128_pair(q2, kSelB2B3)};
+        *(lds_u32x2*)(trow + 96 + 8 * part) = u32x2{bias128_pair(q3, kSelB0B1), bias128_pair(q3, kSelB2B3)};
+        // this part writes (s, t) of quadrant j = part: scale byte 2 part + h of sc
+        const int idx = 2 * part + (s & 1);
+        const uint32_t word = (idx >> 2) ? r.sc.y : r.sc.x;
+        const int sc = __builtin_amdgcn_sbfe((int)word, 8 * (idx & 3), 8);
+        const float c = f16_to_f32(r.d) * (float)sc;
+        srow[part] = c;
+        srow[4 + part] = -160.f * c;
+    }
 };
 
 // D: K steps of loads in flight in the register ring (an even number).
-template <int F, int BM, int BN, int D>
+template <int F, int BM, int D>
 __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
-    using G = KqGeom<F>;
-    constexpr int FM = BM / 64, FN = BN / 64;     // 32x32 fragments per wave
-    constexpr int XCH = BM * 8 / kMfmaThreads;    // 16-byte activation chunks per thread per step
-    constexpr int TILE_X = BM * kMfmaRowBytes;    // activations (bf16, padded rows)
-    constexpr int TILE_W = BN * kMfmaRowBytes;    // codes as bf16(128 + q)
-    constexpr int TILE_S = BN * 16;               // per weight row: s0, s1, t0, t1
-    constexpr int TILE_XS = 2 * BM * 4;           // per sub-block and activation row: X
+    using Fmt = KqFmt<F>;
+    constexpr int BN = 64;
+    constexpr int NSUB = kMfmaKStep / Fmt::SUB;  // sub-blocks per step
+    constexpr int KPS = Fmt::SUB / 16;           // 32x32x16 products per sub-block
+    constexpr int CPS = Fmt::SUB / 8;            // 8-value chunks per sub-block
+    constexpr int FM = BM / 64, FN = BN / 64;    // 32x32 fragments per wave
+    constexpr int XCH = BM * 8 / kMfmaThreads;   // 16-byte activation chunks per thread per step
+    constexpr int TILE_X = BM * kMfmaRowBytes;   // activations (bf16, padded rows)
+    constexpr int TILE_W = BN * kMfmaRowBytes;   // tile values v (bf16)
+    constexpr int TILE_S = BN * 8 * NSUB;        // per weight row: s of each sub-block, then t
+    constexpr int TILE_XS = NSUB * BM * 4;       // per sub-block and activation row: X
     constexpr int BUF = TILE_X + TILE_W + TILE_S + TILE_XS;
+    static_assert(BN * 4 == kMfmaThreads, "four threads per weight row");
     __shared__ __attribute__((aligned(16))) uint8_t smem_generic[2 * BUF];
     lds_u8* smem = (lds_u8*)smem_generic;
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
     const int wm = (wid >> 1) * (BM / 2), wn = (wid & 1) * (BN / 2);
-    const int K = a.K, M = a.M, N = a.N;
-    const int nsteps = K / kMfmaKStep;  // K is a multiple of 256
+    const int M = a.M, N = a.N;
+    const int nsteps = a.K / kMfmaKStep;  // K is a multiple of 64
 
-    // Register ring: activation chunks and this thread's weight piece (a
-    // quarter of one row's 32 code bytes for the step, the row's 16-byte
-    // header and, for Q5_K, the 8 fifth-bit bytes of the same positions).
-    static_assert(BN * 4 == kMfmaThreads, "four threads per weight row");
+    // Register ring: activation chunks and this thread's weight share.
     u32x4 xr[D][XCH];
-    u32x4 wh[D];
-    u32x2 wq[D], wf[D];
-    const int wr = tid >> 2, wpart = tid & 3;  // weight tile row and quarter owned by this thread
+    typename Fmt::Ring wring[D];
+    const int wrow_i = tid >> 2, part = tid & 3;  // weight tile row and quarter decoded by this thread
 
     // Per-thread row pointers, fixed for the whole K loop.  Rows past M or N
     // read row M - 1 or row 0 instead: such rows feed only outputs that are
@@ -77,23 +232,18 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
 #pragma unroll
     for (int c = 0; c < XCH; ++c) {
         const int i = tid + c * kMfmaThreads;
-        xp[c] = a.x + (size_t)min(m0 + (i >> 3), M - 1) * a.ldx + (i & 7) * 8;
+        xp[c] = a.x + (size_t)min(m0 + (i >> 3), M - 1) * a.ldx + Fmt::x_chunk(i & 7);
     }
-    const uint8_t* wrow = a.w + (size_t)(n0 + wr < N ? n0 + wr : 0) * a.rb;
-    const uint8_t* wcode = wrow + G::CODES + 8 * wpart;
-    const uint8_t* whigh = wrow + (G::HIGH >= 0 ? G::HIGH : 0) + 8 * wpart;
+    const uint8_t* wrow = a.w + (size_t)(n0 + wrow_i < N ? n0 + wrow_i : 0) * a.rb;
 
     // Loads without branches: a load under a branch makes the compiler wait
     // for every outstanding load.
     auto load = [&](int s, auto stage_tag) {
         constexpr int j = decltype(stage_tag)::value;
-        const int k0 = s * kMfmaKStep;
+        const int k0 = Fmt::x_step(s);
 #pragma unroll
         for (int c = 0; c < XCH; ++c) xr[j][c] = ld_global128(xp[c] + k0);
-        const size_t bo = (size_t)(s >> 2) * G::BB;
-        wq[j] = ld_global64(wcode + bo + 32 * (s & 3));
-        wh[j] = ld_global128(wrow + bo);
-        if constexpr (G::HIGH >= 0) wf[j] = ld_global64(whigh + bo);
+        wring[j] = Fmt::load(wrow, s, part);
     };
     auto store = [&](int buf, int s, auto stage_tag) {
         constexpr int j = decltype(stage_tag)::value;
@@ -107,7 +257,7 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
             const int r = i >> 3, q = i & 7;
             *(lds_u32x4*)(tx + r * kMfmaRowBytes + q * 16) = xr[j][c];
             // sum of this chunk's 8 values (pairs dotted with (1, 1)), then over
-            // the 4 chunks of the sub-block: lanes xor 1, then xor 2 of a quad
+            // the chunks of the sub-block: lanes xor 1 (and xor 2) of a quad
             // (element copies first: a bit cast of a vector element reads element 0)
             const uint32_t e0 = xr[j][c].x, e1 = xr[j][c].y, e2 = xr[j][c].z, e3 = xr[j][c].w;
             float p = dot2bf(e0, kBf16Ones, 0.f);
@@ -115,48 +265,10 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
             p = dot2bf(e2, kBf16Ones, p);
             p = dot2bf(e3, kBf16Ones, p);
             p += __builtin_amdgcn_update_dpp(0.f, p, kDppQuadXor1, 0xF, 0xF, false);
-            p += __builtin_amdgcn_update_dpp(0.f, p, kDppQuadXor2, 0xF, 0xF, false);
-            if ((q & 3) == 0) txs[(q >> 2) * BM + r] = p;
+            if constexpr (CPS == 4) p += __builtin_amdgcn_update_dpp(0.f, p, kDppQuadXor2, 0xF, 0xF, false);
+            if ((q & (CPS - 1)) == 0) txs[(q / CPS) * BM + r] = p;
         }
-        // codes: bytes [8 part, 8 part + 8) of quarter g; low nibbles are
-        // positions 8 part .. + 7 of sub-block 2g, high nibbles of 2g + 1
-        const int g = s & 3;
-        uint32_t l0 = wq[j].x & 0x0F0F0F0Fu, l1 = wq[j].y & 0x0F0F0F0Fu;
-        uint32_t h0 = (wq[j].x >> 4) & 0x0F0F0F0Fu, h1 = (wq[j].y >> 4) & 0x0F0F0F0Fu;
-        if constexpr (G::HIGH >= 0) {
-            // fifth bit of sub-block 2g + t at bit 2g + t of each H byte
-            const uint32_t f0 = wf[j].x >> (2 * g), f1 = wf[j].y >> (2 * g);
-            l0 |= (f0 << 4) & 0x10101010u;
-            l1 |= (f1 << 4) & 0x10101010u;
-            h0 |= (f0 << 3) & 0x10101010u;
-            h1 |= (f1 << 3) & 0x10101010u;
-        }
-        lds_u8* pw = tw + wr * kMfmaRowBytes;
-        *(lds_u32x4*)(pw + 16 * wpart) =
-            u32x4{bias128_pair(l0, kSelB0B1), bias128_pair(l0, kSelB2B3), bias128_pair(l1, kSelB0B1),
-                  bias128_pair(l1, kSelB2B3)};
-        *(lds_u32x4*)(pw + 64 + 16 * wpart) =
-            u32x4{bias128_pair(h0, kSelB0B1), bias128_pair(h0, kSelB2B3), bias128_pair(h1, kSelB0B1),
-                  bias128_pair(h1, kSelB2B3)};
-        if (wpart < 2) {
-            // 6-bit scale and min of sub-block jb = 2g + part (Q4_K packing over
-            // S[0..3], S[4..7], S[8..11]: jb < 4 whole in S[jb], S[jb + 4];
-            // jb >= 4 low bits in S[jb + 4], top bits in S[jb - 4] and S[jb])
-            const uint32_t S0 = wh[j].y, S1 = wh[j].z, S2 = wh[j].w;
-            const uint32_t o = 8u * (uint32_t)((2 * g + wpart) & 3);
-            uint32_t sc, m;
-            if (g < 2) {
-                sc = __builtin_amdgcn_ubfe(S0, o, 6);
-                m = __builtin_amdgcn_ubfe(S1, o, 6);
-            } else {
-                sc = __builtin_amdgcn_ubfe(S2, o, 4) | (__builtin_amdgcn_ubfe(S0, o + 6, 2) << 4);
-                m = __builtin_amdgcn_ubfe(S2, o + 4, 4) | (__builtin_amdgcn_ubfe(S1, o + 6, 2) << 4);
-            }
-            const float d = f16_to_f32(wh[j].x), dmin = f16_to_f32(wh[j].x >> 16);
-            const float sv = d * (float)sc;
-            ts[wr * 4 + wpart] = sv;
-            ts[wr * 4 + 2 + wpart] = -fmaf(dmin, (float)m, 128.f * sv);
-        }
+        Fmt::decode(wring[j], s, part, tw + wrow_i * kMfmaRowBytes, ts + wrow_i * 2 * NSUB);
     };
 
     // One fp32 accumulator per fragment takes both terms: t * X from the
@@ -175,30 +287,33 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
         const lds_u8* tw = tx + TILE_X;
         const lds_f32* ts = (const lds_f32*)(tw + TILE_W);
         const lds_f32* txs = (const lds_f32*)((const lds_u8*)ts + TILE_S);
-        // t * X of both sub-blocks in one 32x32x2 fp32 product per fragment:
-        // A[m][k] = X(row m, sub-block k), lane l holds m = l % 32, k = l / 32;
-        // B[k][n] = t(row n, sub-block k), same lane mapping.
-        float xa[FM], tb[FN], sv[FN][2];
+        // t * X of two sub-blocks per 32x32x2 fp32 product:
+        // A[m][k] = X(row m, sub-block 2p + k), lane l holds m = l % 32, k = l / 32;
+        // B[k][n] = t(row n, sub-block 2p + k), same lane mapping.
 #pragma unroll
-        for (int i = 0; i < FM; ++i) xa[i] = txs[half * BM + wm + 32 * i + frow];
+        for (int pp = 0; pp < NSUB / 2; ++pp) {
+            float xa[FM], tb[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int row = (wn + 32 * j + frow) * 4;
-            tb[j] = ts[row + 2 + half];
-            sv[j][0] = ts[row];
-            sv[j][1] = ts[row + 1];
+            for (int i = 0; i < FM; ++i) xa[i] = txs[(2 * pp + half) * BM + wm + 32 * i + frow];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) tb[j] = ts[(wn + 32 * j + frow) * 2 * NSUB + NSUB + 2 * pp + half];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa[i], tb[j], acc[i][j], 0, 0, 0);
         }
+        float sv[FN][NSUB];
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa[i], tb[j], acc[i][j], 0, 0, 0);
+            for (int sb = 0; sb < NSUB; ++sb) sv[j][sb] = ts[(wn + 32 * j + frow) * 2 * NSUB + sb];
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            bf16x8_t fa[FM][2], fb[FN][2];
+        for (int sb = 0; sb < NSUB; ++sb) {
+            bf16x8_t fa[FM][KPS], fb[FN][KPS];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int kk = 2 * sb + h;
+            for (int h = 0; h < KPS; ++h) {
+                const int kk = KPS * sb + h;
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
                     fa[i][h] = __builtin_bit_cast(
@@ -212,13 +327,17 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    // D = sum (128 + q) x over the sub-block, then acc += s * D
+                    // D = sum v x over the sub-block, then acc += s * D
                     f32x16 dsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][0], fb[j][0], f32x16{}, 0, 0, 0);
-                    dsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][1], fb[j][1], dsum, 0, 0, 0);
+#pragma unroll
+                    for (int h = 1; h < KPS; ++h)
+                        dsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][h], fb[j][h], dsum, 0, 0, 0);
                     const float s = sv[j][sb];
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(s, dsum[r], acc[i][j][r]);
                 }
+            // with four sub-blocks, one sub-block's products live at a time (registers)
+            if constexpr (NSUB > 2) __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -277,26 +396,34 @@ static hipError_t launch_kq(const KqArgs& a, hipStream_t st) {
     const long tiles = (long)((a.N + 63) / 64) * ((a.M + 127) / 128);
     if (tiles >= cus) {
         dim3 grid((a.N + 63) / 64, (a.M + 127) / 128);
-        hipLaunchKernelGGL((k_mfma_kq<F, 128, 64, 2>), grid, dim3(kMfmaThreads), 0, st, a);
+        hipLaunchKernelGGL((k_mfma_kq<F, 128, 2>), grid, dim3(kMfmaThreads), 0, st, a);
     } else {
         dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
-        hipLaunchKernelGGL((k_mfma_kq<F, 64, 64, 4>), grid, dim3(kMfmaThreads), 0, st, a);
+        hipLaunchKernelGGL((k_mfma_kq<F, 64, 4>), grid, dim3(kMfmaThreads), 0, st, a);
     }
     return hipGetLastError();
+}
+
+bool mfma_kquant_supported(int fmt, int K) {
+    switch (fmt) {
+        case QG_Q4_K:
+        case QG_Q5_K:
+        case QG_Q6_K: return true;                 // K is a multiple of 256
+        case QG_Q8_0: return K % kMfmaKStep == 0;  // whole 64-value steps
+        default: return false;
+    }
 }
 
 hipError_t launch_mfma_kquant(int fmt, const uint8_t* w, int N, int K, const uint16_t* x, int64_t ldx, int M,
                               float* y, int64_t ldy, hipStream_t st) {
     KqArgs a = {x, ldx, w, 0, y, ldy, M, N, K};
-    if (fmt == QG_Q4_K) {
-        a.rb = (int64_t)(K / 256) * KqGeom<QG_Q4_K>::BB;
-        return launch_kq<QG_Q4_K>(a, st);
+    switch (fmt) {
+        case QG_Q4_K: a.rb = (int64_t)(K / 256) * 144; return launch_kq<QG_Q4_K>(a, st);
+        case QG_Q5_K: a.rb = (int64_t)(K / 256) * 176; return launch_kq<QG_Q5_K>(a, st);
+        case QG_Q6_K: a.rb = (int64_t)(K / 256) * 210; return launch_kq<QG_Q6_K>(a, st);
+        case QG_Q8_0: a.rb = (int64_t)(K / 32) * 34; return launch_kq<QG_Q8_0>(a, st);
+        default: return hipErrorInvalidValue;
     }
-    if (fmt == QG_Q5_K) {
-        a.rb = (int64_t)(K / 256) * KqGeom<QG_Q5_K>::BB;
-        return launch_kq<QG_Q5_K>(a, st);
-    }
-    return hipErrorInvalidValue;
 }
 
 }  // namespace qg

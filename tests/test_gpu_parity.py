@@ -93,6 +93,10 @@ PRODUCT_CASES = [
     (qg.Q4_K, 200, 5120, 37), (qg.Q4_K, 130, 256, 33), (qg.Q4_K, 300, 1280, 130), (qg.Q4_K, 1000, 512, 64),
     (qg.Q4_K, 4100, 768, 450),
     (qg.Q5_K, 200, 5120, 37), (qg.Q5_K, 64, 256, 32), (qg.Q5_K, 300, 1792, 130), (qg.Q5_K, 4100, 768, 450),
+    (qg.Q6_K, 200, 5120, 37), (qg.Q6_K, 130, 256, 33), (qg.Q6_K, 300, 1792, 130), (qg.Q6_K, 4100, 768, 450),
+    (qg.Q8_0, 200, 1024, 37), (qg.Q8_0, 130, 64, 33), (qg.Q8_0, 300, 1088, 130), (qg.Q8_0, 4100, 768, 450),
+    # Q8_0 with K % 64 == 32 keeps the 16-row passes
+    (qg.Q8_0, 100, 1056, 40),
 ]
 
 
@@ -164,7 +168,8 @@ FULL = [
     (qg.NVFP4, 17408, 5120, 1), (qg.NVFP4, 17408, 5120, 8),
     (qg.NVFP4, 5120, 17408, 1), (qg.NVFP4, 5120, 17408, 8),
     (qg.NVFP4, 17408, 5120, 512), (qg.NVFP4, 5120, 17408, 512),
-    (qg.Q4_K, 2 * 17408, 5120, 512), (qg.Q5_K, 2 * 17408, 5120, 512),
+    (qg.Q4_K, 2 * 17408, 5120, 512), (qg.Q5_K, 2 * 17408, 5120, 512), (qg.Q6_K, 5120, 17408, 512),
+    (qg.Q8_0, 1024, 1024, 512),
 ]
 
 
@@ -182,7 +187,8 @@ def test_full_size_sampled(fmt, N, K, M):
     assert_band(y[:, cols], y_ref, bound, "full fmt %d N %d K %d M %d" % (fmt, N, K, M))
 
 
-@pytest.mark.parametrize("fmt,N,K", [(qg.NVFP4, 1000, 1040), (qg.Q4_K, 4100, 768), (qg.Q5_K, 4100, 768)])
+@pytest.mark.parametrize("fmt,N,K", [(qg.NVFP4, 1000, 1040), (qg.Q4_K, 4100, 768), (qg.Q5_K, 4100, 768),
+                                     (qg.Q6_K, 4100, 768), (qg.Q8_0, 4100, 768)])
 def test_mfma_rows_independent_of_tiling_and_repeat(fmt, N, K):
     """M >= 32 on the matrix cores: each output is one fixed fp32 accumulation
     over K, so the rows of a 37-row call equal those rows of a 512-row call
