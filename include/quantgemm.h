@@ -67,9 +67,9 @@
  * in a fixed order: results are deterministic run to run, row m of any
  * quant_gemm call with M <= 16 is bitwise equal to quant_gemv on x[m], and
  * such a call is bitwise equal to quant_grouped_gemm with E = 1 and ids =
- * NULL.  QG_NVFP4, QG_Q4_K and QG_Q5_K with M >= 32 accumulate on the matrix
- * cores in another (still fixed) order: their rows do not depend on M or on
- * the other rows.
+ * NULL.  Calls with M >= 32 that run on the matrix cores (below) accumulate
+ * in another (still fixed) order: their rows do not depend on M or on the
+ * other rows.
  */
 #ifndef QUANTGEMM_H
 #define QUANTGEMM_H
@@ -111,11 +111,12 @@ qg_status quant_gemv(const void* w, qg_format fmt, int64_t N, int64_t K, const u
  * x: bf16 [M, K] row-major; y: fp32 [M, N] row-major (overwritten).
  * Each weight block is read once per call for M <= 16 (speculative-verify
  * blocks of 8 positions: "Qwen3.8-27B on one Tenstorrent P150", section "5.
- * DFlash2 on Blackhole"); QG_NVFP4, QG_Q4_K and QG_Q5_K with M >= 32 run
- * bf16 matrix-core tile paths that read each weight block once per tile row of
- * activations ("Qwen3.8-27B on one Tenstorrent P150", section "3. Porting the
- * 9B stack to 27B geometry": prefill must not re-stream the weights per few
- * rows); QG_Q8_0 and QG_Q6_K with M > 16 take passes of 16 rows. */
+ * DFlash2 on Blackhole").  With M >= 32 every format runs a bf16 matrix-core
+ * tile path that reads each weight block once per tile of 64 or 128
+ * activation rows ("Qwen3.8-27B on one Tenstorrent P150", section "3. Porting
+ * the 9B stack to 27B geometry": prefill must not re-stream the weights per
+ * few rows); QG_Q8_0 does so when K is a multiple of 64.  Other calls with
+ * M > 16 take passes of 16 rows. */
 qg_status quant_gemm(const void* w, qg_format fmt, int64_t N, int64_t K, int64_t M, const uint16_t* x, float* y,
                      void* stream);
 
