@@ -34,6 +34,10 @@
  * UNPINNED (no GGUF bytes, gguf-py or llama.cpp are available); the layout is
  * pinned only by encoder round trips written independently in the tests.
  *
+ * orc_moe_block composes these into the mixture-of-experts block (gate|up
+ * product, SwiGLU rounded once to bf16, down product, routing-weighted sum);
+ * its definition and sources are at the function.
+ *
  * Exactness: every DEQ below is evaluated in fp64, where it is exact (the
  * operands carry at most 30 significant bits in total), and then rounded once
  * to fp32 (round to nearest even, the C default).  Q8_0 and Q6_K products are
@@ -334,6 +338,125 @@ int orc_gemm(int fmt, const uint8_t* w, long long E, long long N, long long K, l
         }
         free(wrow);
     }
+    return 0;
+}
+
+/* ---------- the fused MoE block ---------- */
+
+/* bf16 bit pattern of v rounded to nearest, ties to even (directly from fp64,
+ * one rounding), subnormals kept, overflow to infinity, NaN -> 0x7FC0. */
+static uint16_t orc_bf16_rne(double v) {
+    if (isnan(v)) return 0x7FC0;
+    if (v == 0.0) return signbit(v) ? 0x8000 : 0x0000;
+    int e;
+    frexp(fabs(v), &e); /* |v| = m * 2^e, m in [0.5, 1) */
+    /* 8 significant bits: spacing 2^(e - 8); below 2^-126 the subnormal spacing 2^-133 */
+    int shift = 8 - e;
+    if (shift > 133) shift = 133;
+    double r = ldexp(nearbyint(ldexp(v, shift)), -shift); /* default rounding mode: ties to even */
+    if (fabs(r) > 3.3895313892515355e38) return signbit(v) ? 0xFF80 : 0x7F80;
+    float f = (float)r; /* exact: r has at most 8 significant bits */
+    uint32_t b;
+    memcpy(&b, &f, 4);
+    return (uint16_t)(b >> 16);
+}
+
+void orc_round_bf16(const double* v, long long n, uint16_t* out) {
+    for (long long i = 0; i < n; ++i) out[i] = orc_bf16_rne(v[i]);
+}
+
+/* Mixture-of-experts block over T tokens with topk routed experts each
+ * ("A 320B MoE on a free Kaggle TPU", section "The decode kernel's cost is not
+ * distinct experts": x [T, D], idx [T, topk] int32 into E, w [T, topk] fp32 ->
+ * [T, D]; gate, up and down expert matrices; "I Built a Custom Blackwell
+ * Kernel for Qwen3.8-27B", section "What the custom path actually does":
+ * matrices sharing an input are joined, so gate and up form one parent).
+ * Reading: for pair p = t * topk + j with expert e = idx[p]
+ *   g_f = sum_k Wgu[e*2F + f, k] x[t, k],  u_f = sum_k Wgu[e*2F + F + f, k] x[t, k]
+ *   h_f = bf16( g_f / (1 + exp(-g_f)) * u_f )          (SwiGLU, rounded once)
+ *   y[t, d] = sum_j wts[t, j] * sum_f Wdn[e*D + d, f] * h_f
+ * with fp64 sums (f and k ascending, then j ascending) and
+ * bound[t, d] = sum_j |wts[t, j]| * sum_f |Wdn[e*D + d, f] * h_f|.
+ * Wgu is the stacked weight[E * 2F, D] of fmt_gu, Wdn the stacked weight[E * D, F]
+ * of fmt_dn.  A token with an id outside [0, E) gets NaN in y and bound.
+ * h_out (optional): the bf16 intermediate [T * topk, F] (0x7FC0 rows for invalid ids).
+ * Output columns d = cols[c] (cols == NULL: all D). */
+int orc_moe_block(int fmt_gu, const uint8_t* w_gu, int fmt_dn, const uint8_t* w_dn, long long E, long long D,
+                  long long F, long long T, long long topk, const uint16_t* x, const int32_t* idx, const float* wts,
+                  long long ncols, const long long* cols, double* y, double* bound, uint16_t* h_out, int nthreads) {
+    if (orc_block_values(fmt_gu) == 0 || orc_block_values(fmt_dn) == 0) return -1;
+    if (E < 1 || D <= 0 || F <= 0 || T < 0 || topk < 1) return -1;
+    if (D % orc_block_values(fmt_gu) || F % orc_block_values(fmt_dn)) return -1;
+    if (!cols) ncols = D;
+    for (long long c = 0; c < ncols; ++c)
+        if (cols && (cols[c] < 0 || cols[c] >= D)) return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    const long long P = T * topk;
+    uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(P > 0 ? P : 1) * (size_t)F);
+    if (!h) return -2;
+    /* 1. the bf16 intermediate of every (token, expert) pair */
+#pragma omp parallel
+    {
+        float* wg = (float*)malloc(sizeof(float) * (size_t)D);
+        float* wu = (float*)malloc(sizeof(float) * (size_t)D);
+#pragma omp for schedule(dynamic, 64)
+        for (long long pf = 0; pf < P * F; ++pf) {
+            const long long p = pf / F, f = pf % F, t = p / topk;
+            const long long e = idx[p];
+            if (e < 0 || e >= E) {
+                h[pf] = 0x7FC0;
+                continue;
+            }
+            orc_deq_row(fmt_gu, w_gu, E, 2 * F, D, e * 2 * F + f, wg);
+            orc_deq_row(fmt_gu, w_gu, E, 2 * F, D, e * 2 * F + F + f, wu);
+            const uint16_t* xt = x + t * D;
+            double g = 0.0, u = 0.0;
+            for (long long k = 0; k < D; ++k) {
+                const double xv = orc_bf16(xt[k]);
+                g += (double)wg[k] * xv;
+                u += (double)wu[k] * xv;
+            }
+            h[pf] = orc_bf16_rne(g / (1.0 + exp(-g)) * u);
+        }
+        free(wg);
+        free(wu);
+    }
+    /* 2. down projections and the routing-weighted combine */
+#pragma omp parallel
+    {
+        float* wd = (float*)malloc(sizeof(float) * (size_t)F);
+#pragma omp for schedule(dynamic, 4)
+        for (long long tc = 0; tc < T * ncols; ++tc) {
+            const long long t = tc / ncols, c = tc % ncols, d = cols ? cols[c] : c;
+            double s = 0.0, b = 0.0;
+            int bad = 0;
+            for (long long j = 0; j < topk; ++j) {
+                const long long p = t * topk + j, e = idx[p];
+                if (e < 0 || e >= E) {
+                    bad = 1;
+                    break;
+                }
+                orc_deq_row(fmt_dn, w_dn, E, D, F, e * D + d, wd);
+                double sj = 0.0, bj = 0.0;
+                for (long long f = 0; f < F; ++f) {
+                    const double pr = (double)wd[f] * orc_bf16(h[p * F + f]);
+                    sj += pr;
+                    bj += fabs(pr);
+                }
+                s += (double)wts[p] * sj;
+                b += fabs((double)wts[p]) * bj;
+            }
+            y[tc] = bad ? NAN : s;
+            bound[tc] = bad ? NAN : b;
+        }
+        free(wd);
+    }
+    if (h_out) memcpy(h_out, h, sizeof(uint16_t) * (size_t)P * (size_t)F);
+    free(h);
     return 0;
 }
 

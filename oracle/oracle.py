@@ -51,6 +51,10 @@ def load():
     lib.orc_dequant_rows.restype = i32
     lib.orc_gemm.argtypes = [i32, vp, ll, ll, ll, ll, vp, vp, ll, vp, vp, vp, i32]
     lib.orc_gemm.restype = i32
+    lib.orc_round_bf16.argtypes = [vp, ll, vp]
+    lib.orc_round_bf16.restype = None
+    lib.orc_moe_block.argtypes = [i32, vp, i32, vp, ll, ll, ll, ll, ll, vp, vp, vp, ll, vp, vp, vp, vp, i32]
+    lib.orc_moe_block.restype = i32
     lib.orc_max_threads.argtypes = []
     lib.orc_max_threads.restype = i32
     _lib = lib
@@ -131,3 +135,44 @@ def gemm(fmt: int, w, N: int, K: int, x, E: int = 1, ids=None, cols=None, nthrea
     if rc != 0:
         raise ValueError("orc_gemm rejected its arguments")
     return y, b
+
+
+def round_bf16(v) -> np.ndarray:
+    """bf16 bit patterns (uint16) of fp64 values, rounded once to nearest even."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    load().orc_round_bf16(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def moe_block(fmt_gu: int, w_gu, fmt_dn: int, w_dn, E: int, D: int, F: int, x, idx, wts, cols=None,
+              nthreads: int = 0, want_h: bool = False):
+    """(y, bound[, h]) of the mixture-of-experts block (oracle.c, orc_moe_block).
+
+    w_gu: packed weight[E * 2F, D] (rows e*2F .. e*2F+F-1 gate, the next F up);
+    w_dn: packed weight[E * D, F]; x: bf16 bits uint16 [T, D]; idx: int32 [T, topk];
+    wts: fp32 [T, topk].  y, bound: fp64 [T, ncols]; h: bf16 bits [T * topk, F].
+    """
+    w_gu, w_dn = _as_bytes(w_gu), _as_bytes(w_dn)
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    wts = np.ascontiguousarray(wts, dtype=np.float32)
+    T, topk = idx.shape
+    x = x.reshape(T, D)
+    assert wts.shape == (T, topk)
+    if w_gu.size < packed_bytes(fmt_gu, E, 2 * F, D) or w_dn.size < packed_bytes(fmt_dn, E, D, F):
+        raise ValueError("packed buffer too small")
+    if cols is not None:
+        cols = np.ascontiguousarray(cols, dtype=np.int64).reshape(-1)
+        ncols = cols.size
+    else:
+        ncols = D
+    y = np.empty((T, ncols), dtype=np.float64)
+    b = np.empty((T, ncols), dtype=np.float64)
+    h = np.empty((T * topk, F), dtype=np.uint16) if want_h else None
+    rc = load().orc_moe_block(fmt_gu, _ptr(w_gu), fmt_dn, _ptr(w_dn), E, D, F, T, topk, _ptr(x), _ptr(idx),
+                              _ptr(wts), ncols, _ptr(cols) if cols is not None else None, _ptr(y), _ptr(b),
+                              _ptr(h) if want_h else None, int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_moe_block rejected its arguments")
+    return (y, b, h) if want_h else (y, b)

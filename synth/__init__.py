@@ -125,3 +125,10 @@ def routing(g: np.random.Generator, tokens: int, k: int, E: int) -> np.ndarray:
     for t in range(tokens):
         ids[t] = g.choice(E, size=k, replace=False)
     return ids.reshape(-1)
+
+
+def routing_weights(g: np.random.Generator, tokens: int, k: int) -> np.ndarray:
+    """fp32 [tokens, k]: a softmax over k standard normals per token (positive, rows sum to ~1)."""
+    z = g.standard_normal((tokens, k))
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).astype(np.float32)

@@ -8,7 +8,12 @@ Each check is independent of the oracle's own code path:
     byte position), with number formats decoded by numpy / torch;
   * the product against numpy's fp64 matmul, brute-force exact sums, one-hot
     activations and integer closed forms;
-  * the routing generator against the closed form for expected distinct experts.
+  * the routing generator against the closed form for expected distinct experts;
+  * the MoE block's bf16 rounding against exact rational rounding and torch's
+    fp32 -> bf16 conversion, the whole block against a pure-Python brute force
+    on a tiny integer case, and its invariants (linearity in the routing
+    weights, merged duplicate experts, order of a token's experts, E = 1
+    reducing to two pinned products, invalid ids).
 """
 import math
 import os
@@ -507,3 +512,162 @@ def test_routing_distinct_experts_closed_form():
         sem = float(np.std(counts)) / math.sqrt(trials)
         assert abs(mean - expected(T)) < 4 * sem + 0.02, (T, mean, expected(T))
     assert abs(expected(16) - 104.50) < 0.01
+
+
+# ---------------------------------------------------------------- the MoE block
+
+def _rne_bf16_exact(fr):
+    """bf16 bits of an exact rational, rounded to nearest even (normal range only)."""
+    if fr == 0:
+        return 0
+    sign = 0x8000 if fr < 0 else 0
+    a = abs(fr)
+    e = 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    # a in [1, 2): 7 fraction bits
+    scaled = a * 128
+    q = int(scaled)
+    rem = scaled - q
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and q % 2 == 1):
+        q += 1
+    if q == 256:
+        q = 128
+        e += 1
+    return sign | ((e + 127) << 7) | (q - 128)
+
+
+def test_round_bf16_exact_rational_and_torch():
+    g = np.random.default_rng(11)
+    # fp64 values that are not fp32 values: one rounding from fp64, checked exactly
+    v = g.standard_normal(4000) * np.exp2(g.integers(-20, 20, 4000))
+    v = np.concatenate([v, [1 + 2.0**-8 + 2.0**-40, 1 + 2.0**-8, 1 + 3 * 2.0**-8, -(1 + 2.0**-8 + 2.0**-40),
+                            255.5, 256.5, 0.1, -0.1]])
+    got = oracle.round_bf16(v)
+    exp = np.array([_rne_bf16_exact(Fraction(float(t))) for t in v], np.uint16)
+    assert np.array_equal(got, exp)
+    assert got[-8] == 0x3F81 and got[-7] == 0x3F80 and got[-6] == 0x3F82  # above a tie; ties to even
+    # fp32 values (exact in fp64): torch's fp32 -> bf16 conversion, specials included
+    f = (g.standard_normal(20000) * np.exp2(g.integers(-140, 127, 20000))).astype(np.float32)
+    ties = ((g.integers(0, 1 << 15, 2000).astype(np.uint32) << 16) | 0x8000).astype(np.uint32).view(np.float32)
+    f = np.concatenate([f, ties[np.isfinite(ties)], np.float32([0.0, -0.0, np.inf, -np.inf, 3.4e38, -3.39e38,
+                                                               1e-40, -1e-45, 1.17e-38])])
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.round_bf16(f.astype(np.float64)), ref)
+    assert oracle.round_bf16(np.array([np.nan]))[0] == 0x7FC0
+
+
+def test_moe_block_brute_force_tiny():
+    """Q8_0 experts with d = 1 and small integer codes, small integer activations:
+    the block computed by hand (Python integers, exact rational rounding)."""
+    E, D, F, T, topk = 3, 64, 32, 2, 2
+    g = np.random.default_rng(12)
+    one = f16_bits(1.0)
+    qgu = g.integers(-3, 4, (E * 2 * F, D))
+    qdn = g.integers(-3, 4, (E * D, F))
+    w_gu = as_u8(b"".join(enc_q8_0(one, [int(v) for v in row[b * 32:(b + 1) * 32]])
+                          for row in qgu for b in range(D // 32)))
+    w_dn = as_u8(b"".join(enc_q8_0(one, [int(v) for v in row[b * 32:(b + 1) * 32]])
+                          for row in qdn for b in range(F // 32)))
+    xi = g.integers(-2, 3, (T, D))
+    x = np.array([[f16_to_bf16_bits(float(v)) for v in r] for r in xi], np.uint16)
+    idx = np.array([[2, 0], [1, 1]], np.int32)
+    wts = np.array([[0.75, 0.25], [0.5, -1.5]], np.float32)
+    y, b, h = oracle.moe_block(oracle.Q8_0, w_gu, oracle.Q8_0, w_dn, E, D, F, x, idx, wts, want_h=True)
+    for t in range(T):
+        acc = Fraction(0)
+        hs = []
+        for j in range(topk):
+            e = int(idx[t, j])
+            gv = [int(sum(int(qgu[e * 2 * F + f, k]) * int(xi[t, k]) for k in range(D))) for f in range(F)]
+            uv = [int(sum(int(qgu[e * 2 * F + F + f, k]) * int(xi[t, k]) for k in range(D))) for f in range(F)]
+            vs = [gg / (1.0 + math.exp(-gg)) * uu for gg, uu in zip(gv, uv)]
+            # (IEEE sign of zero: a negative silu times u = 0 is -0)
+            hb = [(0x8000 if math.copysign(1.0, v) < 0 else 0) if v == 0 else _rne_bf16_exact(Fraction(v))
+                  for v in vs]
+            assert list(h[t * topk + j]) == hb
+            hs.append(hb)
+        for d in range(D):
+            s = Fraction(0)
+            for j in range(topk):
+                e = int(idx[t, j])
+                hv = [Fraction(float(np.uint32(v << 16).view(np.float32))) for v in hs[j]]
+                s += Fraction(float(wts[t, j])) * sum(int(qdn[e * D + d, f]) * hv[f] for f in range(F))
+            assert abs(Fraction(y[t, d]) - s) <= Fraction(1, 2**40) * (abs(s) + 1), (t, d)
+    assert np.all(np.abs(y) <= b)
+
+
+def f16_to_bf16_bits(v):
+    return int(np.float32(v).view(np.uint32) >> 16)
+
+
+def _moe_case(fmt_gu, fmt_dn, E, D, F, T, topk, seed):
+    w_gu = synth.weights(fmt_gu, synth.rng(seed, 0), E * 2 * F, D, E=E)
+    w_dn = synth.weights(fmt_dn, synth.rng(seed, 1), E * D, F, E=E)
+    x = synth.x_bf16(synth.rng(seed, 2), T, D)
+    idx = synth.routing(synth.rng(seed, 3), T, topk, E).reshape(T, topk)
+    wts = synth.routing_weights(synth.rng(seed, 4), T, topk)
+    return w_gu, w_dn, x, idx, wts
+
+
+def test_moe_block_invariants():
+    fg, fd, E, D, F, T, topk = oracle.Q4_K, oracle.Q6_K, 5, 256, 512, 4, 3
+    w_gu, w_dn, x, idx, wts = _moe_case(fg, fd, E, D, F, T, topk, 13)
+    y, b, h = oracle.moe_block(fg, w_gu, fd, w_dn, E, D, F, x, idx, wts, want_h=True)
+    # linear in the routing weights (doubling is exact in fp64)
+    y2, b2 = oracle.moe_block(fg, w_gu, fd, w_dn, E, D, F, x, idx, 2 * wts)
+    assert np.array_equal(y2, 2 * y) and np.array_equal(b2, 2 * b)
+    # the order of a token's experts does not matter (up to fp64 rounding)
+    yr, _ = oracle.moe_block(fg, w_gu, fd, w_dn, E, D, F, x, idx[:, ::-1], wts[:, ::-1])
+    assert np.all(np.abs(yr - y) <= 1e-12 * b)
+    # a duplicated expert equals one expert with the summed weight
+    idx_d = np.stack([idx[:, 0], idx[:, 0]], 1)
+    wts_d = (np.round(wts[:, :2] * 64) / 64).astype(np.float32)  # multiples of 1/64: sums are exact
+    yd, bd = oracle.moe_block(fg, w_gu, fd, w_dn, E, D, F, x, idx_d, wts_d)
+    ys, _ = oracle.moe_block(fg, w_gu, fd, w_dn, E, D, F, x, idx[:, :1], wts_d.sum(axis=1, keepdims=True))
+    assert np.all(np.abs(yd - ys) <= 1e-12 * bd)
+    # each pair's intermediate and down product are the two pinned products
+    for t in range(T):
+        for j in range(topk):
+            e = int(idx[t, j])
+            gu, _ = oracle.gemm(fg, w_gu, 2 * F, D, x[t:t + 1], E=E, ids=np.array([e], np.int32))
+            gg, uu = gu[0, :F], gu[0, F:]
+            with np.errstate(over="ignore"):
+                v = gg / (1.0 + np.exp(-gg)) * uu
+            hb = oracle.round_bf16(v)
+            # numpy's exp may differ from libm's in the last bit: allow a different
+            # rounding only where v sits within 1e-12 of a bf16 midpoint
+            mid = np.abs(v) * 2.0**-8
+            near = np.abs(np.abs(v) / mid - np.round(np.abs(v) / mid)) < 1e-9
+            diff = hb != h[t * topk + j]
+            assert not np.any(diff & ~near)
+    hx = h[: topk].copy()  # token 0's intermediates as activations of the down product
+    for j in range(topk):
+        e = int(idx[0, j])
+        yd_j, bd_j = oracle.gemm(fd, w_dn, D, F, hx[j:j + 1], E=E, ids=np.array([e], np.int32))
+        if j == 0:
+            acc = wts[0, j].astype(np.float64) * yd_j[0]
+            accb = abs(wts[0, j].astype(np.float64)) * bd_j[0]
+        else:
+            acc = acc + wts[0, j].astype(np.float64) * yd_j[0]
+            accb = accb + abs(wts[0, j].astype(np.float64)) * bd_j[0]
+    assert np.all(np.abs(acc - y[0]) <= 1e-12 * b[0]) and np.allclose(accb, b[0], rtol=1e-12, atol=0)
+    # an id outside [0, E) makes that token's row NaN, and only that row
+    idx_bad = idx.copy()
+    idx_bad[2, 1] = E
+    yb, bb = oracle.moe_block(fg, w_gu, fd, w_dn, E, D, F, x, idx_bad, wts)
+    assert np.isnan(yb[2]).all() and np.isnan(bb[2]).all()
+    assert np.array_equal(np.delete(yb, 2, 0), np.delete(y, 2, 0))
+    # selected columns equal the full result
+    yc, bc = oracle.moe_block(fg, w_gu, fd, w_dn, E, D, F, x, idx, wts, cols=[255, 0, 17])
+    assert np.array_equal(yc, y[:, [255, 0, 17]]) and np.array_equal(bc, b[:, [255, 0, 17]])
+
+
+def test_routing_weights_generator():
+    w = synth.routing_weights(synth.rng(3, 4), 16, 8)
+    assert w.shape == (16, 8) and w.dtype == np.float32
+    assert np.all(w > 0) and np.allclose(w.sum(axis=1), 1.0, atol=1e-6)
