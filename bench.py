@@ -44,9 +44,10 @@ def log(*a):
 
 
 class Workload:
-    def __init__(self, name, fmt, N, K, M, seed, E=1, moe=None):
+    def __init__(self, name, fmt, N, K, M, seed, E=1, moe=None, block=None):
         self.name, self.fmt, self.N, self.K, self.M, self.seed, self.E = name, fmt, N, K, M, seed, E
         self.moe = moe  # (tokens, topk) for the grouped workload
+        self.block = block  # (down format, F, tokens, topk) for the MoE block: N = 2F, K = D
 
 
 def workloads():
@@ -75,6 +76,8 @@ def workloads():
                              moe=(16, 8)),
         "moe_down": Workload("Q4_K grouped experts down, E=288 N=4096 K=2048", qg.Q4_K, 4096, 2048, 128, 5, E=288,
                              moe=(16, 8)),
+        "moe_block": Workload("Q4_K MoE block (gate|up, SwiGLU, down, combine), E=288 D=4096 F=2048, 16 tokens x "
+                              "top-8", qg.Q4_K, 2 * 2048, 4096, 128, 5, E=288, block=(qg.Q4_K, 2048, 16, 8)),
     }
 
 
@@ -87,6 +90,9 @@ class Prepared:
         import gemm_block_quant_amd as qg
         import synth
         self.wl = wl
+        if wl.block is not None:
+            self._prepare_block(wl)
+            return
         tid_w = 0 if wl.moe is None or wl.K == 4096 else 4
         t0 = time.time()
         self.w_host = synth.weights(wl.fmt, synth.rng(wl.seed, tid_w), wl.E * wl.N, wl.K, E=wl.E)
@@ -126,6 +132,47 @@ class Prepared:
         else:
             fn = L.quant_gemm
             self.calls = [lambda s, wp=wp: fn(wp, fmt, N, K, M, xp, yp, s) for wp in wps]
+
+    def _prepare_block(self, wl: Workload):
+        """The MoE block: gate|up weight[E*2F, D], down weight[E*D, F].  Only the
+        first 32 experts are drawn; experts e >= 32 repeat expert e % 32's bytes
+        (same shapes and value distribution, distinct addresses), which keeps
+        generation of the 4 GB layer to a fraction of a minute."""
+        import torch
+
+        import gemm_block_quant_amd as qg
+        import synth
+        fmt_dn, F, T, topk = wl.block
+        D, E, base = wl.K, wl.E, min(wl.E, 32)
+        assert wl.fmt != qg.NVFP4 and fmt_dn != qg.NVFP4, "the tiled generator needs self-contained blocks"
+        t0 = time.time()
+        reps = -(-E // base)
+        gu = synth.weights(wl.fmt, synth.rng(wl.seed, 10), base * 2 * F, D)
+        dn = synth.weights(fmt_dn, synth.rng(wl.seed, 11), base * D, F)
+        self.w_gu = torch.from_numpy(gu).cuda().repeat(reps)[:qg.quant_packed_bytes(wl.fmt, E, 2 * F, D)].contiguous()
+        self.w_dn = torch.from_numpy(dn).cuda().repeat(reps)[:qg.quant_packed_bytes(fmt_dn, E, D, F)].contiguous()
+        self.x_host = synth.x_bf16(synth.rng(wl.seed, 12), T, D)
+        self.idx_host = synth.routing(synth.rng(wl.seed, 13), T, topk, E).reshape(T, topk)
+        self.wts_host = synth.routing_weights(synth.rng(wl.seed, 14), T, topk)
+        self.distinct = len(np.unique(self.idx_host))
+        self.bytes_per_call = self.distinct * (qg.quant_packed_bytes(wl.fmt, 1, 2 * F, D) +
+                                               qg.quant_packed_bytes(fmt_dn, 1, D, F))
+        self.wbytes_total = self.w_gu.numel() + self.w_dn.numel()
+        log("[bench] %s: generated and placed %.1f MB in %.1f s" % (wl.name, self.wbytes_total / 1e6,
+                                                                      time.time() - t0))
+        self.copies = 1
+        self.x = torch.from_numpy(self.x_host.view(np.int16)).cuda()
+        self.idx = torch.from_numpy(self.idx_host).cuda()
+        self.wts = torch.from_numpy(self.wts_host).cuda()
+        self.y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+        wsb = qg.quant_moe_workspace_bytes(wl.fmt, fmt_dn, E, D, F, T, topk)
+        self.ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        L = qg.lib()
+        vp = lambda t: ctypes.c_void_p(t.data_ptr())
+        args = (vp(self.w_gu), wl.fmt, vp(self.w_dn), fmt_dn, E, D, F, T, topk, vp(self.x), vp(self.idx),
+                vp(self.wts), vp(self.y), vp(self.ws), wsb)
+        self.calls = [lambda s: L.quant_moe_block(*args, s)]
 
     def call(self, i, stream=None):
         st = self.calls[i % len(self.calls)](self.stream if stream is None else stream)
@@ -343,9 +390,9 @@ def result_for(p: Prepared, steps: int, warmup: int):
          "weight_GBps": round(gbs, 1), "kernel_weight_GBps": round(kern_gbs, 1),
          "pct_hbm_peak": round(100 * kern_gbs / HBM_PEAK_GBS, 2),
          "implied_tok_s": round(wl.M * gbs / TOKEN_BYTES_GB, 1)}
-    if wl.moe:
+    if wl.moe or wl.block:
         r["distinct_experts"] = p.distinct
-    if wl.M >= 32:
+    if wl.M >= 32 and not wl.block:
         flops = 2.0 * wl.M * wl.N * wl.K
         r["TFLOPs"] = round(flops / per_mean / 1e12, 1)
         r["pct_bf16_mfma_peak"] = round(100 * flops / per_mean / 1e12 / BF16_MFMA_PEAK_TFLOPS, 2)
@@ -417,7 +464,7 @@ def main():
     if args.calibrate_copy:
         copy_calibration()
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and not wl.block:
         cpu = cpu_baseline(p)
         log("[bench] cpu baseline %s" % json.dumps(cpu))
     value = p.bytes_per_call * args.steps / total / 1e9

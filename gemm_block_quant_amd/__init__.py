@@ -64,6 +64,10 @@ def lib():
     L.quant_dequantize_stacked.restype = i32
     L.quant_status_string.argtypes = [i32]
     L.quant_status_string.restype = ctypes.c_char_p
+    L.quant_moe_workspace_bytes.argtypes = [i32, i32, i64, i64, i64, i64, i64]
+    L.quant_moe_workspace_bytes.restype = sz
+    L.quant_moe_block.argtypes = [vp, i32, vp, i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+    L.quant_moe_block.restype = i32
     L.quant_read_probe.argtypes = [vp, sz, vp, vp]
     L.quant_read_probe.restype = i32
     _lib = L
@@ -172,6 +176,37 @@ def quant_grouped_gemm(w, fmt: int, E: int, N: int, K: int, M: int, x, ids=None,
                                   _dev_ptr(y, "y", 4 * M * N), _dev_ptr(workspace, "workspace"),
                                   workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "quant_grouped_gemm")
+    return y
+
+
+def quant_moe_workspace_bytes(fmt_gate_up: int, fmt_down: int, E: int, D: int, F: int, T: int, topk: int) -> int:
+    return int(lib().quant_moe_workspace_bytes(fmt_gate_up, fmt_down, E, D, F, T, topk))
+
+
+def quant_moe_block(w_gate_up, fmt_gate_up: int, w_down, fmt_down: int, E: int, D: int, F: int, x, idx, wts,
+                    y=None, workspace=None, stream=None):
+    """y[t] = sum_j wts[t, j] * down_e(bf16(silu(gate_e x[t]) * up_e x[t])), e = idx[t, j].
+
+    w_gate_up: packed weight[E*2F, D] (gate rows then up rows per expert); w_down:
+    packed weight[E*D, F]; x: bf16 [T, D]; idx: int32 [T, topk]; wts: fp32 [T, topk].
+    """
+    torch = _torch()
+    T, topk = idx.shape
+    if idx.dtype != torch.int32 or wts.dtype != torch.float32:
+        raise ValueError("idx must be int32 and wts float32")
+    if tuple(wts.shape) != (T, topk):
+        raise ValueError("wts must have the shape of idx")
+    y = _out(y, (T, D), x.device)
+    wsb = quant_moe_workspace_bytes(fmt_gate_up, fmt_down, E, D, F, T, topk)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=x.device)
+    st = lib().quant_moe_block(_dev_ptr(w_gate_up, "w_gate_up", quant_packed_bytes(fmt_gate_up, E, 2 * F, D)),
+                               fmt_gate_up, _dev_ptr(w_down, "w_down", quant_packed_bytes(fmt_down, E, D, F)),
+                               fmt_down, E, D, F, T, topk, _x_ptr(x, T, D), _dev_ptr(idx, "idx", 4 * T * topk),
+                               _dev_ptr(wts, "wts", 4 * T * topk), _dev_ptr(y, "y", 4 * T * D),
+                               _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                               _stream(stream))
+    _check(st, "quant_moe_block")
     return y
 
 

@@ -65,6 +65,39 @@ StreamArgs stream_args(const void* w, int fmt, int64_t E, int64_t e, int64_t N, 
 
 qg_status from_hip(hipError_t e) { return e == hipSuccess ? QG_OK : QG_EHIP; }
 
+// Workspace regions of the mixture-of-experts block (256-byte aligned offsets).
+struct MoeLayout {
+    size_t xp, gu, h, yd, gws, total;
+};
+MoeLayout moe_layout(int64_t E, int64_t P, int64_t D, int64_t F) {
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    MoeLayout L;
+    size_t o = 0;
+    L.xp = o;
+    o += up((size_t)P * (size_t)D * 2);  // bf16 activation row per pair
+    L.gu = o;
+    o += up((size_t)P * (size_t)F * 8);  // fp32 gate|up per pair
+    L.h = o;
+    o += up((size_t)P * (size_t)F * 2);  // bf16 SwiGLU per pair
+    L.yd = o;
+    o += up((size_t)P * (size_t)D * 4);  // fp32 down product per pair
+    L.gws = o;
+    o += up(grouped_workspace_bytes(E, P));
+    L.total = o;
+    return L;
+}
+
+// Shape checks of the block; P = T * topk pairs.
+qg_status check_moe(int fmt_gu, int fmt_dn, int64_t E, int64_t D, int64_t F, int64_t T, int64_t topk) {
+    if (block_values(fmt_gu) == 0 || block_values(fmt_dn) == 0) return QG_EFORMAT;
+    if (E < 1 || D <= 0 || F <= 0 || T < 0 || topk < 1 || topk > kGroupedMaxRows) return QG_ESHAPE;
+    if (T > kGroupedMaxRows / topk) return QG_ESHAPE;
+    if (F > INT_MAX / 4) return QG_ESHAPE;
+    qg_status s = check_shape(fmt_gu, E, 2 * F, D, T * topk);
+    if (s != QG_OK) return s;
+    return check_shape(fmt_dn, E, D, F, T * topk);
+}
+
 }  // namespace
 
 namespace qg {
@@ -222,6 +255,56 @@ qg_status quant_grouped_gemm(const void* w, qg_format fmt, int64_t E, int64_t N,
     a.ldy = N;
     const int64_t es0 = N * a.rb0, es1 = N * a.rb1;
     return from_hip(launch_grouped(fmt, a, ids, E, M, (int32_t*)workspace, es0, es1, (hipStream_t)stream));
+}
+
+size_t quant_moe_workspace_bytes(qg_format fmt_gate_up, qg_format fmt_down, int64_t E, int64_t D, int64_t F,
+                                 int64_t T, int64_t topk) {
+    if (check_moe(fmt_gate_up, fmt_down, E, D, F, T, topk) != QG_OK) return 0;
+    return moe_layout(E, T * topk, D, F).total;
+}
+
+qg_status quant_moe_block(const void* w_gate_up, qg_format fmt_gate_up, const void* w_down, qg_format fmt_down,
+                          int64_t E, int64_t D, int64_t F, int64_t T, int64_t topk, const uint16_t* x,
+                          const int32_t* idx, const float* wts, float* y, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    qg_status s = check_moe(fmt_gate_up, fmt_down, E, D, F, T, topk);
+    if (s != QG_OK) return s;
+    if (T == 0) return QG_OK;
+    if (!w_gate_up || !w_down || !x || !idx || !wts || !y) return QG_EINVAL;
+    const int64_t P = T * topk;
+    const MoeLayout L = moe_layout(E, P, D, F);
+    if (!workspace || workspace_bytes < L.total) return QG_EWORKSPACE;
+    if (!aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(x, 16) || !aligned(idx, 4) ||
+        !aligned(wts, 4) || !aligned(y, 4) || !aligned(workspace, 16))
+        return QG_EALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+    uint16_t* xp = (uint16_t*)(ws + L.xp);
+    float* gu = (float*)(ws + L.gu);
+    uint16_t* h = (uint16_t*)(ws + L.h);
+    float* yd = (float*)(ws + L.yd);
+    int32_t* gws = (int32_t*)(ws + L.gws);
+    // 1. one activation row per (token, expert) pair
+    if (launch_moe_gather(x, xp, (int)P, (int)topk, (int)D, st) != hipSuccess) return QG_EHIP;
+    // 2. gate|up of every pair, each distinct expert's weights read once
+    StreamArgs a = stream_args(w_gate_up, fmt_gate_up, E, 0, 2 * F, D);
+    a.x = xp;
+    a.ldx = D;
+    a.y = gu;
+    a.ldy = 2 * F;
+    if (launch_grouped(fmt_gate_up, a, idx, E, P, gws, 2 * F * a.rb0, 2 * F * a.rb1, st) != hipSuccess)
+        return QG_EHIP;
+    // 3. SwiGLU, rounded to bf16
+    if (launch_moe_swiglu(gu, h, (int)P, (int)F, st) != hipSuccess) return QG_EHIP;
+    // 4. down products
+    StreamArgs b = stream_args(w_down, fmt_down, E, 0, D, F);
+    b.x = h;
+    b.ldx = F;
+    b.y = yd;
+    b.ldy = D;
+    if (launch_grouped(fmt_down, b, idx, E, P, gws, D * b.rb0, D * b.rb1, st) != hipSuccess) return QG_EHIP;
+    // 5. routing-weighted sum over each token's experts
+    return from_hip(launch_moe_combine(yd, wts, y, (int)T, (int)topk, (int)D, st));
 }
 
 qg_status quant_dequantize_stacked(const void* w, qg_format fmt, int64_t E, int64_t N, int64_t K, float* out,

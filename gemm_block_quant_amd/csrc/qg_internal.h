@@ -51,6 +51,11 @@ hipError_t launch_mfma_kquant(int fmt, const uint8_t* w, int N, int K, const uin
                               float* y, int64_t ldy, hipStream_t st);
 int num_cus();
 
+// Element-wise steps of the mixture-of-experts block (qg_moe.hip).
+hipError_t launch_moe_gather(const uint16_t* x, uint16_t* xp, int P, int topk, int D, hipStream_t st);
+hipError_t launch_moe_swiglu(const float* gu, uint16_t* h, int P, int F, hipStream_t st);
+hipError_t launch_moe_combine(const float* yd, const float* wts, float* y, int T, int topk, int D, hipStream_t st);
+
 // Dequantization of rows [0, rows) to fp32.
 hipError_t launch_dequant(int fmt, const uint8_t* w, int64_t E, int64_t N, int64_t K, float* out, hipStream_t st);
 

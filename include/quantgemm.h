@@ -19,7 +19,7 @@
  * falsification"): E stacked matrices, E = 1 being the dense case.
  *
  * Conventions shared by every entry point:
- *  - Pointers named w, x, y, ids, out and workspace are DEVICE pointers owned by
+ *  - Pointers named w*, x, y, ids, idx, wts, out and workspace are DEVICE pointers owned by
  *    the caller; the library allocates nothing, keeps no per-call state and
  *    never synchronizes.  `stream` is a hipStream_t (NULL = the null stream);
  *    work is enqueued on it and the call returns immediately.
@@ -140,6 +140,39 @@ size_t quant_grouped_workspace_bytes(int64_t E, int64_t M);
 qg_status quant_grouped_gemm(const void* w, qg_format fmt, int64_t E, int64_t N, int64_t K, int64_t M,
                              const uint16_t* x, const int32_t* ids, float* y, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace quant_moe_block needs (0 when the arguments would be
+ * rejected by quant_moe_block's shape checks).  Host only. */
+size_t quant_moe_workspace_bytes(qg_format fmt_gate_up, qg_format fmt_down, int64_t E, int64_t D, int64_t F,
+                                 int64_t T, int64_t topk);
+
+/* Mixture-of-experts block over T tokens, each routed to topk experts:
+ *     y[t, :] = sum_j wts[t, j] * W_down_e . h_{t,j},   e = idx[t, j],
+ *     h_{t,j} = bf16( silu(g) * u ),  g = W_gate_e . x[t, :],  u = W_up_e . x[t, :],
+ *     silu(g) = g / (1 + exp(-g)),
+ * the dispatch interface x [T, D], idx [T, topk] int32, wts [T, topk] fp32 ->
+ * [T, D] of "A 320B MoE on a free Kaggle TPU" (section "The decode kernel's
+ * cost is not distinct experts"), with gate and up joined into one parent
+ * because they share the input ("I Built a Custom Blackwell Kernel for
+ * Qwen3.8-27B", section "What the custom path actually does").
+ * w_gate_up: packed weight[E * 2F, D] of fmt_gate_up; rows [e*2F, e*2F + F) of
+ *   expert e are its gate, rows [e*2F + F, (e+1)*2F) its up (NVFP4: E tensor
+ *   scales, one per expert's 2F rows).
+ * w_down: packed weight[E * D, F] of fmt_down.
+ * x: bf16 [T, D]; idx: int32 [T, topk]; wts: fp32 [T, topk]; y: fp32 [T, D]
+ * (overwritten).  The intermediate h is rounded once to bf16 (round to
+ * nearest even) from fp32; the sum over j runs in ascending order in fp32.
+ * Each distinct expert's weights are read once per product.
+ * A token with an id outside [0, E) gets NaN in every element of its row.
+ * workspace: device scratch of at least quant_moe_workspace_bytes(...) bytes,
+ * contents undefined between calls; calls sharing it must be ordered on one
+ * stream.  Limits: T * topk <= 16384; D and F multiples of the formats'
+ * blocks (QG_ESHAPE otherwise).  T == 0 is a valid no-op.
+ * Alignment: w_gate_up, w_down, x, workspace 16 bytes; idx, wts, y 4 bytes. */
+qg_status quant_moe_block(const void* w_gate_up, qg_format fmt_gate_up, const void* w_down, qg_format fmt_down,
+                          int64_t E, int64_t D, int64_t F, int64_t T, int64_t topk, const uint16_t* x,
+                          const int32_t* idx, const float* wts, float* y, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Dequantize rows [0, rows) of a packed weight[rows, K] to fp32 out[rows, K]
  * (bit-exact; a test and debugging aid, the products never call it).

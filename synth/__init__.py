@@ -36,7 +36,13 @@ def rng(config_seed: int, tensor_id: int) -> np.random.Generator:
 
 
 def _random_bytes(g: np.random.Generator, n: int) -> np.ndarray:
-    return np.frombuffer(g.bytes(int(n)), dtype=np.uint8).copy()
+    """n uniform bytes: the stream of g.bytes(n) (ceil(n / 4) uniform uint32,
+    little endian), drawn through integers(), which is several times faster."""
+    n = int(n)
+    if n == 0:
+        return np.empty(0, dtype=np.uint8)
+    w = g.integers(0, 1 << 32, size=(n - 1) // 4 + 1, dtype=np.uint32).astype("<u4", copy=False)
+    return w.view(np.uint8)[:n].copy()
 
 
 def _fp16_bytes(v: np.ndarray) -> np.ndarray:

@@ -114,3 +114,39 @@ def test_grouped_validation():
     assert grouped(*args(ids=ctypes.c_void_p(0x500002))) == qg.QG_EALIGN
     assert grouped(*args(M=0, ws=None, wsb=0)) == qg.QG_OK
     assert grouped(*args(M=20000)) == qg.QG_ESHAPE
+
+
+def test_moe_block_validation():
+    moe = _raw("quant_moe_block")
+    fg, fd, E, D, F, T, topk = qg.Q4_K, qg.Q6_K, 6, 512, 768, 5, 3
+    wsb = qg.quant_moe_workspace_bytes(fg, fd, E, D, F, T, topk)
+    # gate|up activations, gate|up fp32, bf16 intermediate, down fp32, grouped workspace
+    P = T * topk
+    assert wsb >= P * D * 2 + P * 2 * F * 4 + P * F * 2 + P * D * 4 + qg.quant_grouped_workspace_bytes(E, P)
+    assert qg.quant_moe_workspace_bytes(fg, fd, E, D + 16, F, T, topk) == 0  # D not a multiple of 256
+    assert qg.quant_moe_workspace_bytes(fg, 9, E, D, F, T, topk) == 0
+    ws = ctypes.c_void_p(0x400000)
+    idx = ctypes.c_void_p(0x500000)
+    wts = ctypes.c_void_p(0x600000)
+    wd = ctypes.c_void_p(0x700000)
+
+    def args(**kw):
+        return [kw.get("wgu", FAKE_W), kw.get("fg", fg), kw.get("wd", wd), kw.get("fd", fd), kw.get("E", E),
+                kw.get("D", D), kw.get("F", F), kw.get("T", T), kw.get("topk", topk), kw.get("x", FAKE_X),
+                kw.get("idx", idx), kw.get("wts", wts), FAKE_Y, kw.get("ws", ws), kw.get("wsb", wsb), None]
+
+    assert moe(*args(fg=0)) == qg.QG_EFORMAT
+    assert moe(*args(fd=6)) == qg.QG_EFORMAT
+    assert moe(*args(E=0)) == qg.QG_ESHAPE
+    assert moe(*args(topk=0)) == qg.QG_ESHAPE
+    assert moe(*args(D=D + 16)) == qg.QG_ESHAPE      # not a multiple of the gate|up block
+    assert moe(*args(F=F + 32)) == qg.QG_ESHAPE      # not a multiple of the down block
+    assert moe(*args(T=4097, topk=4)) == qg.QG_ESHAPE  # more than 16384 pairs
+    assert moe(*args(wd=None)) == qg.QG_EINVAL
+    assert moe(*args(wts=None)) == qg.QG_EINVAL
+    assert moe(*args(ws=None)) == qg.QG_EWORKSPACE
+    assert moe(*args(wsb=wsb - 1)) == qg.QG_EWORKSPACE
+    assert moe(*args(idx=ctypes.c_void_p(0x500002))) == qg.QG_EALIGN
+    assert moe(*args(wts=ctypes.c_void_p(0x600001))) == qg.QG_EALIGN
+    assert moe(*args(x=ctypes.c_void_p(0x200008))) == qg.QG_EALIGN
+    assert moe(*args(T=0, ws=None, wsb=0)) == qg.QG_OK
