@@ -27,6 +27,9 @@
  *  - NVFP4: E2M1 values with block scales and a per-site weight divisor/scale
  *    -- "I Built a Custom Blackwell Kernel for Qwen3.8-27B", section "What the
  *    custom path actually does".
+ *  - Row-scaled FP8 (attention and GDN projections, the output head and the
+ *    last eight MLPs of that model) -- same page and section; read as E4M3
+ *    codes with one fp32 scale per row.
  *
  * The pages fix the byte sizes but not the bit layout inside a block.  The
  * reading taken here is the GGUF convention (the pages gate the K-quants
@@ -51,7 +54,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_Q8_0 = 1, ORC_Q4_K = 2, ORC_Q6_K = 3, ORC_NVFP4 = 4, ORC_Q5_K = 5 };
+enum { ORC_Q8_0 = 1, ORC_Q4_K = 2, ORC_Q6_K = 3, ORC_NVFP4 = 4, ORC_Q5_K = 5, ORC_FP8 = 6 };
 
 /* ---------- scalar decoders written from the number-format definitions ---------- */
 
@@ -103,6 +106,7 @@ long long orc_block_values(int fmt) {
     case ORC_Q6_K: return 256;
     case ORC_NVFP4: return 16;
     case ORC_Q5_K: return 256;
+    case ORC_FP8: return 64; /* no blocks: K must be a multiple of 64 */
     default: return 0;
     }
 }
@@ -111,7 +115,8 @@ long long orc_block_values(int fmt) {
  * 128 nibble bytes = 144 B.  Q5_K: as Q4_K plus 32 bytes of fifth bits =
  * 176 B.  Q6_K: 128 low-nibble bytes + 64 high-bit bytes + 16 int8
  * sub-scales + fp16 d = 210 B.  NVFP4: 8 code bytes + 1 E4M3 scale byte per
- * 16 values (the 4-byte fp32 tensor scale is counted per tensor). */
+ * 16 values (the 4-byte fp32 tensor scale is counted per tensor).  FP8: one
+ * byte per value (the 4-byte fp32 row scale is counted per row). */
 long long orc_block_bytes(int fmt) {
     switch (fmt) {
     case ORC_Q8_0: return 34;
@@ -119,6 +124,7 @@ long long orc_block_bytes(int fmt) {
     case ORC_Q6_K: return 210;
     case ORC_NVFP4: return 9;
     case ORC_Q5_K: return 176;
+    case ORC_FP8: return 64;
     default: return 0;
     }
 }
@@ -129,6 +135,7 @@ long long orc_packed_bytes(int fmt, long long E, long long N, long long K) {
     if (qk == 0 || E < 0 || N < 0 || K < 0 || K % qk) return 0;
     long long rows = E * N, blocks = rows * (K / qk);
     if (fmt == ORC_NVFP4) return blocks * 9 + 4 * E;
+    if (fmt == ORC_FP8) return rows * K + 4 * rows;
     return blocks * orc_block_bytes(fmt);
 }
 
@@ -260,12 +267,31 @@ static void orc_deq_nvfp4_row(const uint8_t* w, long long E, long long N, long l
     }
 }
 
+/* Row-scaled FP8 tensor of R = E*N rows: two planes,
+ *   codes  [R][K] : one E4M3 (fn) byte per value
+ *   scales [R]    : one fp32 scale per row (little endian)
+ * w = e4m3(c) * s, rounded once to fp32 (the product is exact in fp64). */
+static void orc_deq_fp8_row(const uint8_t* w, long long E, long long N, long long K, long long r, float* out) {
+    const long long R = E * N;
+    const uint8_t* codes = w + r * K;
+    const uint8_t* sb = w + R * K + 4 * r;
+    uint32_t bits = (uint32_t)sb[0] | ((uint32_t)sb[1] << 8) | ((uint32_t)sb[2] << 16) | ((uint32_t)sb[3] << 24);
+    float sf;
+    memcpy(&sf, &bits, 4);
+    const double sc = sf;
+    for (long long k = 0; k < K; ++k) out[k] = (float)(orc_e4m3(codes[k]) * sc);
+}
+
 /* Dequantize global row r (0 <= r < E*N) of a packed weight[E*N, K] into out[K]. */
 static void orc_deq_row(int fmt, const uint8_t* w, long long E, long long N, long long K, long long r, float* out) {
     long long qk = orc_block_values(fmt), bb = orc_block_bytes(fmt);
     long long nb = K / qk;
     if (fmt == ORC_NVFP4) {
         orc_deq_nvfp4_row(w, E, N, K, r, out);
+        return;
+    }
+    if (fmt == ORC_FP8) {
+        orc_deq_fp8_row(w, E, N, K, r, out);
         return;
     }
     const uint8_t* row = w + r * nb * bb;

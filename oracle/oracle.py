@@ -12,8 +12,8 @@ import subprocess
 
 import numpy as np
 
-Q8_0, Q4_K, Q6_K, NVFP4, Q5_K = 1, 2, 3, 4, 5
-FORMATS = {"Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K, "NVFP4": NVFP4, "Q5_K": Q5_K}
+Q8_0, Q4_K, Q6_K, NVFP4, Q5_K, FP8 = 1, 2, 3, 4, 5, 6
+FORMATS = {"Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K, "NVFP4": NVFP4, "Q5_K": Q5_K, "FP8": FP8}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")

@@ -18,6 +18,8 @@ hidden 5,120 / MLP 17,408 / vocab 248,320 and the 288-expert, 4096x2048 MoE):
           [-128, 127]; d = fp16(|N(0,1)| * 0.01)
   NVFP4 : code bytes uniform (each E2M1 nibble uniform over 16 values); block
           scale = e4m3fn(|N(0,1)|); per-tensor scale g = f32(0.01 * (1 + U))
+  FP8   : E4M3 code bytes uniform over the 254 finite codes (the two NaN codes
+          drawn are replaced by 0); row scale = f32(0.01 * (0.5 + U) / 448)
   x     : bf16(N(0,1))
   ids   : per token, k distinct experts drawn uniformly from E (token-major rows)
 All float narrowing rounds to nearest even (numpy / torch conversions).
@@ -26,8 +28,8 @@ from __future__ import annotations
 
 import numpy as np
 
-Q8_0, Q4_K, Q6_K, NVFP4, Q5_K = 1, 2, 3, 4, 5
-QK = {Q8_0: 32, Q4_K: 256, Q6_K: 256, NVFP4: 16, Q5_K: 256}
+Q8_0, Q4_K, Q6_K, NVFP4, Q5_K, FP8 = 1, 2, 3, 4, 5, 6
+QK = {Q8_0: 32, Q4_K: 256, Q6_K: 256, NVFP4: 16, Q5_K: 256, FP8: 64}
 BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210, Q5_K: 176}
 
 
@@ -96,6 +98,14 @@ def nvfp4(g: np.random.Generator, rows: int, K: int, E: int = 1) -> np.ndarray:
     return np.concatenate([codes, scales, gs])
 
 
+def fp8(g: np.random.Generator, rows: int, K: int) -> np.ndarray:
+    """Planes [codes rows*K][row scales: rows fp32]."""
+    codes = _random_bytes(g, rows * K)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    scales = (0.01 * (0.5 + g.random(rows)) / 448.0).astype(np.float32).view(np.uint8)
+    return np.concatenate([codes, scales])
+
+
 def weights(fmt: int, g: np.random.Generator, rows: int, K: int, E: int = 1) -> np.ndarray:
     """Packed weight[rows, K] (rows = E*N for a stacked tensor) as flat uint8."""
     if K % QK[fmt]:
@@ -110,6 +120,8 @@ def weights(fmt: int, g: np.random.Generator, rows: int, K: int, E: int = 1) -> 
         return q5_k(g, rows, K)
     if fmt == NVFP4:
         return nvfp4(g, rows, K, E)
+    if fmt == FP8:
+        return fp8(g, rows, K)
     raise ValueError("unknown format %r" % fmt)
 
 

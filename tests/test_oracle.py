@@ -192,6 +192,9 @@ def test_packed_bytes_rejects():
     assert oracle.packed_bytes(9, 1, 4, 256) == 0
     assert oracle.packed_bytes(oracle.NVFP4, 1, 4, 24) == 0
     assert oracle.packed_bytes(oracle.Q8_0, 1, 0, 64) == 0
+    assert oracle.packed_bytes(oracle.FP8, 1, 4, 96) == 0  # K not a multiple of 64
+    # FP8: one byte per value plus one fp32 scale per row
+    assert oracle.packed_bytes(oracle.FP8, 3, 5, 128) == 15 * 128 + 15 * 4
 
 
 # ---------------------------------------------------------------- number formats
@@ -368,6 +371,39 @@ def test_nvfp4_exact_and_order():
     assert differ > 0
 
 
+def enc_fp8(codes, scales):
+    """Planes [codes R x K][R fp32 row scales], written field by field."""
+    b = bytearray()
+    for row in codes:
+        b += bytes(row)
+    for sc in scales:
+        b += np.float32(sc).tobytes()
+    return as_u8(bytes(b))
+
+
+def test_fp8_exact_every_code():
+    """w = RN32(e4m3(c) * s), one rounding; all 256 codes (NaN codes give NaN)
+    under several scales, including subnormal, negative and zero scales."""
+    K = 256
+    scale_list = [1.0, 0.0123456789, -3.5e-3, 1.4e-45, 2.0**-130, 0.0, 3.3e38]
+    codes = [list(range(256)) for _ in scale_list]
+    w = oracle.dequant_rows(oracle.FP8, enc_fp8(codes, scale_list), 1, len(scale_list), K)
+    for r, sc in enumerate(scale_list):
+        sv = Fraction(float(np.float32(sc)))
+        for c in range(256):
+            v = e4m3_value(c)
+            if isinstance(v, float):  # NaN
+                assert np.isnan(w[r, c]), (r, c)
+                continue
+            exact = v * sv
+            big = abs(exact) >= Fraction(2) ** 128
+            exp32 = np.float32(np.inf if exact > 0 else -np.inf) if big else rn32(exact)
+            assert same_values(w[r, c:c + 1], np.array([exp32], np.float32)), (r, c, sc)
+    # stacked rows take their own scales
+    wr = oracle.dequant_rows(oracle.FP8, enc_fp8([[0x38] * 64, [0x38] * 64], [2.0, -0.5]), 1, 2, 64)
+    assert (wr[0] == 2.0).all() and (wr[1] == -0.5).all()  # 0x38 = 1.0
+
+
 def test_generator_fields_in_range():
     g = synth.rng(1, 0)
     w = synth.weights(synth.Q8_0, g, 64, 1024).reshape(-1, 34)
@@ -386,6 +422,12 @@ def test_generator_fields_in_range():
     assert nv.size == oracle.packed_bytes(oracle.NVFP4, 1, 32, 256)
     gsc = nv[-4:].view(np.float32)[0]
     assert 0.01 <= gsc <= 0.02
+    f8 = synth.weights(synth.FP8, synth.rng(7, 0), 40, 512)
+    assert f8.size == oracle.packed_bytes(oracle.FP8, 1, 40, 512)
+    codes = f8[:40 * 512]
+    assert not ((codes & 0x7F) == 0x7F).any() and len(np.unique(codes)) == 254
+    rs = f8[40 * 512:].view(np.float32)
+    assert (rs > 0.005 / 448 - 1e-9).all() and (rs < 0.015 / 448 + 1e-9).all()
 
 
 # ---------------------------------------------------------------- the product
@@ -394,7 +436,7 @@ def _bf16_to_f64(xb):
     return (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-@pytest.mark.parametrize("fmt,K", [(1, 1024), (2, 1024), (3, 768), (4, 512), (5, 768)])
+@pytest.mark.parametrize("fmt,K", [(1, 1024), (2, 1024), (3, 768), (4, 512), (5, 768), (6, 512)])
 def test_gemm_matches_numpy_fp64(fmt, K):
     N, M = 67, 3
     w = synth.weights(fmt, synth.rng(5, 0), N, K)
