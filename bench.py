@@ -72,6 +72,12 @@ def workloads():
         "nvfp4_down_m1": Workload("NVFP4 MLP, N=5120 K=17408", qg.NVFP4, 5120, 17408, 1, 4),
         "nvfp4_down_m8": Workload("NVFP4 MLP, N=5120 K=17408", qg.NVFP4, 5120, 17408, 8, 4),
         "nvfp4_down_m512": Workload("NVFP4 MLP prefill, N=5120 K=17408", qg.NVFP4, 5120, 17408, 512, 4),
+        "fp8_gateup": Workload("row-scaled FP8 fused gate+up GEMV, N=34816 K=5120", qg.FP8, 2 * 17408, 5120, 1, 7),
+        "fp8_gateup_m8": Workload("row-scaled FP8 fused gate+up, N=34816 K=5120", qg.FP8, 2 * 17408, 5120, 8, 7),
+        "fp8_gateup_m512": Workload("row-scaled FP8 fused gate+up prefill, N=34816 K=5120", qg.FP8, 2 * 17408, 5120,
+                                    512, 7),
+        "fp8_head_m1": Workload("row-scaled FP8 LM head, N=248320 K=5120", qg.FP8, 248320, 5120, 1, 7),
+        "fp8_head_m8": Workload("row-scaled FP8 LM head, N=248320 K=5120", qg.FP8, 248320, 5120, 8, 7),
         "moe_gate": Workload("Q4_K grouped experts gate, E=288 N=2048 K=4096", qg.Q4_K, 2048, 4096, 128, 5, E=288,
                              moe=(16, 8)),
         "moe_down": Workload("Q4_K grouped experts down, E=288 N=4096 K=2048", qg.Q4_K, 4096, 2048, 128, 5, E=288,

@@ -21,8 +21,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-Q8_0, Q4_K, Q6_K, NVFP4, Q5_K = 1, 2, 3, 4, 5
-FORMATS = {"Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K, "NVFP4": NVFP4, "Q5_K": Q5_K}
+Q8_0, Q4_K, Q6_K, NVFP4, Q5_K, FP8 = 1, 2, 3, 4, 5, 6
+FORMATS = {"Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K, "NVFP4": NVFP4, "Q5_K": Q5_K, "FP8": FP8}
 
 QG_OK, QG_EINVAL, QG_EFORMAT, QG_EALIGN, QG_ESHAPE, QG_EHIP, QG_ENOTIMPL, QG_EWORKSPACE = range(8)
 

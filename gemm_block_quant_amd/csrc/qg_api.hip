@@ -18,6 +18,7 @@ int64_t block_values(int fmt) {
         case QG_Q5_K: return 256;
         case QG_Q6_K: return 256;
         case QG_NVFP4: return 16;
+        case QG_FP8: return 64;
         default: return 0;
     }
 }
@@ -54,6 +55,11 @@ StreamArgs stream_args(const void* w, int fmt, int64_t E, int64_t e, int64_t N, 
         a.w0 = base + e * N * a.rb0;
         a.w1 = base + R * a.rb0 + e * N * a.rb1;
         a.gbytes = base + R * a.rb0 + R * a.rb1 + 4 * e;
+    } else if (fmt == QG_FP8) {
+        a.rb0 = K;  // codes
+        a.rb1 = 4;  // one fp32 row scale
+        a.w0 = base + e * N * a.rb0;
+        a.w1 = base + R * a.rb0 + e * N * a.rb1;
     } else {
         a.rb0 = (K / block_values(fmt)) * block_bytes(fmt);
         a.w0 = base + e * N * a.rb0;
@@ -169,6 +175,7 @@ size_t quant_packed_bytes(qg_format fmt, int64_t E, int64_t N, int64_t K) {
     if (qk == 0 || E < 0 || N < 0 || K < 0 || K % qk) return 0;
     const int64_t rows = E * N, blocks = rows * (K / qk);
     if (fmt == QG_NVFP4) return (size_t)(blocks * 9 + 4 * E);
+    if (fmt == QG_FP8) return (size_t)(rows * K + 4 * rows);
     return (size_t)(blocks * block_bytes(fmt));
 }
 
@@ -203,7 +210,7 @@ qg_status quant_gemm(const void* w, qg_format fmt, int64_t N, int64_t K, int64_t
     }
     if (M >= kMfmaMinRows && mfma_kquant_supported(fmt, (int)K)) {
         if (M > INT32_MAX) return QG_ESHAPE;
-        return launch_mfma_kquant(fmt, (const uint8_t*)w, (int)N, (int)K, x, K, (int)M, y, N, (hipStream_t)stream) ==
+        return launch_mfma_kquant(fmt, a.w0, a.w1, (int)N, (int)K, x, K, (int)M, y, N, (hipStream_t)stream) ==
                        hipSuccess
                    ? QG_OK
                    : QG_EHIP;

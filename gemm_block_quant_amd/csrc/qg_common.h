@@ -56,6 +56,13 @@ __device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t v) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, SEL));
 }
 
+// Two E4M3 codes in half SEL of v (bytes 2 SEL, 2 SEL + 1) -> packed bf16 pair
+// (exact: E4M3 values are bf16 values; scale 1.0).
+template <int SEL>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t v) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, SEL != 0));
+}
+
 // bf16 pair (128 + a, 128 + b) from the byte values a, b < 128 sitting in bytes
 // i and j of v (bf16 0x43XX is 128 + XX for XX < 128).
 __device__ __forceinline__ uint32_t bias128_pair(uint32_t v, uint32_t sel) {

@@ -8,6 +8,7 @@
 //   Q5_K  the same, with 5-bit codes
 //   Q6_K  w = (d * s) * (q - 32)            (exact)
 //   NVFP4 w = (e2m1 * e4m3) * g             (first product exact, one rounding)
+//   FP8   w = e4m3 * s                      (one rounding; a thread per 64 values)
 // Block sizes: Q8_0 34 bytes and Q6_K 210 bytes (vllm.cpp issue #3030,
 // "BACKEND-TENSTORRENT-KEEPQUANT", issue body); NVFP4 ingredients: E2M1 codes,
 // block scales and a per-tensor scale ("I Built a Custom Blackwell Kernel for
@@ -27,7 +28,7 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
 
 __global__ __launch_bounds__(256) void k_dequant_block(int fmt, const uint8_t* __restrict__ w, int64_t rows, int64_t K,
                                                       int64_t N, float* __restrict__ out) {
-    const int qk = fmt == QG_Q8_0 ? 32 : fmt == QG_NVFP4 ? 16 : 256;
+    const int qk = fmt == QG_Q8_0 ? 32 : fmt == QG_NVFP4 ? 16 : fmt == QG_FP8 ? 64 : 256;
     const int64_t nb = K / qk;
     const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (blk >= rows * nb) return;
@@ -101,6 +102,12 @@ __global__ __launch_bounds__(256) void k_dequant_block(int fmt, const uint8_t* _
                 }
             }
         }
+    } else if (fmt == QG_FP8) {  // planes over R = rows: codes [R][K], fp32 row scales [R]
+        const uint8_t* codes = w + r * K + b * 64;
+        const uint8_t* sp = w + rows * K + 4 * r;
+        const uint32_t sb = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8) | ((uint32_t)sp[2] << 16) | ((uint32_t)sp[3] << 24);
+        const float s = __builtin_bit_cast(float, sb);
+        for (int i = 0; i < 64; ++i) o[i] = e4m3_to_f32<0>(codes[i]) * s;
     } else {  // NVFP4 planes over R = rows: codes [R][K/2], scales [R][K/16], g [rows / N]
         const uint8_t* codes = w + r * (K / 2) + b * 8;
         const uint8_t sb = w[rows * (K / 2) + r * (K / 16) + b];
@@ -116,7 +123,7 @@ __global__ __launch_bounds__(256) void k_dequant_block(int fmt, const uint8_t* _
 }
 
 hipError_t launch_dequant(int fmt, const uint8_t* w, int64_t E, int64_t N, int64_t K, float* out, hipStream_t st) {
-    const int qk = fmt == QG_Q8_0 ? 32 : fmt == QG_NVFP4 ? 16 : 256;
+    const int qk = fmt == QG_Q8_0 ? 32 : fmt == QG_NVFP4 ? 16 : fmt == QG_FP8 ? 64 : 256;
     const int64_t rows = E * N;
     const int64_t nblk = rows * (K / qk);
     if (nblk == 0) return hipSuccess;

@@ -374,6 +374,68 @@ template <> struct Direct<QG_NVFP4> {
     }
 };
 
+// Row-scaled FP8.  Unit u of a row = codes 64u .. 64u + 63, one E4M3 byte per
+// value (exact in bf16); with them each lane loads the row's fp32 scale (the
+// same 4 bytes for all units of a row: one line, no extra HBM traffic) and
+// adds the unit's sum scaled by it.
+template <> struct Direct<QG_FP8> {
+    static constexpr int UV = 64;
+    static constexpr int REGS = 17;
+    static constexpr bool SUMS = false;
+    struct Lane {};
+    __device__ static Lane lane_consts(int) { return Lane{}; }
+    __device__ __host__ static int units_per_row(int K) { return K / 64; }
+    // Bytes of one pass (16 units) of a row: codes; the scale does not move.
+    static constexpr int PASS0 = 16 * 64, PASS1 = 0;
+    // Offsets from the start of a pass's stretch: codes (a), row scale (b).
+    struct Offs {
+        uint32_t a, b;
+    };
+    __device__ static Offs slot_offs(int s) { return Offs{64u * (uint32_t)s, 0u}; }
+    __device__ static Offs shift(const Offs& o, uint32_t r0, uint32_t r1) { return Offs{o.a + r0, o.b + r1}; }
+    __device__ static Offs pick(bool c, const Offs& x, const Offs& y) { return Offs{c ? x.a : y.a, c ? x.b : y.b}; }
+    __device__ static void load_at(uint32_t (&r)[REGS], const uint8_t* b0, const uint8_t* b1, const Offs& o) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 q = ld_stream128(b0 + o.a + 16 * i);
+            r[4 * i] = q.x;
+            r[4 * i + 1] = q.y;
+            r[4 * i + 2] = q.z;
+            r[4 * i + 3] = q.w;
+        }
+        r[16] = *(const QG_GLOBAL uint32_t*)(uintptr_t)(b1 + o.b);
+    }
+    template <int MT>
+    __device__ static void decode(const uint32_t (&r)[REGS], const Lane&, int u, bool live, const lds_u8* xa,
+                                  int xmg_bytes, const lds_f32*, int, float (&acc)[MT]) {
+        constexpr int MG = (MT + 3) / 4;
+        f32x4_t c[MG];
+#pragma unroll
+        for (int g = 0; g < MG; ++g) c[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int rot = u & 3;
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) {
+            // values 8ch .. 8ch + 7: code dwords 2ch, 2ch + 1
+            const uint32_t p0 = e4m3x2_to_bf16x2<0>(r[2 * ch]), p1 = e4m3x2_to_bf16x2<1>(r[2 * ch]);
+            const uint32_t p2 = e4m3x2_to_bf16x2<0>(r[2 * ch + 1]), p3 = e4m3x2_to_bf16x2<1>(r[2 * ch + 1]);
+#pragma unroll
+            for (int g = 0; g < MG; ++g) {
+                const u32x4 xv = lds_ld128(xa + g * xmg_bytes + ((ch ^ rot) * 4 * 16));
+                c[g] = mfma4(xv.x, xv.y, p0, p1, c[g]);
+                c[g] = mfma4(xv.z, xv.w, p2, p3, c[g]);
+            }
+        }
+        if (live) {
+            const float s = __builtin_bit_cast(float, r[16]);
+#pragma unroll
+            for (int g = 0; g < MG; ++g)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * g + i < MT) acc[4 * g + i] = fmaf(s, c[g][i], acc[4 * g + i]);
+        }
+    }
+};
+
 // Q6_K.  Unit u of a row = quarter of super-block u / 4: half h = (u / 2) % 2,
 // part t = u % 2, i.e. the 64 values 128h + 32p + 16t + [0,16), p = 0..3,
 // each group of 16 with its own int8 sub-scale s[8h + 2p + t].  Its bytes: low
@@ -694,7 +756,7 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
     const int live_last = U - (P - 1) * G;  // live slots of the last pass, 1..16
     const typename D::Offs o_last = D::slot_offs(slot < live_last ? slot : slot % live_last);
     const uint32_t lrow0 = (uint32_t)grp * (uint32_t)mv.rb0;
-    const uint32_t lrow1 = F == QG_NVFP4 ? (uint32_t)grp * (uint32_t)mv.rb1 : 0u;
+    const uint32_t lrow1 = F == QG_NVFP4 || F == QG_FP8 ? (uint32_t)grp * (uint32_t)mv.rb1 : 0u;
 
     // current item: local row group, segment, pass cursor and end pass; its
     // row group's bases and this lane's offsets (rows past N read the group's
@@ -718,7 +780,7 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
             cur_end = min(P, cur_p + PS);
             const int rg = rg_base + q;
             cur_b0 = mv.w0 + (size_t)(RW * rg) * mv.rb0;
-            cur_b1 = F == QG_NVFP4 ? mv.w1 + (size_t)(RW * rg) * mv.rb1 : nullptr;
+            cur_b1 = F == QG_NVFP4 || F == QG_FP8 ? mv.w1 + (size_t)(RW * rg) * mv.rb1 : nullptr;
             const bool real = RW * rg + grp < N;
             cur_o = D::shift(o_slot, real ? lrow0 : 0u, real ? lrow1 : 0u);
             cur_ol = D::shift(o_last, real ? lrow0 : 0u, real ? lrow1 : 0u);
@@ -813,7 +875,7 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
 }
 
 inline bool direct_eligible(int fmt, int K) {
-    return fmt == QG_Q4_K || fmt == QG_Q5_K || fmt == QG_Q6_K || (fmt == QG_NVFP4 && K % 64 == 0);
+    return fmt == QG_Q4_K || fmt == QG_Q5_K || fmt == QG_Q6_K || fmt == QG_FP8 || (fmt == QG_NVFP4 && K % 64 == 0);
 }
 
 }  // namespace qg

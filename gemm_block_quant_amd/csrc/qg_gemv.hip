@@ -172,6 +172,7 @@ template <int MT> struct DirectTune<QG_Q4_K, MT> { static constexpr int SP = 1, 
 template <int MT> struct DirectTune<QG_Q5_K, MT> { static constexpr int SP = 1, PF = 2; };
 template <int MT> struct DirectTune<QG_NVFP4, MT> { static constexpr int SP = 1, PF = 2; };
 template <int MT> struct DirectTune<QG_Q6_K, MT> { static constexpr int SP = 1, PF = 2; };
+template <int MT> struct DirectTune<QG_FP8, MT> { static constexpr int SP = 1, PF = 2; };
 
 template <int F, int MT>
 static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
@@ -204,7 +205,7 @@ static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
 
 template <int F>
 static hipError_t dispatch_mt(const StreamArgs& a, int mt, hipStream_t st) {
-    if constexpr (F == QG_Q4_K || F == QG_Q5_K || F == QG_Q6_K || F == QG_NVFP4) {
+    if constexpr (F == QG_Q4_K || F == QG_Q5_K || F == QG_Q6_K || F == QG_NVFP4 || F == QG_FP8) {
         if (direct_eligible(F, a.K)) {
             switch (mt) {
                 case 1: return dispatch_direct<F, 1>(a, st);
@@ -251,6 +252,7 @@ hipError_t launch_stream_gemm(int fmt, StreamArgs a, hipStream_t st) {
         case QG_Q4_K: return dispatch_mt<QG_Q4_K>(a, mt, st);
         case QG_Q5_K: return dispatch_mt<QG_Q5_K>(a, mt, st);
         case QG_Q6_K: return dispatch_mt<QG_Q6_K>(a, mt, st);
+        case QG_FP8: return dispatch_mt<QG_FP8>(a, mt, st);
         default: return dispatch_mt<QG_NVFP4>(a, mt, st);
     }
 }

@@ -244,7 +244,7 @@ static hipError_t launch_grouped_one(Kern kern, size_t lds, const StreamArgs& a,
 template <int F, int MTMAX>
 static hipError_t grouped_paths(StreamArgs a, const int32_t* ws, int64_t E, int64_t M, int64_t es0, int64_t es1,
                                 hipStream_t st) {
-    if constexpr (F == QG_Q4_K || F == QG_Q5_K || F == QG_Q6_K || F == QG_NVFP4) {
+    if constexpr (F == QG_Q4_K || F == QG_Q5_K || F == QG_Q6_K || F == QG_NVFP4 || F == QG_FP8) {
         if (direct_eligible(F, a.K)) {
             const Segments sg = direct_segments(F, a.N, a.K, num_cus());
             a.seg_S = sg.S;
@@ -311,6 +311,7 @@ hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int6
         case QG_Q4_K: return grouped_mt<QG_Q4_K>(a, mtmax, ws, E, M, estride0, estride1, st);
         case QG_Q5_K: return grouped_mt<QG_Q5_K>(a, mtmax, ws, E, M, estride0, estride1, st);
         case QG_Q6_K: return grouped_mt<QG_Q6_K>(a, mtmax, ws, E, M, estride0, estride1, st);
+        case QG_FP8: return grouped_mt<QG_FP8>(a, mtmax, ws, E, M, estride0, estride1, st);
         default: return grouped_mt<QG_NVFP4>(a, mtmax, ws, E, M, estride0, estride1, st);
     }
 }

@@ -1,5 +1,5 @@
-// qg_mfma_kq.hip -- Q4_K, Q5_K, Q6_K and Q8_0 products for M >= 32 activation
-// rows on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
+// qg_mfma_kq.hip -- Q4_K, Q5_K, Q6_K, Q8_0 and row-scaled FP8 products for
+// M >= 32 activation rows on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
 //
 // Prefill must read each packed weight slab once for all rows rather than once
 // per few rows ("Qwen3.8-27B on one Tenstorrent P150", section "3. Porting the
@@ -15,6 +15,8 @@
 //   Q8_0 (32 values):       v = q + 128 (the code as an unsigned byte),
 //                           s = d, t = -128 d
 // (the factorisation of the decode path, applied per 32 x 32 output block).
+// Row-scaled FP8 needs none of it: v = e4m3 (exact in bf16) over all of K, the
+// products accumulate in place and the row's scale multiplies the result.
 //
 // Tiling: a 256-thread workgroup computes a BM x 64 tile of y, four waves own
 // (BM/2) x 32 quarters as 32x32 accumulators.  A K step is 64 values staged in
@@ -28,8 +30,9 @@ namespace qg {
 struct KqArgs {
     const uint16_t* x;  // bf16 [M, K], row stride ldx
     int64_t ldx;
-    const uint8_t* w;  // packed rows
-    int64_t rb;        // bytes per weight row
+    const uint8_t* w;   // packed rows
+    const uint8_t* w1;  // FP8: fp32 row scales
+    int64_t rb;         // bytes per weight row
     float* y;          // fp32 [M, N], row stride ldy
     int64_t ldy;
     int M, N, K;
@@ -42,6 +45,7 @@ __device__ __forceinline__ uint32_t bf16_pair_exact(float lo, float hi) {
 
 // Per-format pieces.  Each provides:
 //   SUB            values per sub-block (32 or 16); a step holds 64 / SUB
+//   ROWSCALE       no per-sub-block terms: one scale per weight row (FP8)
 //   Ring           registers one thread holds for one step
 //   x_step(s)      offset of step s's first activation (uniform)
 //   x_chunk(q)     offset of the step's 8-value chunk q (tile columns 8q..8q+7)
@@ -55,6 +59,7 @@ template <int F> struct KqFmt;
 // p decodes code bytes 8p..8p+7 of the quarter: positions 8p..8p+7 of both.
 template <int BB, int CODES, int HIGH> struct KqFmtK4 {
     static constexpr int SUB = 32;
+    static constexpr bool ROWSCALE = false;
     struct Ring {
         u32x4 hdr;  // d, dmin, 12 scale bytes
         u32x2 q;    // 8 code bytes
@@ -114,6 +119,7 @@ template <> struct KqFmt<QG_Q5_K> : KqFmtK4<176, 48, 16> {};  // fifth bits at [
 // 2-byte aligned).  Part p decodes codes 16 (p & 1) .. + 15 of block 2s + p / 2.
 template <> struct KqFmt<QG_Q8_0> {
     static constexpr int SUB = 32;
+    static constexpr bool ROWSCALE = false;
     struct Ring {
         u32x4 q;     // 16 codes
         uint32_t d;  // fp16 d of the block
@@ -158,6 +164,7 @@ template <> struct KqFmt<QG_Q8_0> {
 // decodes l = 16 h + 4 p .. + 3 of the four quadrants.
 template <> struct KqFmt<QG_Q6_K> {
     static constexpr int SUB = 16;
+    static constexpr bool ROWSCALE = false;
     struct Ring {
         uint32_t qa, qb, qh;  // low-bit bytes (quadrants 0/2, 1/3) and high-bit bytes of 4 positions
         u32x2 sc;             // scales 8n .. 8n + 7
@@ -195,6 +202,28 @@ template <> struct KqFmt<QG_Q6_K> {
     }
 };
 
+// Row-scaled FP8: step s is codes 64s .. 64s + 63 of the row; part p converts
+// codes 16p .. 16p + 15 to bf16 (exact).  The row scale is applied at the end.
+template <> struct KqFmt<QG_FP8> {
+    static constexpr int SUB = 64;
+    static constexpr bool ROWSCALE = true;
+    struct Ring {
+        u32x4 q;  // 16 codes
+    };
+    __device__ static int x_step(int s) { return 64 * s; }
+    __device__ static int x_chunk(int q) { return 8 * q; }
+    __device__ static Ring load(const uint8_t* wrow, int s, int part) {
+        return Ring{ld_global128(wrow + 64 * (size_t)s + 16 * part)};
+    }
+    __device__ static void decode(const Ring& r, int, int part, lds_u8* trow, lds_f32*) {
+        const uint32_t c0 = r.q.x, c1 = r.q.y, c2 = r.q.z, c3 = r.q.w;
+        *(lds_u32x4*)(trow + 32 * part) = u32x4{e4m3x2_to_bf16x2<0>(c0), e4m3x2_to_bf16x2<1>(c0),
+                                                e4m3x2_to_bf16x2<0>(c1), e4m3x2_to_bf16x2<1>(c1)};
+        *(lds_u32x4*)(trow + 32 * part + 16) = u32x4{e4m3x2_to_bf16x2<0>(c2), e4m3x2_to_bf16x2<1>(c2),
+                                                     e4m3x2_to_bf16x2<0>(c3), e4m3x2_to_bf16x2<1>(c3)};
+    }
+};
+
 // D: K steps of loads in flight in the register ring (an even number).
 template <int F, int BM, int D>
 __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
@@ -207,8 +236,8 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
     constexpr int XCH = BM * 8 / kMfmaThreads;   // 16-byte activation chunks per thread per step
     constexpr int TILE_X = BM * kMfmaRowBytes;   // activations (bf16, padded rows)
     constexpr int TILE_W = BN * kMfmaRowBytes;   // tile values v (bf16)
-    constexpr int TILE_S = BN * 8 * NSUB;        // per weight row: s of each sub-block, then t
-    constexpr int TILE_XS = NSUB * BM * 4;       // per sub-block and activation row: X
+    constexpr int TILE_S = Fmt::ROWSCALE ? 0 : BN * 8 * NSUB;   // per weight row: s of each sub-block, then t
+    constexpr int TILE_XS = Fmt::ROWSCALE ? 0 : NSUB * BM * 4;  // per sub-block and activation row: X
     constexpr int BUF = TILE_X + TILE_W + TILE_S + TILE_XS;
     static_assert(BN * 4 == kMfmaThreads, "four threads per weight row");
     __shared__ __attribute__((aligned(16))) uint8_t smem_generic[2 * BUF];
@@ -256,6 +285,7 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
             const int i = tid + c * kMfmaThreads;
             const int r = i >> 3, q = i & 7;
             *(lds_u32x4*)(tx + r * kMfmaRowBytes + q * 16) = xr[j][c];
+            if constexpr (Fmt::ROWSCALE) continue;
             // sum of this chunk's 8 values (pairs dotted with (1, 1)), then over
             // the chunks of the sub-block: lanes xor 1 (and xor 2) of a quad
             // (element copies first: a bit cast of a vector element reads element 0)
@@ -287,6 +317,27 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
         const lds_u8* tw = tx + TILE_X;
         const lds_f32* ts = (const lds_f32*)(tw + TILE_W);
         const lds_f32* txs = (const lds_f32*)((const lds_u8*)ts + TILE_S);
+        if constexpr (Fmt::ROWSCALE) {
+            // the whole step accumulates in place
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                bf16x8_t fa[FM], fb[FN];
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    fa[i] = __builtin_bit_cast(
+                        bf16x8_t, lds_ld128(tx + (wm + 32 * i + frow) * kMfmaRowBytes + kk * 32 + fcol));
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    fb[j] = __builtin_bit_cast(
+                        bf16x8_t, lds_ld128(tw + (wn + 32 * j + frow) * kMfmaRowBytes + kk * 32 + fcol));
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            }
+            return;
+        }
         // t * X of two sub-blocks per 32x32x2 fp32 product:
         // A[m][k] = X(row m, sub-block 2p + k), lane l holds m = l % 32, k = l / 32;
         // B[k][n] = t(row n, sub-block 2p + k), same lane mapping.
@@ -376,15 +427,19 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
     });
 
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j) {
+        const int n = n0 + wn + 32 * j + (lane & 31);
+        float rs = 1.f;
+        if constexpr (Fmt::ROWSCALE) rs = *(const QG_GLOBAL float*)(uintptr_t)(a.w1 + 4 * (size_t)(n < N ? n : 0));
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int n = n0 + wn + 32 * j + (lane & 31);
-                if (m < M && n < N) st_global_f32(a.y + (size_t)m * a.ldy + n, acc[i][j][r]);
+                if (m < M && n < N)
+                    st_global_f32(a.y + (size_t)m * a.ldy + n, Fmt::ROWSCALE ? acc[i][j][r] * rs : acc[i][j][r]);
             }
+    }
 }
 
 // Tile shape: 128 x 64 when its tile count covers every CU, else 64 x 64.
@@ -408,20 +463,22 @@ bool mfma_kquant_supported(int fmt, int K) {
     switch (fmt) {
         case QG_Q4_K:
         case QG_Q5_K:
-        case QG_Q6_K: return true;                 // K is a multiple of 256
+        case QG_Q6_K:                              // K is a multiple of 256
+        case QG_FP8: return true;                  // K is a multiple of 64
         case QG_Q8_0: return K % kMfmaKStep == 0;  // whole 64-value steps
         default: return false;
     }
 }
 
-hipError_t launch_mfma_kquant(int fmt, const uint8_t* w, int N, int K, const uint16_t* x, int64_t ldx, int M,
-                              float* y, int64_t ldy, hipStream_t st) {
-    KqArgs a = {x, ldx, w, 0, y, ldy, M, N, K};
+hipError_t launch_mfma_kquant(int fmt, const uint8_t* w, const uint8_t* w1, int N, int K, const uint16_t* x,
+                              int64_t ldx, int M, float* y, int64_t ldy, hipStream_t st) {
+    KqArgs a = {x, ldx, w, w1, 0, y, ldy, M, N, K};
     switch (fmt) {
         case QG_Q4_K: a.rb = (int64_t)(K / 256) * 144; return launch_kq<QG_Q4_K>(a, st);
         case QG_Q5_K: a.rb = (int64_t)(K / 256) * 176; return launch_kq<QG_Q5_K>(a, st);
         case QG_Q6_K: a.rb = (int64_t)(K / 256) * 210; return launch_kq<QG_Q6_K>(a, st);
         case QG_Q8_0: a.rb = (int64_t)(K / 32) * 34; return launch_kq<QG_Q8_0>(a, st);
+        case QG_FP8: a.rb = K; return launch_kq<QG_FP8>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -60,6 +60,11 @@
  *    w = (e2m1 * e4m3) * g  ("I Built a Custom Blackwell Kernel for
  *    Qwen3.8-27B", section "What the custom path actually does": E2M1 codes,
  *    block scales and a per-site weight scale kept in the artefact).
+ *  - QG_FP8 (row-scaled FP8; K a multiple of 64): two planes over R = E*N rows:
+ *      codes  [R][K]  one E4M3 (fn) byte per value;
+ *      scales [R]     one fp32 scale per row.
+ *    w = e4m3 * s  (same page and section: attention and GDN projections, the
+ *    output head and the last eight MLPs stay row-scaled FP8).
  *  quant_packed_bytes() is the single source of truth for buffer sizes.
  *
  * Numerics: the dequantized weights of quant_dequantize are bit-exact fp32
@@ -81,7 +86,7 @@
 extern "C" {
 #endif
 
-typedef enum { QG_Q8_0 = 1, QG_Q4_K = 2, QG_Q6_K = 3, QG_NVFP4 = 4, QG_Q5_K = 5 } qg_format;
+typedef enum { QG_Q8_0 = 1, QG_Q4_K = 2, QG_Q6_K = 3, QG_NVFP4 = 4, QG_Q5_K = 5, QG_FP8 = 6 } qg_format;
 
 typedef enum {
     QG_OK = 0,
@@ -94,7 +99,8 @@ typedef enum {
     QG_EWORKSPACE = 7 /* workspace missing or smaller than quant_grouped_workspace_bytes() */
 } qg_status;
 
-/* Values per block (32, 256, 256, 16) for a tag, 0 for an unknown tag.  Host only. */
+/* Values per block (Q8_0 32, Q4_K / Q5_K / Q6_K 256, NVFP4 16; FP8 64, the
+ * granularity of K) for a tag, 0 for an unknown tag.  Host only. */
 int64_t quant_block_values(qg_format fmt);
 
 /* Bytes of a packed weight[E*N, K] tensor in the layout above; 0 when the tag

@@ -34,12 +34,12 @@ def test_library_exports_every_declared_function():
 def test_packed_bytes_agrees_with_oracle():
     g = np.random.default_rng(0)
     for _ in range(300):
-        fmt = int(g.integers(0, 6))
+        fmt = int(g.integers(0, 8))
         E = int(g.integers(0, 5))
         N = int(g.integers(0, 3000))
         K = int(g.integers(0, 40)) * 16
         assert qg.quant_packed_bytes(fmt, E, N, K) == oracle.packed_bytes(fmt, E, N, K), (fmt, E, N, K)
-    for fmt in (1, 2, 3, 4):
+    for fmt in (1, 2, 3, 4, 5, 6):
         assert qg.quant_block_values(fmt) == oracle.block_values(fmt)
     assert qg.quant_block_values(0) == 0 and qg.quant_block_values(7) == 0
 
@@ -67,6 +67,7 @@ def test_validation_rejects_before_launch():
     assert gemm(FAKE_W, qg.Q4_K, -1, 256, 1, FAKE_X, FAKE_Y, None) == qg.QG_ESHAPE
     assert gemm(FAKE_W, qg.Q4_K, 4, 256, -2, FAKE_X, FAKE_Y, None) == qg.QG_ESHAPE
     assert gemm(FAKE_W, qg.NVFP4, 4, 24, 1, FAKE_X, FAKE_Y, None) == qg.QG_ESHAPE
+    assert gemm(FAKE_W, qg.FP8, 4, 96, 1, FAKE_X, FAKE_Y, None) == qg.QG_ESHAPE  # K a multiple of 64
     # empty products are valid no-ops, even with null pointers
     assert gemm(None, qg.Q4_K, 0, 256, 3, None, None, None) == qg.QG_OK
     assert gemm(None, qg.Q4_K, 5, 256, 0, None, None, None) == qg.QG_OK
@@ -107,7 +108,7 @@ def test_grouped_validation():
     args = lambda **kw: [kw.get("w", FAKE_W), kw.get("fmt", qg.Q4_K), kw.get("E", E), N, K, kw.get("M", M), FAKE_X,
                          kw.get("ids", ids), FAKE_Y, kw.get("ws", ws), kw.get("wsb", wsb), None]
     assert grouped(*args(E=0)) == qg.QG_ESHAPE
-    assert grouped(*args(fmt=6)) == qg.QG_EFORMAT
+    assert grouped(*args(fmt=7)) == qg.QG_EFORMAT
     assert grouped(*args(ws=None)) == qg.QG_EWORKSPACE
     assert grouped(*args(wsb=wsb - 1)) == qg.QG_EWORKSPACE
     assert grouped(*args(ws=ctypes.c_void_p(0x400004))) == qg.QG_EALIGN
@@ -136,7 +137,7 @@ def test_moe_block_validation():
                 kw.get("idx", idx), kw.get("wts", wts), FAKE_Y, kw.get("ws", ws), kw.get("wsb", wsb), None]
 
     assert moe(*args(fg=0)) == qg.QG_EFORMAT
-    assert moe(*args(fd=6)) == qg.QG_EFORMAT
+    assert moe(*args(fd=9)) == qg.QG_EFORMAT
     assert moe(*args(E=0)) == qg.QG_ESHAPE
     assert moe(*args(topk=0)) == qg.QG_ESHAPE
     assert moe(*args(D=D + 16)) == qg.QG_ESHAPE      # not a multiple of the gate|up block

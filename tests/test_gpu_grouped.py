@@ -18,6 +18,7 @@ def _ids_dev(ids):
 @pytest.mark.parametrize("fmt,E,N,K,M", [
     (qg.Q4_K, 5, 100, 512, 12), (qg.Q6_K, 4, 77, 768, 9), (qg.Q8_0, 6, 50, 1024, 20),
     (qg.NVFP4, 3, 64, 592, 7), (qg.Q4_K, 40, 130, 2048, 37), (qg.Q5_K, 6, 90, 1024, 15),
+    (qg.FP8, 5, 100, 1024, 13),
 ])
 def test_grouped_band_and_invalid_rows(fmt, E, N, K, M):
     w = synth.weights(fmt, synth.rng(21, 0), E * N, K, E=E)
@@ -34,7 +35,8 @@ def test_grouped_band_and_invalid_rows(fmt, E, N, K, M):
     assert_band(y[~bad], y_ref[~bad], bound[~bad], "grouped fmt %d" % fmt)
 
 
-@pytest.mark.parametrize("fmt,K", [(qg.Q4_K, 4096), (qg.NVFP4, 5120), (qg.Q6_K, 2048), (qg.Q5_K, 2048)])
+@pytest.mark.parametrize("fmt,K", [(qg.Q4_K, 4096), (qg.NVFP4, 5120), (qg.Q6_K, 2048), (qg.Q5_K, 2048),
+                                   (qg.FP8, 2048)])
 def test_grouped_e1_is_dense_bitwise(fmt, K):
     N, M = 257, 11
     w = synth.weights(fmt, synth.rng(22, 0), N, K)
@@ -55,6 +57,11 @@ def test_grouped_e1_is_dense_bitwise(fmt, K):
             sc = ws[R * K // 2 + e * N * K // 16: R * K // 2 + (e + 1) * N * K // 16]
             gs = ws[R * K // 2 + R * K // 16 + 4 * e: R * K // 2 + R * K // 16 + 4 * e + 4]
             we = np.concatenate([codes, sc, gs])
+        elif fmt == qg.FP8:  # planes: codes [E*N][K], then E*N fp32 row scales
+            R = E * N
+            codes = ws[e * N * K:(e + 1) * N * K]
+            sc = ws[R * K + 4 * e * N: R * K + 4 * (e + 1) * N]
+            we = np.concatenate([codes, sc])
         else:
             eb = oracle.packed_bytes(fmt, 1, N, K)
             we = ws[e * eb:(e + 1) * eb]

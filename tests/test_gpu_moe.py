@@ -37,6 +37,7 @@ def _run(fg, w_gu, fd, w_dn, E, D, F, x, idx, wts):
     (qg.NVFP4, qg.NVFP4, 5, 592, 288, 6, 2),  # D % 64 = 16: the row-buffer path for gate|up
     (qg.Q8_0, qg.Q8_0, 5, 1024, 512, 3, 3),
     (qg.Q4_K, qg.Q4_K, 40, 1024, 512, 16, 8),  # experts shared across tokens
+    (qg.FP8, qg.FP8, 6, 512, 768, 5, 3),
 ])
 def test_moe_block_band(fg, fd, E, D, F, T, topk):
     w_gu, w_dn, x, idx, wts = _case(fg, fd, E, D, F, T, topk, 31 + E + T)

@@ -23,6 +23,7 @@ DEQ_SHAPES = [
     (qg.Q5_K, 7, 512), (qg.Q5_K, 3, 5120),
     (qg.Q6_K, 11, 768), (qg.Q6_K, 2, 17408),
     (qg.NVFP4, 9, 48), (qg.NVFP4, 17, 5120),
+    (qg.FP8, 5, 64), (qg.FP8, 9, 5120),
 ]
 
 
@@ -42,6 +43,14 @@ def _with_specials(fmt, w, N, K):
         for i, s in enumerate(specials[: R * K // 16]):
             w[sc0 + i] = s
         w[0] = 0x08  # codes -0 and +0
+        return w
+    if fmt == qg.FP8:
+        codes = [0x00, 0x80, 0x01, 0x81, 0x07, 0x08, 0x7E, 0xFE, 0x7F, 0xFF, 0x38, 0xB8]
+        w[:len(codes)] = codes  # zeros, subnormals, smallest normal, max, NaN, +-1
+        rs = w[N * K:].view(np.float32)
+        for i, v in enumerate([0.0, 1.4e-45, -2.5e-3, 3.0e38]):
+            if i < N:
+                rs[i] = v
         return w
     bb = {qg.Q8_0: 34, qg.Q4_K: 144, qg.Q5_K: 176, qg.Q6_K: 210}[fmt]
     doff = {qg.Q8_0: 0, qg.Q4_K: 0, qg.Q5_K: 0, qg.Q6_K: 208}[fmt]
@@ -97,6 +106,10 @@ PRODUCT_CASES = [
     (qg.Q8_0, 200, 1024, 37), (qg.Q8_0, 130, 64, 33), (qg.Q8_0, 300, 1088, 130), (qg.Q8_0, 4100, 768, 450),
     # Q8_0 with K % 64 == 32 keeps the 16-row passes
     (qg.Q8_0, 100, 1056, 40),
+    # row-scaled FP8: decode, skinny, tall and matrix-core shapes
+    (qg.FP8, 1, 64, 1), (qg.FP8, 7, 192, 2), (qg.FP8, 1000, 5120, 1), (qg.FP8, 777, 5120, 8),
+    (qg.FP8, 257, 1792, 16), (qg.FP8, 130, 17408, 1), (qg.FP8, 64, 17408, 17), (qg.FP8, 33, 4096, 3),
+    (qg.FP8, 200, 5120, 37), (qg.FP8, 130, 64, 33), (qg.FP8, 300, 1088, 130), (qg.FP8, 4100, 768, 450),
 ]
 
 
@@ -113,7 +126,7 @@ def test_product_band(fmt, N, K, M):
 
 
 @pytest.mark.parametrize("fmt,N,K", [(qg.Q8_0, 300, 1024), (qg.Q4_K, 300, 5120), (qg.Q6_K, 300, 17408),
-                                     (qg.NVFP4, 300, 5120), (qg.Q5_K, 300, 5120),
+                                     (qg.NVFP4, 300, 5120), (qg.Q5_K, 300, 5120), (qg.FP8, 300, 5120),
                                      # tall: up to 8 rows take the whole-row-group kernel, 16 the direct one
                                      (qg.Q4_K, 16385, 5120), (qg.NVFP4, 16387, 5120)])
 def test_rows_match_decode_bitwise_and_repeat(fmt, N, K):
@@ -170,12 +183,15 @@ FULL = [
     (qg.NVFP4, 17408, 5120, 512), (qg.NVFP4, 5120, 17408, 512),
     (qg.Q4_K, 2 * 17408, 5120, 512), (qg.Q5_K, 2 * 17408, 5120, 512), (qg.Q6_K, 5120, 17408, 512),
     (qg.Q8_0, 1024, 1024, 512),
+    # row-scaled FP8: the output head and the fused gate+up shape
+    (qg.FP8, 248320, 5120, 1), (qg.FP8, 248320, 5120, 8),
+    (qg.FP8, 2 * 17408, 5120, 1), (qg.FP8, 2 * 17408, 5120, 8), (qg.FP8, 2 * 17408, 5120, 512),
 ]
 
 
 @pytest.mark.parametrize("fmt,N,K,M", FULL)
 def test_full_size_sampled(fmt, N, K, M):
-    seed = {qg.Q8_0: 1, qg.Q4_K: 2, qg.Q6_K: 3, qg.NVFP4: 4, qg.Q5_K: 6}[fmt]
+    seed = {qg.Q8_0: 1, qg.Q4_K: 2, qg.Q6_K: 3, qg.NVFP4: 4, qg.Q5_K: 6, qg.FP8: 7}[fmt]
     w = synth.weights(fmt, synth.rng(seed, 0), N, K)
     x = synth.x_bf16(synth.rng(seed, 1), M, K)
     wd, xd = dev_bytes(w), dev_x(x)
@@ -188,7 +204,7 @@ def test_full_size_sampled(fmt, N, K, M):
 
 
 @pytest.mark.parametrize("fmt,N,K", [(qg.NVFP4, 1000, 1040), (qg.Q4_K, 4100, 768), (qg.Q5_K, 4100, 768),
-                                     (qg.Q6_K, 4100, 768), (qg.Q8_0, 4100, 768)])
+                                     (qg.Q6_K, 4100, 768), (qg.Q8_0, 4100, 768), (qg.FP8, 4100, 768)])
 def test_mfma_rows_independent_of_tiling_and_repeat(fmt, N, K):
     """M >= 32 on the matrix cores: each output is one fixed fp32 accumulation
     over K, so the rows of a 37-row call equal those rows of a 512-row call
