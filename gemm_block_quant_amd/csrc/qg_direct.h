@@ -324,10 +324,12 @@ template <> struct Direct<QG_NVFP4> {
     __device__ static Offs shift(const Offs& o, uint32_t r0, uint32_t r1) { return Offs{o.a + r0, o.b + r1}; }
     __device__ static Offs pick(bool c, const Offs& x, const Offs& y) { return Offs{c ? x.a : y.a, c ? x.b : y.b}; }
     __device__ static void load_at(uint32_t (&r)[REGS], const uint8_t* b0, const uint8_t* b1, const Offs& o) {
-        const u32x4 q0 = ld_stream128(b0 + o.a), q1 = ld_stream128(b0 + o.a + 16);
+        // ordinary loads: each instruction uses half of the lines it touches
+        // (non-temporal loads of such lines were refetched)
+        const u32x4 q0 = ld_global128(b0 + o.a), q1 = ld_global128(b0 + o.a + 16);
         r[0] = q0.x; r[1] = q0.y; r[2] = q0.z; r[3] = q0.w;
         r[4] = q1.x; r[5] = q1.y; r[6] = q1.z; r[7] = q1.w;
-        r[8] = __builtin_nontemporal_load((const QG_GLOBAL uint32_t*)(uintptr_t)(b1 + o.b));
+        r[8] = *(const QG_GLOBAL uint32_t*)(uintptr_t)(b1 + o.b);
     }
     template <int MT>
     __device__ static void decode(const uint32_t (&r)[REGS], const Lane&, int u, bool live, const lds_u8* xa,
