@@ -201,19 +201,22 @@ qg_status quant_gemm(const void* w, qg_format fmt, int64_t N, int64_t K, int64_t
     if (!w || !x || !y) return QG_EINVAL;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
     StreamArgs a = stream_args(w, fmt, 1, 0, N, K);
-    if (fmt == QG_NVFP4 && M >= kMfmaMinRows) {
-        if (M > INT32_MAX) return QG_ESHAPE;
-        return launch_mfma_nvfp4(a.w0, a.w1, a.gbytes, (int)N, (int)K, x, K, (int)M, y, N, (hipStream_t)stream) ==
-                       hipSuccess
-                   ? QG_OK
-                   : QG_EHIP;
-    }
-    if (M >= kMfmaMinRows && mfma_kquant_supported(fmt, (int)K)) {
-        if (M > INT32_MAX) return QG_ESHAPE;
-        return launch_mfma_kquant(fmt, a.w0, a.w1, (int)N, (int)K, x, K, (int)M, y, N, (hipStream_t)stream) ==
-                       hipSuccess
-                   ? QG_OK
-                   : QG_EHIP;
+    if (M >= kMfmaMinRows && (fmt == QG_NVFP4 || mfma_kquant_supported(fmt, (int)K))) {
+        // matrix-core tiles; rows in chunks that keep the grid's row-tile
+        // count within its 65,535 limit (each row's result does not depend on
+        // the other rows)
+        constexpr int64_t kChunk = (int64_t)1 << 21;
+        for (int64_t m0 = 0; m0 < M; m0 += kChunk) {
+            const int cnt = (int)(M - m0 < kChunk ? M - m0 : kChunk);
+            const uint16_t* xc = x + m0 * K;
+            float* yc = y + m0 * N;
+            const hipError_t e =
+                fmt == QG_NVFP4
+                    ? launch_mfma_nvfp4(a.w0, a.w1, a.gbytes, (int)N, (int)K, xc, K, cnt, yc, N, (hipStream_t)stream)
+                    : launch_mfma_kquant(fmt, a.w0, a.w1, (int)N, (int)K, xc, K, cnt, yc, N, (hipStream_t)stream);
+            if (e != hipSuccess) return QG_EHIP;
+        }
+        return QG_OK;
     }
     const int rows = stream_rows_per_pass(fmt, N, (int)K, (int)(M < 16 ? M : 16));
     if (rows <= 0) return QG_ESHAPE;

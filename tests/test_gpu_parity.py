@@ -216,3 +216,26 @@ def test_mfma_rows_independent_of_tiling_and_repeat(fmt, N, K):
     assert same_bits(y37, y512[:37])
     again = qg.quant_gemm(wd, fmt, N, K, 512, xd).cpu().numpy()
     assert same_bits(again, y512)
+
+
+def test_mfma_rows_past_the_grid_row_limit():
+    """More activation rows than one launch's row tiles can hold (2^21 per
+    launch): rows on both sides of the chunk boundary equal the same rows of a
+    small call bit for bit."""
+    import torch
+    fmt, N, K = qg.FP8, 64, 64
+    M = (1 << 21) + 40
+    w, _ = make_case(fmt, N, K, 1, seed=91)
+    g = torch.Generator().manual_seed(91)
+    xd = torch.randn((M, K), generator=g).to(torch.bfloat16).cuda()
+    wd = dev_bytes(w)
+    y = qg.quant_gemm(wd, fmt, N, K, M, xd)
+    for r0 in (0, (1 << 21) - 20, M - 40):
+        ys = qg.quant_gemm(wd, fmt, N, K, 40, xd[r0:r0 + 40].contiguous())
+        assert same_bits(y[r0:r0 + 40].cpu().numpy(), ys.cpu().numpy()), r0
+    # and against the oracle on the rows around the boundary
+    xs = xd[(1 << 21) - 4:(1 << 21) + 4].cpu().view(torch.int16).numpy().view(np.uint16)
+    y_ref, bound = oracle.gemm(fmt, w, N, K, xs)
+    assert_band(y[(1 << 21) - 4:(1 << 21) + 4].cpu().numpy(), y_ref, bound, "rows past the grid limit")
+    del y, xd
+    torch.cuda.empty_cache()
