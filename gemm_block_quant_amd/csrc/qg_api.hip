@@ -73,14 +73,12 @@ qg_status from_hip(hipError_t e) { return e == hipSuccess ? QG_OK : QG_EHIP; }
 
 // Workspace regions of the mixture-of-experts block (256-byte aligned offsets).
 struct MoeLayout {
-    size_t xp, gu, h, yd, gws, total;
+    size_t gu, h, yd, gws, total;
 };
 MoeLayout moe_layout(int64_t E, int64_t P, int64_t D, int64_t F) {
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     MoeLayout L;
     size_t o = 0;
-    L.xp = o;
-    o += up((size_t)P * (size_t)D * 2);  // bf16 activation row per pair
     L.gu = o;
     o += up((size_t)P * (size_t)F * 8);  // fp32 gate|up per pair
     L.h = o;
@@ -289,31 +287,30 @@ qg_status quant_moe_block(const void* w_gate_up, qg_format fmt_gate_up, const vo
         return QG_EALIGN;
     hipStream_t st = (hipStream_t)stream;
     uint8_t* ws = (uint8_t*)workspace;
-    uint16_t* xp = (uint16_t*)(ws + L.xp);
     float* gu = (float*)(ws + L.gu);
     uint16_t* h = (uint16_t*)(ws + L.h);
     float* yd = (float*)(ws + L.yd);
     int32_t* gws = (int32_t*)(ws + L.gws);
-    // 1. one activation row per (token, expert) pair
-    if (launch_moe_gather(x, xp, (int)P, (int)topk, (int)D, st) != hipSuccess) return QG_EHIP;
-    // 2. gate|up of every pair, each distinct expert's weights read once
+    // 1. gate|up of every (token, expert) pair p, reading token p / topk's
+    // activations; each distinct expert's weights read once
     StreamArgs a = stream_args(w_gate_up, fmt_gate_up, E, 0, 2 * F, D);
-    a.x = xp;
+    a.x = x;
     a.ldx = D;
+    a.xdiv = (int)topk;
     a.y = gu;
     a.ldy = 2 * F;
     if (launch_grouped(fmt_gate_up, a, idx, E, P, gws, 2 * F * a.rb0, 2 * F * a.rb1, st) != hipSuccess)
         return QG_EHIP;
-    // 3. SwiGLU, rounded to bf16
+    // 2. SwiGLU, rounded to bf16
     if (launch_moe_swiglu(gu, h, (int)P, (int)F, st) != hipSuccess) return QG_EHIP;
-    // 4. down products
+    // 3. down products
     StreamArgs b = stream_args(w_down, fmt_down, E, 0, D, F);
     b.x = h;
     b.ldx = F;
     b.y = yd;
     b.ldy = D;
     if (launch_grouped(fmt_down, b, idx, E, P, gws, D * b.rb0, D * b.rb1, st) != hipSuccess) return QG_EHIP;
-    // 5. routing-weighted sum over each token's experts
+    // 4. routing-weighted sum over each token's experts
     return from_hip(launch_moe_combine(yd, wts, y, (int)T, (int)topk, (int)D, st));
 }
 

@@ -40,14 +40,14 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
                                                            int64_t ldy) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     QG_LDS uint64_t* keys = (QG_LDS uint64_t*)smem_generic;                       // P keys
-    QG_LDS int32_t* part = (QG_LDS int32_t*)(smem_generic + (size_t)P * 8);      // kBucketThreads partial counts
-    const int tid = threadIdx.x;
+    QG_LDS int32_t* part = (QG_LDS int32_t*)(smem_generic + (size_t)P * 8);      // per-wave partial counts
+    const int tid = threadIdx.x, nt = blockDim.x;  // nt: a multiple of 64, at most kBucketThreads
     const int64_t S = ws_slots(E, M);
     int32_t* slot_expert = ws + 4;
     int32_t* slot_start = ws + 4 + S;
     int32_t* perm = ws + 5 + 2 * S;
 
-    for (int i = tid; i < P; i += kBucketThreads) {
+    for (int i = tid; i < P; i += nt) {
         uint64_t k = ~0ull;
         if (i < M) {
             const int id = ids ? ids[i] : 0;
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
     // bitonic sort, ascending
     for (int size = 2; size <= P; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < P / 2; i += kBucketThreads) {
+            for (int i = tid; i < P / 2; i += nt) {
                 const int lo = 2 * i - (i & (stride - 1));
                 const int hi = lo + stride;
                 const bool up = (lo & size) == 0;
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
         }
     }
     // heads of runs of equal valid ids -> slots (block scan over contiguous chunks)
-    const int per = (M + kBucketThreads - 1) / kBucketThreads;
+    const int per = (M + nt - 1) / nt;
     const int b0 = tid * per, b1 = min(M, b0 + per);
     int cnt = 0;
     for (int i = b0; i < b1; ++i) {
@@ -83,11 +83,20 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
         const bool head = valid && (i == 0 || (uint32_t)(keys[i - 1] >> 32) != id);
         cnt += head;
     }
-    part[tid] = cnt;
+    // exclusive scan of the counts: inclusive within each wave (shuffles),
+    // then the waves' totals in order
+    const int lane = tid & 63, wv = tid >> 6;
+    int inc = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += v;
+    }
+    if (lane == 63) part[wv] = inc;
     __syncthreads();
     if (tid == 0) {
         int run = 0;
-        for (int t = 0; t < kBucketThreads; ++t) {
+        for (int t = 0; t < nt / 64; ++t) {
             const int c = part[t];
             part[t] = run;
             run += c;
@@ -95,7 +104,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
         ws[0] = run;
     }
     __syncthreads();
-    int slot = part[tid];
+    int slot = part[wv] + inc - cnt;
     for (int i = b0; i < b1; ++i) {
         const uint64_t k = keys[i];
         const uint32_t id = (uint32_t)(k >> 32);
@@ -122,7 +131,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
     for (int i = M - 1; i >= 0; --i) {
         if ((uint32_t)(keys[i] >> 32) != 0x7fffffffu) break;
         const int row = (int)(uint32_t)keys[i];
-        for (int n = tid; n < N; n += kBucketThreads) y[(int64_t)row * ldy + n] = __builtin_nanf("");
+        for (int n = tid; n < N; n += nt) y[(int64_t)row * ldy + n] = __builtin_nanf("");
     }
 }
 
@@ -166,7 +175,8 @@ __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32
         if (p0 != r0) __syncthreads();  // every wave is done with the previous pass's activations
         const int li = DIRECT ? direct_out_slot(lane) : lane;
         const int64_t yrow = perm[p0 + (li < cnt ? li : 0)];
-        auto row_of = [&](int m) { return perm[p0 + m]; };
+        const int xdiv = a.xdiv > 1 ? a.xdiv : 1;
+        auto row_of = [&](int m) { return perm[p0 + m] / xdiv; };
         auto run = [&](auto mt_tag) {
             constexpr int MT = decltype(mt_tag)::value;
             if constexpr (DIRECT) {
@@ -290,14 +300,16 @@ hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int6
     // 1. bucketing
     int P = 1;
     while (P < M) P <<= 1;
-    const size_t lds = (size_t)P * 8 + kBucketThreads * 4;
+    // one thread per compare-exchange of the sort (P / 2), whole waves, 64..1024
+    const int nt = P / 2 < 64 ? 64 : (P / 2 > kBucketThreads ? kBucketThreads : P / 2);
+    const size_t lds = (size_t)P * 8 + (kBucketThreads / 64) * 4;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)k_bucket, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBucketThreads), lds, st, ids, (int)E, (int)M, P, ws, a.y, a.N, a.ldy);
+    hipLaunchKernelGGL(k_bucket, dim3(1), dim3(nt), lds, st, ids, (int)E, (int)M, P, ws, a.y, a.N, a.ldy);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // 2. rows per pass: room for the expected rows per distinct expert (twice the

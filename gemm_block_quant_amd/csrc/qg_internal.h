@@ -25,6 +25,7 @@ struct StreamArgs {
     float* y;            // output; row m of this pass is y + yrow[m] * ldy
     int64_t ldy;
     int M;               // activation rows in this pass (1..16)
+    int xdiv;            // grouped product: row i of the call reads activation row i / xdiv (0 or 1: i)
     int xrow[kMaxPassRows];
     int yrow[kMaxPassRows];
 };
@@ -53,7 +54,6 @@ hipError_t launch_mfma_kquant(int fmt, const uint8_t* w, const uint8_t* w1, int 
 int num_cus();
 
 // Element-wise steps of the mixture-of-experts block (qg_moe.hip).
-hipError_t launch_moe_gather(const uint16_t* x, uint16_t* xp, int P, int topk, int D, hipStream_t st);
 hipError_t launch_moe_swiglu(const float* gu, uint16_t* h, int P, int F, hipStream_t st);
 hipError_t launch_moe_combine(const float* yd, const float* wts, float* y, int T, int topk, int D, hipStream_t st);
 

@@ -1,21 +1,10 @@
 // qg_moe.hip -- the element-wise steps of the mixture-of-experts block around
-// the two grouped products: activation rows per (token, expert) pair, SwiGLU
-// to bf16, and the routing-weighted combine.  All three are HBM-bound copies
-// over a few MB; each thread moves 16 bytes or one output element.
+// the two grouped products: SwiGLU to bf16 and the routing-weighted combine.
+// Both are HBM-bound passes over a few MB; each thread produces two values or
+// one output element.
 #include "qg_internal.h"
 
 namespace qg {
-
-// xp[p, :] = x[p / topk, :] for pairs p < P; rows of D bf16 (D % 8 == 0).
-__global__ __launch_bounds__(256) void k_moe_gather(const uint16_t* __restrict__ x, uint16_t* __restrict__ xp,
-                                                    int P, int topk, int D) {
-    const int chunks = D / 8;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)P * chunks) return;
-    const int p = (int)(i / chunks), c = (int)(i % chunks);
-    const u32x4 v = ld_global128(x + (int64_t)(p / topk) * D + 8 * c);
-    *(QG_GLOBAL u32x4*)(uintptr_t)(xp + (int64_t)p * D + 8 * c) = v;
-}
 
 // fp32 -> bf16 bits, round to nearest even; NaN -> 0x7FC0; overflow -> infinity.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
@@ -51,11 +40,6 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ y
 }
 
 static unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
-
-hipError_t launch_moe_gather(const uint16_t* x, uint16_t* xp, int P, int topk, int D, hipStream_t st) {
-    hipLaunchKernelGGL(k_moe_gather, dim3(blocks_for((int64_t)P * (D / 8))), dim3(256), 0, st, x, xp, P, topk, D);
-    return hipGetLastError();
-}
 
 hipError_t launch_moe_swiglu(const float* gu, uint16_t* h, int P, int F, hipStream_t st) {
     hipLaunchKernelGGL(k_moe_swiglu, dim3(blocks_for((int64_t)P * (F / 2))), dim3(256), 0, st, gu, h, P, F);

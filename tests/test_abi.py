@@ -121,9 +121,9 @@ def test_moe_block_validation():
     moe = _raw("quant_moe_block")
     fg, fd, E, D, F, T, topk = qg.Q4_K, qg.Q6_K, 6, 512, 768, 5, 3
     wsb = qg.quant_moe_workspace_bytes(fg, fd, E, D, F, T, topk)
-    # gate|up activations, gate|up fp32, bf16 intermediate, down fp32, grouped workspace
+    # gate|up fp32, bf16 intermediate, down fp32, grouped workspace
     P = T * topk
-    assert wsb >= P * D * 2 + P * 2 * F * 4 + P * F * 2 + P * D * 4 + qg.quant_grouped_workspace_bytes(E, P)
+    assert wsb >= P * 2 * F * 4 + P * F * 2 + P * D * 4 + qg.quant_grouped_workspace_bytes(E, P)
     assert qg.quant_moe_workspace_bytes(fg, fd, E, D + 16, F, T, topk) == 0  # D not a multiple of 256
     assert qg.quant_moe_workspace_bytes(fg, 9, E, D, F, T, topk) == 0
     ws = ctypes.c_void_p(0x400000)
