@@ -309,9 +309,10 @@ qg_status quant_moe_block(const void* w_gate_up, qg_format fmt_gate_up, const vo
     b.ldx = F;
     b.y = yd;
     b.ldy = D;
-    if (launch_grouped(fmt_down, b, idx, E, P, gws, D * b.rb0, D * b.rb1, st) != hipSuccess) return QG_EHIP;
+    // (the same ids: the bucketing of step 1 is reused)
+    if (launch_grouped(fmt_down, b, idx, E, P, gws, D * b.rb0, D * b.rb1, st, false) != hipSuccess) return QG_EHIP;
     // 4. routing-weighted sum over each token's experts
-    return from_hip(launch_moe_combine(yd, wts, y, (int)T, (int)topk, (int)D, st));
+    return from_hip(launch_moe_combine(yd, wts, idx, (int)E, y, (int)T, (int)topk, (int)D, st));
 }
 
 qg_status quant_dequantize_stacked(const void* w, qg_format fmt, int64_t E, int64_t N, int64_t K, float* out,

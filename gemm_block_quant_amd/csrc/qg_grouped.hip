@@ -35,6 +35,13 @@ constexpr int kBucketThreads = 1024;
 // slot start, then M sorted rows.  S = min(E, M).
 __host__ __device__ inline int64_t ws_slots(int64_t E, int64_t M) { return E < M ? E : M; }
 
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int d) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, d, 64);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), d, 64);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// P: sort keys, a power of two >= max(M, 128); P == 128 sorts in one wave's registers.
 __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __restrict__ ids, int E, int M, int P,
                                                            int32_t* __restrict__ ws, float* __restrict__ y, int N,
                                                            int64_t ldy) {
@@ -57,20 +64,48 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
         keys[i] = k;
     }
     __syncthreads();
-    // bitonic sort, ascending
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < P / 2; i += nt) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool up = (lo & size) == 0;
-                const uint64_t a = keys[lo], b = keys[hi];
-                if ((a > b) == up) {
-                    keys[lo] = b;
-                    keys[hi] = a;
+    if (P == 128) {
+        // one wave (nt == 64): keys 2 t and 2 t + 1 in lane t's registers and
+        // the same bitonic network by lane shuffles (no barriers)
+        uint64_t k0 = keys[2 * tid], k1 = keys[2 * tid + 1];
+        for (int size = 2; size <= P; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                const bool up = ((2 * tid) & size) == 0;
+                if (stride == 1) {
+                    if ((k0 > k1) == up) {
+                        const uint64_t t = k0;
+                        k0 = k1;
+                        k1 = t;
+                    }
+                } else {
+                    // partner of position 2 t + e is 2 (t ^ d) + e, d = stride / 2
+                    const int d = stride >> 1;
+                    const uint64_t p0 = shfl_xor_u64(k0, d), p1 = shfl_xor_u64(k1, d);
+                    const bool keep_min = ((tid & d) == 0) == up;  // lower position of an ascending pair, or upper of a descending one
+                    k0 = keep_min ? (k0 < p0 ? k0 : p0) : (k0 > p0 ? k0 : p0);
+                    k1 = keep_min ? (k1 < p1 ? k1 : p1) : (k1 > p1 ? k1 : p1);
                 }
             }
-            __syncthreads();
+        }
+        keys[2 * tid] = k0;
+        keys[2 * tid + 1] = k1;
+        __syncthreads();
+    } else {
+        // bitonic sort in LDS, ascending
+        for (int size = 2; size <= P; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int i = tid; i < P / 2; i += nt) {
+                    const int lo = 2 * i - (i & (stride - 1));
+                    const int hi = lo + stride;
+                    const bool up = (lo & size) == 0;
+                    const uint64_t a = keys[lo], b = keys[hi];
+                    if ((a > b) == up) {
+                        keys[lo] = b;
+                        keys[hi] = a;
+                    }
+                }
+                __syncthreads();
+            }
         }
     }
     // heads of runs of equal valid ids -> slots (block scan over contiguous chunks)
@@ -296,9 +331,9 @@ static hipError_t grouped_mt(const StreamArgs& a, int mtmax, const int32_t* ws, 
 }
 
 hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int64_t E, int64_t M, int32_t* ws,
-                          int64_t estride0, int64_t estride1, hipStream_t st) {
+                          int64_t estride0, int64_t estride1, hipStream_t st, bool bucket) {
     // 1. bucketing
-    int P = 1;
+    int P = 128;
     while (P < M) P <<= 1;
     // one thread per compare-exchange of the sort (P / 2), whole waves, 64..1024
     const int nt = P / 2 < 64 ? 64 : (P / 2 > kBucketThreads ? kBucketThreads : P / 2);
@@ -309,9 +344,11 @@ hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int6
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(k_bucket, dim3(1), dim3(nt), lds, st, ids, (int)E, (int)M, P, ws, a.y, a.N, a.ldy);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (bucket) {
+        hipLaunchKernelGGL(k_bucket, dim3(1), dim3(nt), lds, st, ids, (int)E, (int)M, P, ws, a.y, a.N, a.ldy);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     // 2. rows per pass: room for the expected rows per distinct expert (twice the
     // mean, at least 1), as LDS allows
     const int64_t S = ws_slots(E, M);

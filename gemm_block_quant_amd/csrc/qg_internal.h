@@ -37,8 +37,10 @@ size_t stream_lds_bytes(int fmt, int K, int mt);
 // Grouped-expert product: bucketing + streaming over the distinct experts.
 constexpr int64_t kGroupedMaxRows = 16384;
 size_t grouped_workspace_bytes(int64_t E, int64_t M);
+// bucket == false: ws already holds the bucketing of these ids (an earlier call
+// on the same stream); rows with invalid ids are then left unwritten.
 hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int64_t E, int64_t M, int32_t* ws,
-                          int64_t estride0, int64_t estride1, hipStream_t st);
+                          int64_t estride0, int64_t estride1, hipStream_t st, bool bucket = true);
 
 // NVFP4 product for M >= kMfmaMinRows on the bf16 matrix cores.
 constexpr int kMfmaMinRows = 32;
@@ -55,7 +57,8 @@ int num_cus();
 
 // Element-wise steps of the mixture-of-experts block (qg_moe.hip).
 hipError_t launch_moe_swiglu(const float* gu, uint16_t* h, int P, int F, hipStream_t st);
-hipError_t launch_moe_combine(const float* yd, const float* wts, float* y, int T, int topk, int D, hipStream_t st);
+hipError_t launch_moe_combine(const float* yd, const float* wts, const int32_t* idx, int E, float* y, int T, int topk,
+                              int D, hipStream_t st);
 
 // Dequantization of rows [0, rows) to fp32.
 hipError_t launch_dequant(int fmt, const uint8_t* w, int64_t E, int64_t N, int64_t K, float* out, hipStream_t st);

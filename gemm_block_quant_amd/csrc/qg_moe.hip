@@ -28,15 +28,23 @@ __global__ __launch_bounds__(256) void k_moe_swiglu(const float* __restrict__ gu
     *(QG_GLOBAL uint32_t*)(uintptr_t)(h + (int64_t)p * F + f) = f32_to_bf16_rne(h0) | (f32_to_bf16_rne(h1) << 16);
 }
 
-// y[t, d] = sum_j wts[t, j] * yd[t * topk + j, d], j ascending, fp32 fused multiply-adds.
+// y[t, d] = sum_j wts[t, j] * yd[t * topk + j, d], j ascending, fp32 fused
+// multiply-adds; NaN for a token with an id outside [0, E) (the down product
+// does not write those pairs).
 __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ yd, const float* __restrict__ wts,
-                                                     float* __restrict__ y, int T, int topk, int D) {
+                                                     const int32_t* __restrict__ idx, int E, float* __restrict__ y,
+                                                     int T, int topk, int D) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (int64_t)T * D) return;
     const int t = (int)(i / D), d = (int)(i % D);
     float acc = 0.f;
-    for (int j = 0; j < topk; ++j) acc = fmaf(wts[(int64_t)t * topk + j], yd[((int64_t)t * topk + j) * D + d], acc);
-    y[i] = acc;
+    bool bad = false;
+    for (int j = 0; j < topk; ++j) {
+        const int e = idx[(int64_t)t * topk + j];
+        bad |= e < 0 || e >= E;
+        acc = fmaf(wts[(int64_t)t * topk + j], yd[((int64_t)t * topk + j) * D + d], acc);
+    }
+    y[i] = bad ? __builtin_nanf("") : acc;
 }
 
 static unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
@@ -46,8 +54,10 @@ hipError_t launch_moe_swiglu(const float* gu, uint16_t* h, int P, int F, hipStre
     return hipGetLastError();
 }
 
-hipError_t launch_moe_combine(const float* yd, const float* wts, float* y, int T, int topk, int D, hipStream_t st) {
-    hipLaunchKernelGGL(k_moe_combine, dim3(blocks_for((int64_t)T * D)), dim3(256), 0, st, yd, wts, y, T, topk, D);
+hipError_t launch_moe_combine(const float* yd, const float* wts, const int32_t* idx, int E, float* y, int T, int topk,
+                              int D, hipStream_t st) {
+    hipLaunchKernelGGL(k_moe_combine, dim3(blocks_for((int64_t)T * D)), dim3(256), 0, st, yd, wts, idx, E, y, T, topk,
+                       D);
     return hipGetLastError();
 }
 
