@@ -200,6 +200,7 @@ qg_status quant_gemm(const void* w, qg_format fmt, int64_t N, int64_t K, int64_t
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
     StreamArgs a = stream_args(w, fmt, 1, 0, N, K);
     if (M >= kMfmaMinRows && (fmt == QG_NVFP4 || mfma_kquant_supported(fmt, (int)K))) {
+        const bool tile = mfma_kquant_supported(fmt, (int)K);  // NVFP4 with K % 64 != 0: its own kernel
         // matrix-core tiles; rows in chunks that keep the grid's row-tile
         // count within its 65,535 limit (each row's result does not depend on
         // the other rows)
@@ -209,9 +210,9 @@ qg_status quant_gemm(const void* w, qg_format fmt, int64_t N, int64_t K, int64_t
             const uint16_t* xc = x + m0 * K;
             float* yc = y + m0 * N;
             const hipError_t e =
-                fmt == QG_NVFP4
-                    ? launch_mfma_nvfp4(a.w0, a.w1, a.gbytes, (int)N, (int)K, xc, K, cnt, yc, N, (hipStream_t)stream)
-                    : launch_mfma_kquant(fmt, a.w0, a.w1, (int)N, (int)K, xc, K, cnt, yc, N, (hipStream_t)stream);
+                !tile ? launch_mfma_nvfp4(a.w0, a.w1, a.gbytes, (int)N, (int)K, xc, K, cnt, yc, N, (hipStream_t)stream)
+                      : launch_mfma_kquant(fmt, a.w0, a.w1, a.gbytes, (int)N, (int)K, xc, K, cnt, yc, N,
+                                           (hipStream_t)stream);
             if (e != hipSuccess) return QG_EHIP;
         }
         return QG_OK;

@@ -50,9 +50,10 @@ hipError_t launch_mfma_nvfp4(const uint8_t* codes, const uint8_t* scales, const 
 // cores (codes as exact bf16, sub-block scales and offsets in fp32), for the
 // formats and K that mfma_kquant_supported accepts.
 bool mfma_kquant_supported(int fmt, int K);
-// w1: the row scales of QG_FP8 (unused otherwise).
-hipError_t launch_mfma_kquant(int fmt, const uint8_t* w, const uint8_t* w1, int N, int K, const uint16_t* x,
-                              int64_t ldx, int M, float* y, int64_t ldy, hipStream_t st);
+// w1: the row scales of QG_FP8, the scale plane of QG_NVFP4; gbytes: the NVFP4
+// tensor scale (unused otherwise).
+hipError_t launch_mfma_kquant(int fmt, const uint8_t* w, const uint8_t* w1, const uint8_t* gbytes, int N, int K,
+                              const uint16_t* x, int64_t ldx, int M, float* y, int64_t ldy, hipStream_t st);
 int num_cus();
 
 // Element-wise steps of the mixture-of-experts block (qg_moe.hip).

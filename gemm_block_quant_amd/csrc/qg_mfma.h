@@ -20,6 +20,32 @@ constexpr int kMfmaKStep = 64;
 constexpr int kMfmaRowBytes = 144;  // one tile row: 64 bf16 (128 B) + 16 B padding (conflict-free fragment reads)
 constexpr int kMfmaThreads = 256;
 
+__device__ __forceinline__ uint32_t bf16_pair_from_exact(float lo, float hi) {
+    // lo, hi are exact in bf16: their top 16 bits are the bf16 encodings.
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+}
+
+// 16 NVFP4 values (8 code bytes c0, c1; E4M3 scale s) -> 8 dwords of bf16
+// pairs bf16(e2m1 * s), value order k = 0..15.
+__device__ __forceinline__ void decode_nvfp4_block_bf16(uint32_t c0, uint32_t c1, float s, uint32_t (&o)[8]) {
+    auto pair = [&](uint32_t c, int sel) -> uint32_t {
+        f32x2 v;
+        switch (sel) {
+            case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0); break;
+            case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1); break;
+            case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2); break;
+            default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3); break;
+        }
+        const float lo = v.x * s, hi = v.y * s;
+        return bf16_pair_from_exact(lo, hi);
+    };
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        o[b] = pair(c0, b);
+        o[4 + b] = pair(c1, b);
+    }
+}
+
 // f(std::integral_constant<int, i>{}) for i = 0 .. N-1, unrolled.
 template <int N, int I = 0, class Fn>
 __device__ __forceinline__ void static_for(Fn&& f) {

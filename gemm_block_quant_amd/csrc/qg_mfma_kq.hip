@@ -30,18 +30,15 @@ namespace qg {
 struct KqArgs {
     const uint16_t* x;  // bf16 [M, K], row stride ldx
     int64_t ldx;
-    const uint8_t* w;   // packed rows
-    const uint8_t* w1;  // FP8: fp32 row scales
-    int64_t rb;         // bytes per weight row
+    const uint8_t* w;      // packed rows (NVFP4: the code plane)
+    const uint8_t* w1;     // FP8: fp32 row scales; NVFP4: the E4M3 scale plane
+    const uint8_t* gbytes; // NVFP4: the fp32 tensor scale (any alignment)
+    int64_t rb;            // bytes per weight row
+    int64_t rb1;           // NVFP4: scale bytes per row
     float* y;          // fp32 [M, N], row stride ldy
     int64_t ldy;
     int M, N, K;
 };
-
-// bf16 pair from the upper halves of two exactly representable fp32 values.
-__device__ __forceinline__ uint32_t bf16_pair_exact(float lo, float hi) {
-    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
-}
 
 // Per-format pieces.  Each provides:
 //   SUB            values per sub-block (32 or 16); a step holds 64 / SUB
@@ -49,7 +46,8 @@ __device__ __forceinline__ uint32_t bf16_pair_exact(float lo, float hi) {
 //   Ring           registers one thread holds for one step
 //   x_step(s)      offset of step s's first activation (uniform)
 //   x_chunk(q)     offset of the step's 8-value chunk q (tile columns 8q..8q+7)
-//   load(wrow, s, part)               this thread's share of row wrow for step s
+//   load(wrow, wrow1, s, part)        this thread's share of row wrow (wrow1: the
+//                                     row in the second plane, NVFP4) for step s
 //   decode(r, s, part, trow, srow)    tile values of the share into the LDS row
 //                                     trow, (s, t) of the row's sub-blocks into srow
 template <int F> struct KqFmt;
@@ -67,7 +65,7 @@ template <int BB, int CODES, int HIGH> struct KqFmtK4 {
     };
     __device__ static int x_step(int s) { return 64 * s; }
     __device__ static int x_chunk(int q) { return 8 * q; }
-    __device__ static Ring load(const uint8_t* wrow, int s, int part) {
+    __device__ static Ring load(const uint8_t* wrow, const uint8_t*, int s, int part) {
         const uint8_t* blk = wrow + (size_t)(s >> 2) * BB;
         Ring r;
         r.hdr = ld_global128(blk);
@@ -126,7 +124,7 @@ template <> struct KqFmt<QG_Q8_0> {
     };
     __device__ static int x_step(int s) { return 64 * s; }
     __device__ static int x_chunk(int q) { return 8 * q; }
-    __device__ static Ring load(const uint8_t* wrow, int s, int part) {
+    __device__ static Ring load(const uint8_t* wrow, const uint8_t*, int s, int part) {
         const uint8_t* blk = wrow + (size_t)(2 * s + (part >> 1)) * 34;
         Ring r;
         r.q = ld_global128_a2(blk + 2 + 16 * (part & 1));
@@ -141,8 +139,8 @@ template <> struct KqFmt<QG_Q8_0> {
         uint32_t o[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            o[2 * e] = bf16_pair_exact((float)(w[e] & 0xFFu), (float)((w[e] >> 8) & 0xFFu));
-            o[2 * e + 1] = bf16_pair_exact((float)((w[e] >> 16) & 0xFFu), (float)(w[e] >> 24));
+            o[2 * e] = bf16_pair_from_exact((float)(w[e] & 0xFFu), (float)((w[e] >> 8) & 0xFFu));
+            o[2 * e + 1] = bf16_pair_from_exact((float)((w[e] >> 16) & 0xFFu), (float)(w[e] >> 24));
         }
         *(lds_u32x4*)(trow + 32 * part) = u32x4{o[0], o[1], o[2], o[3]};
         *(lds_u32x4*)(trow + 32 * part + 16) = u32x4{o[4], o[5], o[6], o[7]};
@@ -172,7 +170,7 @@ template <> struct KqFmt<QG_Q6_K> {
     };
     __device__ static int x_step(int s) { return 256 * (s >> 2) + 128 * ((s >> 1) & 1) + 16 * (s & 1); }
     __device__ static int x_chunk(int q) { return 32 * (q >> 1) + 8 * (q & 1); }
-    __device__ static Ring load(const uint8_t* wrow, int s, int part) {
+    __device__ static Ring load(const uint8_t* wrow, const uint8_t*, int s, int part) {
         const uint8_t* blk = wrow + (size_t)(s >> 2) * 210;
         const int n = (s >> 1) & 1, l = 16 * (s & 1) + 4 * part;
         Ring r;
@@ -212,8 +210,12 @@ template <> struct KqFmt<QG_FP8> {
     };
     __device__ static int x_step(int s) { return 64 * s; }
     __device__ static int x_chunk(int q) { return 8 * q; }
-    __device__ static Ring load(const uint8_t* wrow, int s, int part) {
+    __device__ static Ring load(const uint8_t* wrow, const uint8_t*, int s, int part) {
         return Ring{ld_global128(wrow + 64 * (size_t)s + 16 * part)};
+    }
+    // the row's scale multiplies the finished sums
+    __device__ static float out_scale(const KqArgs& a, int n) {
+        return *(const QG_GLOBAL float*)(uintptr_t)(a.w1 + 4 * (size_t)n);
     }
     __device__ static void decode(const Ring& r, int, int part, lds_u8* trow, lds_f32*) {
         const uint32_t c0 = r.q.x, c1 = r.q.y, c2 = r.q.z, c3 = r.q.w;
@@ -221,6 +223,39 @@ template <> struct KqFmt<QG_FP8> {
                                                 e4m3x2_to_bf16x2<0>(c1), e4m3x2_to_bf16x2<1>(c1)};
         *(lds_u32x4*)(trow + 32 * part + 16) = u32x4{e4m3x2_to_bf16x2<0>(c2), e4m3x2_to_bf16x2<1>(c2),
                                                      e4m3x2_to_bf16x2<0>(c3), e4m3x2_to_bf16x2<1>(c3)};
+    }
+};
+
+// NVFP4 (K a multiple of 64): step s is blocks 4s .. 4s + 3 of the row; part p
+// decodes block 4s + p (8 code bytes, one E4M3 scale) to bf16(e2m1 * scale),
+// exact (at most 6 significant bits).  The tensor scale g multiplies the
+// finished sums.
+template <> struct KqFmt<QG_NVFP4> {
+    static constexpr int SUB = 64;
+    static constexpr bool ROWSCALE = true;
+    struct Ring {
+        u32x2 q;      // 16 codes
+        uint32_t sc;  // the scale bytes of blocks 4s .. 4s + 3
+    };
+    __device__ static int x_step(int s) { return 64 * s; }
+    __device__ static int x_chunk(int q) { return 8 * q; }
+    __device__ static Ring load(const uint8_t* wrow, const uint8_t* wrow1, int s, int part) {
+        Ring r;
+        r.q = ld_global64(wrow + 32 * (size_t)s + 8 * part);
+        r.sc = *(const QG_GLOBAL uint32_t*)(uintptr_t)(wrow1 + 4 * (size_t)s);
+        return r;
+    }
+    __device__ static void decode(const Ring& r, int, int part, lds_u8* trow, lds_f32*) {
+        uint32_t o[8];
+        decode_nvfp4_block_bf16(r.q.x, r.q.y, __builtin_amdgcn_cvt_f32_fp8(r.sc >> (8 * part), 0), o);
+        *(lds_u32x4*)(trow + 32 * part) = u32x4{o[0], o[1], o[2], o[3]};
+        *(lds_u32x4*)(trow + 32 * part + 16) = u32x4{o[4], o[5], o[6], o[7]};
+    }
+    __device__ static float out_scale(const KqArgs& a, int) {
+        const uint8_t* gb = a.gbytes;
+        const uint32_t bits = (uint32_t)gb[0] | ((uint32_t)gb[1] << 8) | ((uint32_t)gb[2] << 16) |
+                              ((uint32_t)gb[3] << 24);
+        return __builtin_bit_cast(float, bits);
     }
 };
 
@@ -263,7 +298,9 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
         const int i = tid + c * kMfmaThreads;
         xp[c] = a.x + (size_t)min(m0 + (i >> 3), M - 1) * a.ldx + Fmt::x_chunk(i & 7);
     }
-    const uint8_t* wrow = a.w + (size_t)(n0 + wrow_i < N ? n0 + wrow_i : 0) * a.rb;
+    const size_t wrow_n = (size_t)(n0 + wrow_i < N ? n0 + wrow_i : 0);
+    const uint8_t* wrow = a.w + wrow_n * a.rb;
+    const uint8_t* wrow1 = a.w1 ? a.w1 + wrow_n * a.rb1 : nullptr;
 
     // Loads without branches: a load under a branch makes the compiler wait
     // for every outstanding load.
@@ -272,7 +309,7 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
         const int k0 = Fmt::x_step(s);
 #pragma unroll
         for (int c = 0; c < XCH; ++c) xr[j][c] = ld_global128(xp[c] + k0);
-        wring[j] = Fmt::load(wrow, s, part);
+        wring[j] = Fmt::load(wrow, wrow1, s, part);
     };
     auto store = [&](int buf, int s, auto stage_tag) {
         constexpr int j = decltype(stage_tag)::value;
@@ -430,7 +467,7 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
     for (int j = 0; j < FN; ++j) {
         const int n = n0 + wn + 32 * j + (lane & 31);
         float rs = 1.f;
-        if constexpr (Fmt::ROWSCALE) rs = *(const QG_GLOBAL float*)(uintptr_t)(a.w1 + 4 * (size_t)(n < N ? n : 0));
+        if constexpr (Fmt::ROWSCALE) rs = Fmt::out_scale(a, n < N ? n : 0);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -465,20 +502,22 @@ bool mfma_kquant_supported(int fmt, int K) {
         case QG_Q5_K:
         case QG_Q6_K:                              // K is a multiple of 256
         case QG_FP8: return true;                  // K is a multiple of 64
+        case QG_NVFP4: return K % kMfmaKStep == 0;  // whole 64-value steps
         case QG_Q8_0: return K % kMfmaKStep == 0;  // whole 64-value steps
         default: return false;
     }
 }
 
-hipError_t launch_mfma_kquant(int fmt, const uint8_t* w, const uint8_t* w1, int N, int K, const uint16_t* x,
-                              int64_t ldx, int M, float* y, int64_t ldy, hipStream_t st) {
-    KqArgs a = {x, ldx, w, w1, 0, y, ldy, M, N, K};
+hipError_t launch_mfma_kquant(int fmt, const uint8_t* w, const uint8_t* w1, const uint8_t* gbytes, int N, int K,
+                              const uint16_t* x, int64_t ldx, int M, float* y, int64_t ldy, hipStream_t st) {
+    KqArgs a = {x, ldx, w, w1, gbytes, 0, 0, y, ldy, M, N, K};
     switch (fmt) {
         case QG_Q4_K: a.rb = (int64_t)(K / 256) * 144; return launch_kq<QG_Q4_K>(a, st);
         case QG_Q5_K: a.rb = (int64_t)(K / 256) * 176; return launch_kq<QG_Q5_K>(a, st);
         case QG_Q6_K: a.rb = (int64_t)(K / 256) * 210; return launch_kq<QG_Q6_K>(a, st);
         case QG_Q8_0: a.rb = (int64_t)(K / 32) * 34; return launch_kq<QG_Q8_0>(a, st);
         case QG_FP8: a.rb = K; return launch_kq<QG_FP8>(a, st);
+        case QG_NVFP4: a.rb = K / 2; a.rb1 = K / 16; return launch_kq<QG_NVFP4>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -204,7 +204,8 @@ def test_full_size_sampled(fmt, N, K, M):
 
 
 @pytest.mark.parametrize("fmt,N,K", [(qg.NVFP4, 1000, 1040), (qg.Q4_K, 4100, 768), (qg.Q5_K, 4100, 768),
-                                     (qg.Q6_K, 4100, 768), (qg.Q8_0, 4100, 768), (qg.FP8, 4100, 768)])
+                                     (qg.Q6_K, 4100, 768), (qg.Q8_0, 4100, 768), (qg.FP8, 4100, 768),
+                                     (qg.NVFP4, 4100, 768)])
 def test_mfma_rows_independent_of_tiling_and_repeat(fmt, N, K):
     """M >= 32 on the matrix cores: each output is one fixed fp32 accumulation
     over K, so the rows of a 37-row call equal those rows of a 512-row call
