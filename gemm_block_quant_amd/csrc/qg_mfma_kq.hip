@@ -260,10 +260,13 @@ template <> struct KqFmt<QG_NVFP4> {
 };
 
 // D: K steps of loads in flight in the register ring (an even number).
-template <int F, int BM, int D>
+// BN: 64, or 128 for the formats without per-sub-block terms.
+template <int F, int BM, int BN, int D>
 __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
     using Fmt = KqFmt<F>;
-    constexpr int BN = 64;
+    constexpr int TPR = kMfmaThreads / BN;  // threads per weight row (4 or 2)
+    constexpr int QPT = 4 / TPR;            // quarters of a row's step decoded per thread
+    static_assert(TPR * QPT == 4 && (BN == 64 || Fmt::ROWSCALE), "tile shape");
     constexpr int NSUB = kMfmaKStep / Fmt::SUB;  // sub-blocks per step
     constexpr int KPS = Fmt::SUB / 16;           // 32x32x16 products per sub-block
     constexpr int CPS = Fmt::SUB / 8;            // 8-value chunks per sub-block
@@ -274,7 +277,6 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
     constexpr int TILE_S = Fmt::ROWSCALE ? 0 : BN * 8 * NSUB;   // per weight row: s of each sub-block, then t
     constexpr int TILE_XS = Fmt::ROWSCALE ? 0 : NSUB * BM * 4;  // per sub-block and activation row: X
     constexpr int BUF = TILE_X + TILE_W + TILE_S + TILE_XS;
-    static_assert(BN * 4 == kMfmaThreads, "four threads per weight row");
     __shared__ __attribute__((aligned(16))) uint8_t smem_generic[2 * BUF];
     lds_u8* smem = (lds_u8*)smem_generic;
 
@@ -286,8 +288,8 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
 
     // Register ring: activation chunks and this thread's weight share.
     u32x4 xr[D][XCH];
-    typename Fmt::Ring wring[D];
-    const int wrow_i = tid >> 2, part = tid & 3;  // weight tile row and quarter decoded by this thread
+    typename Fmt::Ring wring[D][QPT];
+    const int wrow_i = tid / TPR, part0 = (tid % TPR) * QPT;  // weight tile row, first quarter decoded by this thread
 
     // Per-thread row pointers, fixed for the whole K loop.  Rows past M or N
     // read row M - 1 or row 0 instead: such rows feed only outputs that are
@@ -309,7 +311,8 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
         const int k0 = Fmt::x_step(s);
 #pragma unroll
         for (int c = 0; c < XCH; ++c) xr[j][c] = ld_global128(xp[c] + k0);
-        wring[j] = Fmt::load(wrow, wrow1, s, part);
+#pragma unroll
+        for (int q = 0; q < QPT; ++q) wring[j][q] = Fmt::load(wrow, wrow1, s, part0 + q);
     };
     auto store = [&](int buf, int s, auto stage_tag) {
         constexpr int j = decltype(stage_tag)::value;
@@ -335,7 +338,9 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
             if constexpr (CPS == 4) p += __builtin_amdgcn_update_dpp(0.f, p, kDppQuadXor2, 0xF, 0xF, false);
             if ((q & (CPS - 1)) == 0) txs[(q / CPS) * BM + r] = p;
         }
-        Fmt::decode(wring[j], s, part, tw + wrow_i * kMfmaRowBytes, ts + wrow_i * 2 * NSUB);
+#pragma unroll
+        for (int q = 0; q < QPT; ++q)
+            Fmt::decode(wring[j][q], s, part0 + q, tw + wrow_i * kMfmaRowBytes, ts + wrow_i * 2 * NSUB);
     };
 
     // One fp32 accumulator per fragment takes both terms: t * X from the
@@ -479,19 +484,23 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
     }
 }
 
-// Tile shape: 128 x 64 when its tile count covers every CU, else 64 x 64.
-// (A 128 x 128 tile needs more than the 256 registers per lane that keep the
-// matrix-core results in VGPRs.)
+// Tile shape: the largest whose tile count still gives every CU work: 128 x
+// 128 (formats without per-sub-block terms, two tiles per CU), 128 x 64, else
+// 64 x 64.  (With per-sub-block terms a 128 x 128 tile needs more than the 256
+// registers per lane that keep the matrix-core results in VGPRs.)
 template <int F>
 static hipError_t launch_kq(const KqArgs& a, hipStream_t st) {
     const long cus = num_cus();
-    const long tiles = (long)((a.N + 63) / 64) * ((a.M + 127) / 128);
-    if (tiles >= cus) {
+    auto tiles = [&](int bm, int bn) { return (long)((a.N + bn - 1) / bn) * ((a.M + bm - 1) / bm); };
+    if (KqFmt<F>::ROWSCALE && tiles(128, 128) >= 2 * cus) {
+        dim3 grid((a.N + 127) / 128, (a.M + 127) / 128);
+        hipLaunchKernelGGL((k_mfma_kq<F, 128, KqFmt<F>::ROWSCALE ? 128 : 64, 2>), grid, dim3(kMfmaThreads), 0, st, a);
+    } else if (tiles(128, 64) >= cus) {
         dim3 grid((a.N + 63) / 64, (a.M + 127) / 128);
-        hipLaunchKernelGGL((k_mfma_kq<F, 128, 2>), grid, dim3(kMfmaThreads), 0, st, a);
+        hipLaunchKernelGGL((k_mfma_kq<F, 128, 64, 2>), grid, dim3(kMfmaThreads), 0, st, a);
     } else {
         dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
-        hipLaunchKernelGGL((k_mfma_kq<F, 64, 4>), grid, dim3(kMfmaThreads), 0, st, a);
+        hipLaunchKernelGGL((k_mfma_kq<F, 64, 64, 4>), grid, dim3(kMfmaThreads), 0, st, a);
     }
     return hipGetLastError();
 }
