@@ -53,23 +53,53 @@ __device__ __forceinline__ f32x4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, 
     return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// Sum over the 16 unit slots of a lane's row (lanes l, l ^ 4, l ^ 8, ...):
-// an xor butterfly, so every lane of the row ends with the same bits.
-__device__ __forceinline__ float slot_sum(float v) {
-    auto swz = [](float x, int pattern) -> float {
-        int y;
-        switch (pattern) {
-            case 4: y = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), (4 << 10) | 0x1F); break;
-            case 8: y = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), (8 << 10) | 0x1F); break;
-            default: y = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), (16 << 10) | 0x1F); break;
+// The value of lane l ^ (4 << J) (the lane of the same row in unit slot
+// s ^ (1 << J)).
+template <int J>
+__device__ __forceinline__ float slot_xor(float x) {
+    if constexpr (J == 3) {
+        return __shfl_xor(x, 32, kWave);
+    } else {
+        return __builtin_bit_cast(float,
+                                  __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), ((4 << J) << 10) | 0x1F));
+    }
+}
+
+// Butterfly stages J.. of the sums over the 16 unit slots of a lane's row of
+// the N values c[]: while N > 1 a stage hands half of the values to the
+// partner lane (the lane whose slot has bit J clear keeps the values whose
+// index has bit 0 clear), so a stage costs N / 2 exchanges; a single value
+// is exchanged whole.  Every value is added along the same xor tree as a
+// plain butterfly (each addition has the same two operands), so the totals do
+// not depend on N.  On return c[0] holds the total of original value
+// slot % N0 (N0 the initial N).
+template <int J, int N>
+__device__ __forceinline__ float slot_stages(const float (&c)[N], int slot) {
+    if constexpr (J == 4) {
+        return c[0];
+    } else if constexpr (N == 1) {
+        const float v = c[0] + slot_xor<J>(c[0]);
+        const float n[1] = {v};
+        return slot_stages<J + 1, 1>(n, slot);
+    } else {
+        const bool hi = (slot >> J) & 1;
+        float n[N / 2];
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            const float keep = hi ? c[2 * i + 1] : c[2 * i];
+            const float send = hi ? c[2 * i] : c[2 * i + 1];
+            n[i] = keep + slot_xor<J>(send);
         }
-        return __builtin_bit_cast(float, y);
-    };
-    v += swz(v, 4);
-    v += swz(v, 8);
-    v += swz(v, 16);
-    v += __shfl_xor(v, 32, kWave);
-    return v;
+        return slot_stages<J + 1, N / 2>(n, slot);
+    }
+}
+
+// Sum over the 16 unit slots of a lane's row (lanes l, l ^ 4, l ^ 8, ...) of
+// each of the MT values v[]: lane of slot s gets the total of v[s % MT].
+template <int MT>
+__device__ __forceinline__ float slot_sum_rows(const float (&v)[MT], int slot) {
+    static_assert(MT == 1 || MT == 2 || MT == 4 || MT == 8 || MT == 16, "power of two up to 16");
+    return slot_stages<0, MT>(v, slot);
 }
 
 constexpr int kDirectRows = 4;    // weight rows per wave at a time
@@ -836,13 +866,9 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
         }
         if (last) {
             const int n = RW * (rg_base + rgl) + grp;
-            float mine = 0.f;
+            float mine = slot_sum_rows<MT>(acc, slot);
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const float tot = slot_sum(acc[m]);
-                if (slot == m) mine = tot;
-                acc[m] = 0.f;
-            }
+            for (int m = 0; m < MT; ++m) acc[m] = 0.f;
             if (S > 1) {
                 // add this segment after the ones before it, in segment order
                 // (the oldest unfinished item never waits, so this ends; the

@@ -128,7 +128,10 @@ def test_product_band(fmt, N, K, M):
 @pytest.mark.parametrize("fmt,N,K", [(qg.Q8_0, 300, 1024), (qg.Q4_K, 300, 5120), (qg.Q6_K, 300, 17408),
                                      (qg.NVFP4, 300, 5120), (qg.Q5_K, 300, 5120), (qg.FP8, 300, 5120),
                                      # tall: up to 8 rows take the whole-row-group kernel, 16 the direct one
-                                     (qg.Q4_K, 16385, 5120), (qg.NVFP4, 16387, 5120)])
+                                     (qg.Q4_K, 16385, 5120), (qg.NVFP4, 16387, 5120),
+                                     # rows in K segments whose 8 and 16 activation rows are staged in
+                                     # K phases (sums carried across phases)
+                                     (qg.Q6_K, 5120, 17408), (qg.NVFP4, 5120, 17408)])
 def test_rows_match_decode_bitwise_and_repeat(fmt, N, K):
     """Row m of M = 8 (and M = 16) equals the M = 1 result bit for bit; runs repeat."""
     M = 16
