@@ -2,6 +2,7 @@
 // Nothing here allocates device memory or synchronizes a stream.
 #include <limits.h>
 
+#include <atomic>
 #include <mutex>
 #include <unordered_map>
 
@@ -106,38 +107,71 @@ qg_status check_moe(int fmt_gu, int fmt_dn, int64_t E, int64_t D, int64_t F, int
 
 namespace qg {
 
-int num_cus() {
-    static int n = 0;
-    if (!n) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-            v = 256;
-        n = v;
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];  // CU count per device, 0 until queried
+
+int current_device() {
+    int dev = 0;
+    return hipGetDevice(&dev) == hipSuccess ? dev : 0;
+}
+
+// Launch attributes and residencies per (device, kernel): the opt-in to the
+// whole LDS is set once per kernel on each device, and residencies are cached
+// per dynamic LDS size.
+std::mutex g_fn_mu;
+std::unordered_map<uint64_t, std::unordered_map<const void*, std::unordered_map<size_t, int>>> g_fn_cache;
+
+// Looks up (creating it on first use) the residency map of fn on the current
+// device; the caller holds g_fn_mu.
+hipError_t fn_entry(const void* fn, std::unordered_map<size_t, int>** out) {
+    auto& per_dev = g_fn_cache[(uint64_t)current_device()];
+    auto it = per_dev.find(fn);
+    if (it == per_dev.end()) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        if (e != hipSuccess) return e;
+        it = per_dev.emplace(fn, std::unordered_map<size_t, int>()).first;
     }
-    return n;
+    *out = &it->second;
+    return hipSuccess;
+}
+}  // namespace
+
+int num_cus() {
+    const int dev = current_device();
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int n = g_cus[dev].load(std::memory_order_relaxed);
+        if (n > 0) return n;
+    }
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+        return 256;  // not cached: the next call asks again
+    if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+hipError_t allow_full_lds(const void* fn) {
+    std::lock_guard<std::mutex> lock(g_fn_mu);
+    std::unordered_map<size_t, int>* m = nullptr;
+    return fn_entry(fn, &m);
 }
 
 hipError_t kernel_residency(const void* fn, size_t lds, int* per_cu, int block) {
-    static std::mutex mu;
-    static std::unordered_map<const void*, std::unordered_map<size_t, int>> cache;  // per kernel, per LDS size
-    std::lock_guard<std::mutex> lock(mu);
-    auto it = cache.find(fn);
-    if (it == cache.end()) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-        if (e != hipSuccess) return e;
-        it = cache.emplace(fn, std::unordered_map<size_t, int>()).first;
-    }
-    auto jt = it->second.find(lds);
-    if (jt != it->second.end()) {
+    std::lock_guard<std::mutex> lock(g_fn_mu);
+    std::unordered_map<size_t, int>* m = nullptr;
+    hipError_t e = fn_entry(fn, &m);
+    if (e != hipSuccess) return e;
+    // a kernel is always launched with the same block size, so LDS is the key
+    auto jt = m->find(lds);
+    if (jt != m->end()) {
         *per_cu = jt->second;
         return hipSuccess;
     }
     int fit = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, fn, block, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, fn, block, lds);
     if (e != hipSuccess) return e;
     if (fit < 1) fit = 1;
-    it->second.emplace(lds, fit);
+    m->emplace(lds, fit);
     *per_cu = fit;
     return hipSuccess;
 }

@@ -338,11 +338,9 @@ hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int6
     // one thread per compare-exchange of the sort (P / 2), whole waves, 64..1024
     const int nt = P / 2 < 64 ? 64 : (P / 2 > kBucketThreads ? kBucketThreads : P / 2);
     const size_t lds = (size_t)P * 8 + (kBucketThreads / 64) * 4;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_bucket, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    {
+        hipError_t e = allow_full_lds((const void*)k_bucket);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     if (bucket) {
         hipLaunchKernelGGL(k_bucket, dim3(1), dim3(nt), lds, st, ids, (int)E, (int)M, P, ws, a.y, a.N, a.ldy);

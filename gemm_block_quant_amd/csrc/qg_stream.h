@@ -471,9 +471,12 @@ inline int segment_blocks(int fmt, int K, int cpl) {
 }
 
 // Workgroups of `block` threads with `lds` bytes of dynamic LDS that one CU holds
-// at once for kernel `fn` (at least 1).  The first call per kernel also lifts
-// the kernel's dynamic-LDS limit to 160 KB.  Cached per (kernel, lds).
+// at once for kernel `fn` on the current device (at least 1).  The first call
+// per kernel and device also lifts the kernel's dynamic-LDS limit to 160 KB.
+// Cached per (device, kernel, lds); safe to call from several threads.
 hipError_t kernel_residency(const void* fn, size_t lds, int* per_cu, int block = 256);
+// Opts kernel fn into the whole LDS on the current device (once per device).
+hipError_t allow_full_lds(const void* fn);
 
 
 }  // namespace qg
