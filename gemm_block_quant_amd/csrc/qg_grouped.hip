@@ -259,8 +259,10 @@ size_t grouped_workspace_bytes(int64_t E, int64_t M) {
     return (size_t)((ints * 4 + 15) / 16 * 16);
 }
 
-// lds: the kernel's LDS; seg_mt > 0: rows are split into K segments whose sums
-// take LDS per row group of a chunk (chunks then hold at most 16 row groups).
+// lds: the kernel's LDS; seg_mt > 0: the register-direct path, whose chunks
+// hold at most 16 row groups (many short workgroups keep the CUs evenly busy
+// over the live experts), with LDS for the K-segment sums of a chunk when
+// rows are cut into segments.
 template <class Kern>
 static hipError_t launch_grouped_one(Kern kern, size_t lds, const StreamArgs& a, const int32_t* ws, int64_t E,
                                      int64_t M, int64_t estride0, int64_t estride1, hipStream_t st,
@@ -278,7 +280,7 @@ static hipError_t launch_grouped_one(Kern kern, size_t lds, const StreamArgs& a,
     int rpc = (int)((a.N + nchunks - 1) / nchunks);
     rpc = (rpc + 3) & ~3;  // a multiple of every rows-per-wave (1, 2, 4)
     const bool split = seg_mt > 0 && a.seg_S > 1;
-    if (split && rpc > 4 * kDirectSegRgsMax) rpc = 4 * kDirectSegRgsMax;
+    if (seg_mt > 0 && rpc > 4 * kDirectSegRgsMax) rpc = 4 * kDirectSegRgsMax;
     nchunks = (a.N + rpc - 1) / rpc;
     if (split) lds += direct_seg_lds_bytes(a.seg_S, rpc / 4, seg_mt);
     hipLaunchKernelGGL(kern, dim3((unsigned)(S * nchunks)), dim3(256), lds, st, a, ws, E, M, rpc, (int)nchunks,
@@ -291,7 +293,12 @@ static hipError_t grouped_paths(StreamArgs a, const int32_t* ws, int64_t E, int6
                                 hipStream_t st) {
     if constexpr (F == QG_Q4_K || F == QG_Q5_K || F == QG_Q6_K || F == QG_NVFP4 || F == QG_FP8) {
         if (direct_eligible(F, a.K)) {
-            const Segments sg = direct_segments(F, a.N, a.K, num_cus());
+            // E = 1 splits rows exactly as the dense product does (so the two
+            // agree bit for bit); stacked experts give enough row groups to
+            // fill the CUs without cutting rows along K (8 % faster on the
+            // 288-expert layers than with one expert's split)
+            const int P = (a.K / 64 + kDirectSlots - 1) / kDirectSlots;
+            const Segments sg = E > 1 ? Segments{1, P} : direct_segments(F, a.N, a.K, num_cus());
             a.seg_S = sg.S;
             a.seg_PS = sg.PS;
             const size_t lds = direct_lds_bytes(F, MTMAX, a.K);

@@ -38,6 +38,10 @@ def test_grouped_band_and_invalid_rows(fmt, E, N, K, M):
 @pytest.mark.parametrize("fmt,K", [(qg.Q4_K, 4096), (qg.NVFP4, 5120), (qg.Q6_K, 2048), (qg.Q5_K, 2048),
                                    (qg.FP8, 2048)])
 def test_grouped_e1_is_dense_bitwise(fmt, K):
+    """E = 1 is the dense product bit for bit.  With E > 1 rows are never cut
+    into K segments, so a row equals its expert's decode GEMV bit for bit
+    wherever that dense shape is not cut either (here 16384-row experts), and
+    permuting the rows of a call permutes its outputs bit for bit."""
     N, M = 257, 11
     w = synth.weights(fmt, synth.rng(22, 0), N, K)
     x = synth.x_bf16(synth.rng(22, 1), M, K)
@@ -46,10 +50,11 @@ def test_grouped_e1_is_dense_bitwise(fmt, K):
     yg = qg.quant_grouped_gemm(wd, fmt, 1, N, K, M, xd, None).cpu().numpy()
     assert same_bits(yg, yd)
     # each row of a grouped call equals the decode GEMV of its own expert
-    E = 3
+    E, N = 3, 16384
     ws = synth.weights(fmt, synth.rng(23, 0), E * N, K, E=E)
     ids = np.array([2, 0, 2, 1, 2, 0, 1, 1, 2, 0, 2], np.int32)
-    yg = qg.quant_grouped_gemm(dev_bytes(ws), fmt, E, N, K, M, xd, _ids_dev(ids)).cpu().numpy()
+    wsd = dev_bytes(ws)
+    yg = qg.quant_grouped_gemm(wsd, fmt, E, N, K, M, xd, _ids_dev(ids)).cpu().numpy()
     for i, e in enumerate(ids):
         if fmt == qg.NVFP4:
             R = E * N
@@ -67,6 +72,9 @@ def test_grouped_e1_is_dense_bitwise(fmt, K):
             we = ws[e * eb:(e + 1) * eb]
         y1 = qg.quant_gemv(dev_bytes(we), fmt, N, K, xd[i].contiguous()).cpu().numpy()
         assert same_bits(yg[i], y1), i
+    perm = np.random.default_rng(24).permutation(M)
+    yp = qg.quant_grouped_gemm(wsd, fmt, E, N, K, M, dev_x(x[perm]), _ids_dev(ids[perm])).cpu().numpy()
+    assert same_bits(yp, yg[perm])
 
 
 @pytest.mark.parametrize("N,K", [(2048, 4096), (4096, 2048)])
