@@ -151,3 +151,21 @@ def test_moe_block_validation():
     assert moe(*args(wts=ctypes.c_void_p(0x600001))) == qg.QG_EALIGN
     assert moe(*args(x=ctypes.c_void_p(0x200008))) == qg.QG_EALIGN
     assert moe(*args(T=0, ws=None, wsb=0)) == qg.QG_OK
+
+
+def test_missing_library_raises_instead_of_falling_back():
+    """Without the built library every entry point raises: there is no CPU path."""
+    import subprocess
+    import sys
+    code = ("import gemm_block_quant_amd as qg\n"
+            "qg.LIB_PATH = '/nonexistent/libquantgemm.so'\n"
+            "try:\n"
+            "    qg.quant_packed_bytes(qg.Q4_K, 1, 4, 256)\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    print('no error')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("raised:") and "not built" in r.stdout
