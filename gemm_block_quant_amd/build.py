@@ -1,8 +1,9 @@
 """Build libquantgemm.so (HIP, gfx950) in the package directory.
 
-    python -m gemm_block_quant_amd.build
+    python -m gemm_block_quant_amd.build [-v] [--incremental]
 
-Every call compiles from source (hipcc cross-compiles without a GPU).
+Every call compiles from source (hipcc cross-compiles without a GPU).  With
+--incremental, objects newer than their source and every header are kept.
 """
 from __future__ import annotations
 
@@ -26,18 +27,27 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+def _headers():
+    root = os.path.dirname(HERE)
+    return glob.glob(os.path.join(HERE, "csrc", "*.h")) + glob.glob(os.path.join(root, "include", "*.h"))
+
+
+def build(verbose: bool = False, jobs: int = 8, incremental: bool = False) -> str:
     objs = []
     procs = []
     os.makedirs(os.path.join(HERE, "_build"), exist_ok=True)
+    newest_header = max((os.path.getmtime(h) for h in _headers()), default=0.0)
     for src in sources():
         obj = os.path.join(HERE, "_build", os.path.basename(src) + ".o")
+        objs.append(obj)
+        if incremental and os.path.exists(obj) and \
+                os.path.getmtime(obj) > max(os.path.getmtime(src), newest_header):
+            continue
         cmd = [HIPCC, "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
                "-Wno-unused-function", "-c", src, "-o", obj] + DEVICE_FLAGS
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
-        objs.append(obj)
         if len(procs) >= jobs:
             _drain(procs)
     _drain(procs)
@@ -65,4 +75,4 @@ def _drain(procs):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))

@@ -36,13 +36,21 @@ int64_t block_bytes(int fmt) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// Shape checks common to every product entry point.
+// Shape checks common to every product entry point.  K is capped at
+// kMaxK so that every LDS size and offset the kernels derive from it fits in
+// an int.
+constexpr int64_t kMaxK = (int64_t)1 << 24;
 qg_status check_shape(int fmt, int64_t E, int64_t N, int64_t K, int64_t M) {
     if (block_values(fmt) == 0) return QG_EFORMAT;
     if (E < 1 || N < 0 || M < 0 || K <= 0 || K % block_values(fmt)) return QG_ESHAPE;
-    if (N > INT_MAX / 2 || K > INT_MAX / 2 || M > INT_MAX / 2) return QG_ESHAPE;
+    if (N > INT_MAX / 2 || K > kMaxK || M > INT_MAX / 2) return QG_ESHAPE;
     if (E > 0 && N > 0 && E > (int64_t)INT_MAX / N) return QG_ESHAPE;
     return QG_OK;
+}
+
+// The grouped product stages one activation row of the whole K in LDS.
+qg_status check_grouped_k(int fmt, int64_t K) {
+    return stream_lds_bytes(fmt, (int)K, 1) <= (size_t)kLdsBytes ? QG_OK : QG_ESHAPE;
 }
 
 // Streaming-kernel arguments for matrix e of a stacked weight[E*N, K].
@@ -100,7 +108,11 @@ qg_status check_moe(int fmt_gu, int fmt_dn, int64_t E, int64_t D, int64_t F, int
     if (F > INT_MAX / 4) return QG_ESHAPE;
     qg_status s = check_shape(fmt_gu, E, 2 * F, D, T * topk);
     if (s != QG_OK) return s;
-    return check_shape(fmt_dn, E, D, F, T * topk);
+    s = check_shape(fmt_dn, E, D, F, T * topk);
+    if (s != QG_OK) return s;
+    s = check_grouped_k(fmt_gu, D);
+    if (s != QG_OK) return s;
+    return check_grouped_k(fmt_dn, F);
 }
 
 }  // namespace
@@ -285,6 +297,8 @@ qg_status quant_grouped_gemm(const void* w, qg_format fmt, int64_t E, int64_t N,
     qg_status s = check_shape(fmt, E, N, K, M);
     if (s != QG_OK) return s;
     if (M > kGroupedMaxRows) return QG_ESHAPE;
+    s = check_grouped_k(fmt, K);
+    if (s != QG_OK) return s;
     if (M == 0 || N == 0) return QG_OK;
     if (!w || !x || !y) return QG_EINVAL;
     if (!workspace || workspace_bytes < grouped_workspace_bytes(E, M)) return QG_EWORKSPACE;

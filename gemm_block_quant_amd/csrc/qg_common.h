@@ -63,13 +63,20 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t v) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, SEL != 0));
 }
 
-// bf16 pair (128 + a, 128 + b) from the byte values a, b < 128 sitting in bytes
-// i and j of v (bf16 0x43XX is 128 + XX for XX < 128).
-__device__ __forceinline__ uint32_t bias128_pair(uint32_t v, uint32_t sel) {
-    return __builtin_amdgcn_perm(0x43434343u, v, sel);
+// Exact bf16 pair of the small integers held in bytes 2 SEL and 2 SEL + 1 of
+// v, each byte an E4M3 code c of the value c * 2^-9: every byte below 16
+// (E4M3's subnormals and its first normal binade share the spacing 2^-9, so
+// byte b < 16 is b * 2^-9), and the codes 0x10 (16 * 2^-9), 0x90 (-16 * 2^-9),
+// 0x98 (-32 * 2^-9).  The conversion scales by the exponent of its scale
+// operand, 2^9, so the pair holds the integers themselves.
+template <int SEL>
+__device__ __forceinline__ uint32_t int_pair_bf16(uint32_t v) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 512.0f, SEL != 0));
 }
-constexpr uint32_t kSelB0B1 = 0x04010400u;  // [v.b0, 0x43, v.b1, 0x43]
-constexpr uint32_t kSelB2B3 = 0x04030402u;  // [v.b2, 0x43, v.b3, 0x43]
+// E4M3 codes of 16 (h - 2) * 2^-9 for h = 0..3, indexed by v_perm selectors 0..3.
+constexpr uint32_t kQ6HighCodes = 0x10009098u;
+// Each byte h (0..3) of v replaced by the E4M3 code of 16 (h - 2) * 2^-9.
+__device__ __forceinline__ uint32_t q6_high_codes(uint32_t v) { return __builtin_amdgcn_perm(0u, kQ6HighCodes, v); }
 
 // ---------------------------------------------------------------- LDS access
 

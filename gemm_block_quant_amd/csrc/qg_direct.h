@@ -110,8 +110,8 @@ template <int F> struct Direct;
 // Q4_K.  Unit u of a row = quarter g = u % 4 of super-block u / 4: code bytes
 // [32g, 32g + 32), whose low nibbles are the 32 values of sub-block 2g and
 // high nibbles the 32 values of sub-block 2g + 1.
-// sum w x = a0 (D0 - 128 X0) - dmin m0 X0 + a1 (...) with a = d * sc,
-// D = sum (128 + q) x and X = sum x over the sub-block.
+// sum w x = a0 D0 - dmin m0 X0 + a1 D1 - dmin m1 X1 with a = d * sc,
+// D = sum q x (the nibbles as exact bf16) and X = sum x over the sub-block.
 template <> struct Direct<QG_Q4_K> {
     static constexpr int UV = 64;  // activation values per unit
     static constexpr int REGS = 12;
@@ -175,8 +175,7 @@ template <> struct Direct<QG_Q4_K> {
             __builtin_amdgcn_ubfe(am, L.oam + 8, L.wa) | (__builtin_amdgcn_ubfe(z, L.off + 14, L.wb) << 4);
         const float d = f16_to_f32(r[8]), dmin = f16_to_f32(r[8] >> 16);
         const float a0 = d * (float)sc0, a1 = d * (float)sc1;
-        const float b0 = -fmaf(dmin, (float)m0, 128.f * a0);
-        const float b1 = -fmaf(dmin, (float)m1, 128.f * a1);
+        const float b0 = -(dmin * (float)m0), b1 = -(dmin * (float)m1);
 
         f32x4_t c0[MG], c1[MG];
 #pragma unroll
@@ -188,10 +187,10 @@ template <> struct Direct<QG_Q4_K> {
             // nibbles: sub-block 2g; high nibbles: sub-block 2g+1)
             const uint32_t l0 = r[2 * rp] & 0x0F0F0F0Fu, l1 = r[2 * rp + 1] & 0x0F0F0F0Fu;
             const uint32_t h0 = (r[2 * rp] >> 4) & 0x0F0F0F0Fu, h1 = (r[2 * rp + 1] >> 4) & 0x0F0F0F0Fu;
-            const uint32_t bl0 = bias128_pair(l0, kSelB0B1), bl1 = bias128_pair(l0, kSelB2B3);
-            const uint32_t bl2 = bias128_pair(l1, kSelB0B1), bl3 = bias128_pair(l1, kSelB2B3);
-            const uint32_t bh0 = bias128_pair(h0, kSelB0B1), bh1 = bias128_pair(h0, kSelB2B3);
-            const uint32_t bh2 = bias128_pair(h1, kSelB0B1), bh3 = bias128_pair(h1, kSelB2B3);
+            const uint32_t bl0 = int_pair_bf16<0>(l0), bl1 = int_pair_bf16<1>(l0);
+            const uint32_t bl2 = int_pair_bf16<0>(l1), bl3 = int_pair_bf16<1>(l1);
+            const uint32_t bh0 = int_pair_bf16<0>(h0), bh1 = int_pair_bf16<1>(h0);
+            const uint32_t bh2 = int_pair_bf16<0>(h1), bh3 = int_pair_bf16<1>(h1);
 #pragma unroll
             for (int g = 0; g < MG; ++g) {
                 const u32x4 xl = lds_ld128(xa + g * xmg_bytes + ((rp ^ rot) * 4 * 16));
@@ -227,8 +226,9 @@ template <> struct Direct<QG_Q4_K> {
 // super-block u / 4: code bytes [48 + 32g, 48 + 32g + 32) (low nibbles:
 // sub-block 2g, high: 2g + 1), the 32 fifth-bit bytes H at [16, 48) (bit 2g of
 // H[l] for the low nibble of position l, bit 2g + 1 for the high one) and the
-// 16-byte header.  The codes go to the matrix cores as exact bf16 128 + q
-// (q <= 31), with the sums of Q4_K.
+// 16-byte header.  q = lo + 16 f goes to the matrix cores as two exact parts,
+// the nibble lo and 16 f, chained into one sum per sub-block; the sums X are
+// those of Q4_K.
 template <> struct Direct<QG_Q5_K> {
     static constexpr int UV = 64;
     static constexpr int REGS = 20;
@@ -281,8 +281,7 @@ template <> struct Direct<QG_Q5_K> {
             __builtin_amdgcn_ubfe(am, L.oam + 8, L.wa) | (__builtin_amdgcn_ubfe(z, L.off + 14, L.wb) << 4);
         const float d = f16_to_f32(r[16]), dmin = f16_to_f32(r[16] >> 16);
         const float a0 = d * (float)sc0, a1 = d * (float)sc1;
-        const float b0 = -fmaf(dmin, (float)m0, 128.f * a0);
-        const float b1 = -fmaf(dmin, (float)m1, 128.f * a1);
+        const float b0 = -(dmin * (float)m0), b1 = -(dmin * (float)m1);
 
         f32x4_t c0[MG], c1[MG];
 #pragma unroll
@@ -291,25 +290,34 @@ template <> struct Direct<QG_Q5_K> {
 #pragma unroll
         for (int rp = 0; rp < 4; ++rp) {
             // values 8rp..8rp+7 of each sub-block: code dwords 2rp, 2rp+1 and the
-            // fifth-bit bytes of the same positions (H dwords 2rp, 2rp+1), moved
-            // to bit 0 of each byte for sub-block 2g and bit 1 for 2g+1
+            // fifth-bit bytes of the same positions (H dwords 2rp, 2rp+1): bit 2g
+            // (sub-block 2g) or 2g + 1 (sub-block 2g + 1) of each byte, placed
+            // as the E4M3 code 0x10 (16 * 2^-9) or 0
             const uint32_t e0 = r[8 + 2 * rp] >> LL.hsh, e1 = r[8 + 2 * rp + 1] >> LL.hsh;
-            const uint32_t l0 = (r[2 * rp] & 0x0F0F0F0Fu) | ((e0 << 4) & 0x10101010u);
-            const uint32_t l1 = (r[2 * rp + 1] & 0x0F0F0F0Fu) | ((e1 << 4) & 0x10101010u);
-            const uint32_t h0 = ((r[2 * rp] >> 4) & 0x0F0F0F0Fu) | ((e0 << 3) & 0x10101010u);
-            const uint32_t h1 = ((r[2 * rp + 1] >> 4) & 0x0F0F0F0Fu) | ((e1 << 3) & 0x10101010u);
-            const uint32_t bl0 = bias128_pair(l0, kSelB0B1), bl1 = bias128_pair(l0, kSelB2B3);
-            const uint32_t bl2 = bias128_pair(l1, kSelB0B1), bl3 = bias128_pair(l1, kSelB2B3);
-            const uint32_t bh0 = bias128_pair(h0, kSelB0B1), bh1 = bias128_pair(h0, kSelB2B3);
-            const uint32_t bh2 = bias128_pair(h1, kSelB0B1), bh3 = bias128_pair(h1, kSelB2B3);
+            const uint32_t l0 = r[2 * rp] & 0x0F0F0F0Fu, l1 = r[2 * rp + 1] & 0x0F0F0F0Fu;
+            const uint32_t h0 = (r[2 * rp] >> 4) & 0x0F0F0F0Fu, h1 = (r[2 * rp + 1] >> 4) & 0x0F0F0F0Fu;
+            const uint32_t fl0 = (e0 << 4) & 0x10101010u, fl1 = (e1 << 4) & 0x10101010u;
+            const uint32_t fh0 = (e0 << 3) & 0x10101010u, fh1 = (e1 << 3) & 0x10101010u;
+            const uint32_t bl0 = int_pair_bf16<0>(l0), bl1 = int_pair_bf16<1>(l0);
+            const uint32_t bl2 = int_pair_bf16<0>(l1), bl3 = int_pair_bf16<1>(l1);
+            const uint32_t bh0 = int_pair_bf16<0>(h0), bh1 = int_pair_bf16<1>(h0);
+            const uint32_t bh2 = int_pair_bf16<0>(h1), bh3 = int_pair_bf16<1>(h1);
+            const uint32_t gl0 = int_pair_bf16<0>(fl0), gl1 = int_pair_bf16<1>(fl0);
+            const uint32_t gl2 = int_pair_bf16<0>(fl1), gl3 = int_pair_bf16<1>(fl1);
+            const uint32_t gh0 = int_pair_bf16<0>(fh0), gh1 = int_pair_bf16<1>(fh0);
+            const uint32_t gh2 = int_pair_bf16<0>(fh1), gh3 = int_pair_bf16<1>(fh1);
 #pragma unroll
             for (int g = 0; g < MG; ++g) {
                 const u32x4 xl = lds_ld128(xa + g * xmg_bytes + ((rp ^ rot) * 4 * 16));
                 const u32x4 xh = lds_ld128(xa + g * xmg_bytes + (((4 + rp) ^ rot) * 4 * 16));
                 c0[g] = mfma4(xl.x, xl.y, bl0, bl1, c0[g]);
                 c1[g] = mfma4(xh.x, xh.y, bh0, bh1, c1[g]);
+                c0[g] = mfma4(xl.x, xl.y, gl0, gl1, c0[g]);
+                c1[g] = mfma4(xh.x, xh.y, gh0, gh1, c1[g]);
                 c0[g] = mfma4(xl.z, xl.w, bl2, bl3, c0[g]);
                 c1[g] = mfma4(xh.z, xh.w, bh2, bh3, c1[g]);
+                c0[g] = mfma4(xl.z, xl.w, gl2, gl3, c0[g]);
+                c1[g] = mfma4(xh.z, xh.w, gh2, gh3, c1[g]);
             }
         }
         if (live) {
@@ -478,11 +486,13 @@ template <> struct Direct<QG_FP8> {
 // ql[64h + 32 + 16t ..] (p = 1, 3), 2-bit high parts qh[32h + 16t ..], the 8
 // sub-scales of the half and d.  Blocks are 210 bytes, so these loads are
 // only 2-byte aligned.
-// w = d s (q - 32)  ->  sum w x = d s (D - 160 X) with D = sum (128 + q) x.
+// w = d s (q - 32)  ->  sum w x = d s D with D = sum (q - 32) x, formed as
+// sum lo x + sum 16 (hi - 2) x (lo the low nibble, hi the 2-bit high part,
+// both exact bf16) in one fp32 chain.
 template <> struct Direct<QG_Q6_K> {
     static constexpr int UV = 64;
     static constexpr int REGS = 15;
-    static constexpr bool SUMS = true;
+    static constexpr bool SUMS = false;
     struct Lane {
         uint32_t tsh;  // 8 * t: selects the part's sub-scales
     };
@@ -529,20 +539,25 @@ template <> struct Direct<QG_Q6_K> {
         const int rot = u & 3;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            // values 4i..4i+3 of each of the 4 groups: 6-bit codes in bytes
+            // values 4i..4i+3 of each of the 4 groups: low nibbles and the
+            // 2-bit high parts, one byte per value
             const uint32_t A = r[i], B = r[4 + i], H = r[8 + i];
-            const uint32_t v[4] = {(A & 0x0F0F0F0Fu) | ((H << 4) & 0x30303030u),
-                                   (B & 0x0F0F0F0Fu) | ((H << 2) & 0x30303030u),
-                                   ((A >> 4) & 0x0F0F0F0Fu) | (H & 0x30303030u),
-                                   ((B >> 4) & 0x0F0F0F0Fu) | ((H >> 2) & 0x30303030u)};
+            const uint32_t lo[4] = {A & 0x0F0F0F0Fu, B & 0x0F0F0F0Fu, (A >> 4) & 0x0F0F0F0Fu,
+                                    (B >> 4) & 0x0F0F0F0Fu};
+            const uint32_t hi[4] = {H & 0x03030303u, (H >> 2) & 0x03030303u, (H >> 4) & 0x03030303u,
+                                    (H >> 6) & 0x03030303u};
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const uint32_t b0 = bias128_pair(v[p], kSelB0B1), b1 = bias128_pair(v[p], kSelB2B3);
+                const uint32_t b0 = int_pair_bf16<0>(lo[p]), b1 = int_pair_bf16<1>(lo[p]);
+                const uint32_t hc = q6_high_codes(hi[p]);
+                const uint32_t e0 = int_pair_bf16<0>(hc), e1 = int_pair_bf16<1>(hc);
 #pragma unroll
                 for (int g = 0; g < MG; ++g) {
                     // position group 2p + i/2 holds values 8(i/2)..8(i/2)+7 of group p
                     const u32x4 xv = lds_ld128(xa + g * xmg_bytes + (((2 * p + (i >> 1)) ^ rot) * 4 * 16));
-                    c[p][g] = (i & 1) ? mfma4(xv.z, xv.w, b0, b1, c[p][g]) : mfma4(xv.x, xv.y, b0, b1, c[p][g]);
+                    const uint32_t x0 = (i & 1) ? xv.z : xv.x, x1 = (i & 1) ? xv.w : xv.y;
+                    c[p][g] = mfma4(x0, x1, b0, b1, c[p][g]);
+                    c[p][g] = mfma4(x0, x1, e0, e1, c[p][g]);
                 }
             }
         }
@@ -558,15 +573,9 @@ template <> struct Direct<QG_Q6_K> {
             for (int g = 0; g < MG; ++g) {
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const f32x4_t sx = *(const QG_LDS f32x4_t*)(xs + (size_t)g * xs_mg + (4 * u + p) * 4);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        if (4 * g + i < MT) {
-                            float t = acc[4 * g + i];
-                            t = fmaf(a[p], c[p][g][i], t);
-                            t = fmaf(-160.f * a[p], sx[i], t);
-                            acc[4 * g + i] = t;
-                        }
+                        if (4 * g + i < MT) acc[4 * g + i] = fmaf(a[p], c[p][g][i], acc[4 * g + i]);
                     }
                 }
             }
@@ -585,11 +594,9 @@ template <> struct Direct<QG_Q6_K> {
 __host__ __device__ constexpr int direct_uv(int) { return 64; }
 __host__ __device__ constexpr int direct_mg(int mt) { return (mt + 3) / 4; }
 __host__ __device__ constexpr int direct_units(int K) { return K / 64; }
-// Activation sub-blocks (one scale, one sum) per unit: Q4_K and Q5_K 2 x 32 values,
-// Q6_K 4 x 16 values; NVFP4 needs no sums.
-__host__ __device__ constexpr int direct_sub(int fmt) {
-    return fmt == QG_Q4_K || fmt == QG_Q5_K ? 2 : fmt == QG_Q6_K ? 4 : 0;
-}
+// Activation sums per unit (the sub-blocks whose mins need sum x): Q4_K and
+// Q5_K 2 x 32 values; the other formats need none.
+__host__ __device__ constexpr int direct_sub(int fmt) { return fmt == QG_Q4_K || fmt == QG_Q5_K ? 2 : 0; }
 // Bytes of one unit for one group of 4 activation rows.
 __host__ __device__ constexpr int direct_unit_bytes(int) { return 8 * 4 * 16; }
 // Bytes of one group of 4 activation rows (all units).
@@ -622,7 +629,7 @@ __host__ __device__ constexpr int direct_x_offset(int fmt, int K, int m, int k) 
 // weight loads can be issued in between: issue() loads up to XV 16-byte
 // vectors per thread into registers, commit() writes them (and any vectors
 // beyond XV per thread, loaded and written on the spot) to LDS, then, for
-// Q4_K, computes the per-32-value sums (sequential order).  Rows >= cnt are
+// Q4_K and Q5_K, computes the per-32-value sums (sequential order).  Rows >= cnt are
 // zero.  commit() ends with a workgroup barrier.
 template <int F, int MT, int XV>
 struct XStage {
@@ -874,13 +881,19 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
                 // (the oldest unfinished item never waits, so this ends; the
                 // bound only guarantees that every wave exits)
                 QG_LDS int* prog = sl.progress + rgl;
+                bool in_order = false;
                 for (int spin = 0; spin < (1 << 22); ++spin) {
-                    if (__hip_atomic_load(prog, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == s) break;
+                    if (__hip_atomic_load(prog, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == s) {
+                        in_order = true;
+                        break;
+                    }
                     __builtin_amdgcn_s_sleep(1);
                 }
                 lds_f32* tp = sl.total + (size_t)(rgl * RW + grp) * sl.mtmax + (slot < MT ? slot : 0);
                 if (slot < MT) {
-                    const float sum = s == 0 ? mine : *tp + mine;
+                    // a wait that gave up would add out of order: the row's
+                    // result is poisoned instead of silently reordered
+                    const float sum = !in_order ? __builtin_nanf("") : s == 0 ? mine : *tp + mine;
                     *tp = sum;
                     mine = sum;
                 }

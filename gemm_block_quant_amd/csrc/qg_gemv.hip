@@ -44,10 +44,8 @@ template <int F, int MT, int CPL, int CPLS, int PF>
 __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8* smem = (lds_u8*)smem_generic;
-    constexpr bool kSums = (F == QG_Q4_K || F == QG_Q6_K);
     const int K = a.K;
     lds_u8* xl = smem;
-    lds_f32* xs = (lds_f32*)(smem + (size_t)MT * K * 2);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     lds_u8* rowbuf = smem + rowbuf_offset(MT, K) + (size_t)wid * rowbuf_bytes(CPL, CPLS);
     lds_u8* rowbuf_s = rowbuf + CPL * 1024 + 32;
@@ -56,9 +54,9 @@ __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
     const int gw = blockIdx.x * kWavesPerBlock + wid;
     MatView mv = {a.w0, a.rb0, a.w1, a.rb1, a.gbytes};
     const int64_t yrow = a.yrow[lane < a.M ? lane : 0];
-    auto stage = [&] { stage_x<MT, kSums>(xl, xs, a.x, a.ldx, a.M, K, [&](int m) { return a.xrow[m]; }); };
-    wave_stream<F, MT, CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf, rowbuf_s, gw, GW, a.N, a.y,
-                                      a.ldy, yrow, a.M, stage);
+    auto stage = [&] { stage_x<MT>(xl, a.x, a.ldx, a.M, K, [&](int m) { return a.xrow[m]; }); };
+    wave_stream<F, MT, CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, rowbuf, rowbuf_s, gw, GW, a.N, a.y, a.ldy,
+                                      yrow, a.M, stage);
 }
 
 // Direct path: one 16-wave workgroup per CU.  Workgroup b owns an equal

@@ -179,7 +179,6 @@ __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32
                                                  int64_t estride1) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8* smem = (lds_u8*)smem_generic;
-    constexpr bool kSums = F == QG_Q4_K || F == QG_Q5_K || F == QG_Q6_K;
     const int K = a.K;
     const int slot = blockIdx.x / nchunks, chunk = blockIdx.x % nchunks;
     const int nslots = ws[0];
@@ -240,9 +239,9 @@ __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32
                 wave_stream_direct<F, MT, SP, PF, true>(mv, n_end, K, xl, xs, next_item, rg0, sg, ph, sl, a.y, a.ldy,
                                                   yrow, cnt, between);
             } else {
-                auto stage = [&] { stage_x<MT, kSums>(xl, xs, a.x, a.ldx, cnt, K, row_of); };
-                wave_stream<F, MT, CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, xs, rowbuf, rowbuf_s,
-                                                  n_begin + wid, kWavesPerBlock, n_end, a.y, a.ldy, yrow, cnt, stage);
+                auto stage = [&] { stage_x<MT>(xl, a.x, a.ldx, cnt, K, row_of); };
+                wave_stream<F, MT, CPL, CPLS, PF>(mv, K, a.seg_blocks, a.nseg, xl, rowbuf, rowbuf_s, n_begin + wid,
+                                                  kWavesPerBlock, n_end, a.y, a.ldy, yrow, cnt, stage);
             }
         };
         if (cnt <= 1 || MTMAX == 1) run(std::integral_constant<int, 1>{});

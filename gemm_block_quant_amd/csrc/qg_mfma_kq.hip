@@ -1,28 +1,35 @@
-// qg_mfma_kq.hip -- Q4_K, Q5_K, Q6_K, Q8_0 and row-scaled FP8 products for
-// M >= 32 activation rows on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
+// qg_mfma_kq.hip -- Q4_K, Q5_K, Q6_K, Q8_0, NVFP4 and row-scaled FP8 products
+// for M >= 32 activation rows on the bf16 matrix cores
+// (v_mfma_f32_32x32x16_bf16).
 //
 // Prefill must read each packed weight slab once for all rows rather than once
 // per few rows ("Qwen3.8-27B on one Tenstorrent P150", section "3. Porting the
 // 9B stack to 27B geometry": re-streaming the weights per 32 rows was the
-// prefill bug).  A dequantized weight of these formats is not exact in bf16,
-// but inside one sub-block it is an affine function of an integer code that
-// is: w = s * v + t with v exact in bf16 and s, t fp32 per weight row and
-// sub-block.  The tile holds v, the matrix cores form D = sum v x over the
-// sub-block in fp32, and the scale and offset enter in fp32 afterwards:
+// prefill bug).  A dequantized weight of the K-quant formats is not exact in
+// bf16, but its integer code is: inside one sub-block w = s * v + t with v an
+// integer that bf16 holds exactly and s, t fp32 per weight row and sub-block.
+// The tile holds v, the matrix cores form D = sum v x over the sub-block in
+// fp32, and the scale and the min enter in fp32 afterwards:
 //   sum_k w x = s * D + t * X,   X = sum of the sub-block's activations.
-//   Q4_K, Q5_K (32 values): v = 128 + q, s = d sc, t = -(128 s + dmin m)
-//   Q6_K (16 values):       v = 128 + q, s = d sc, t = -160 s   (w = s (q - 32))
-//   Q8_0 (32 values):       v = q + 128 (the code as an unsigned byte),
-//                           s = d, t = -128 d
-// (the factorisation of the decode path, applied per 32 x 32 output block).
-// Row-scaled FP8 needs none of it: v = e4m3 (exact in bf16) over all of K, the
-// products accumulate in place and the row's scale multiplies the result.
+//   Q4_K (32 values): v = q (0..15),            s = d sc, t = -dmin m
+//   Q5_K (32 values): v = lo + 16 f (two planes: lo and 16 f), s, t as Q4_K
+//   Q6_K (16 values): v = q - 32 = lo + 16 (hi - 2) (two planes), s = d sc, t = 0
+//   Q8_0 (32 values): v = q (int8),             s = d, t = 0
+// The codes enter with their own value, never with an offset, so a zero-point
+// code contributes exactly zero and each sum's rounding error stays relative
+// to sum |v x|.  Where v needs more than one exact bf16 part, the parts sit in
+// two tile planes whose products with the same activations chain into one
+// fp32 sum.
+// NVFP4 and row-scaled FP8 need none of it: v = e2m1 * e4m3 or e4m3 (exact in
+// bf16) over all of K, the products accumulate in place and the tensor or row
+// scale multiplies the result.
 //
-// Tiling: a 256-thread workgroup computes a BM x 64 tile of y, four waves own
-// (BM/2) x 32 quarters as 32x32 accumulators.  A K step is 64 values staged in
-// one of two LDS buffers: activations, their sub-block sums per row, the tile
-// values v, and per weight row (s, t) of each sub-block.  Four threads decode
-// each weight row.  The loads of the next steps run in a register ring.
+// Tiling: a 256-thread workgroup computes a BM x BN tile of y, four waves own
+// (BM/2) x (BN/2) quarters as 32x32 accumulators.  A K step is 64 values staged
+// in one of two LDS buffers: activations, their sub-block sums per row (formats
+// with mins), the tile values v, and per weight row the s (and t) of each
+// sub-block.  Four threads decode each weight row.  The loads of the next steps
+// run in a register ring.
 #include "qg_mfma.h"
 
 namespace qg {
@@ -42,22 +49,30 @@ struct KqArgs {
 
 // Per-format pieces.  Each provides:
 //   SUB            values per sub-block (32 or 16); a step holds 64 / SUB
-//   ROWSCALE       no per-sub-block terms: one scale per weight row (FP8)
+//   ROWSCALE       no per-sub-block terms: one scale per weight row (FP8) or
+//                  per matrix (NVFP4), applied to the finished sums
+//   PLANES         tile planes of exact parts of v (1 or 2)
+//   MINS           the sub-blocks carry a min term t * X
 //   Ring           registers one thread holds for one step
 //   x_step(s)      offset of step s's first activation (uniform)
 //   x_chunk(q)     offset of the step's 8-value chunk q (tile columns 8q..8q+7)
 //   load(wrow, wrow1, s, part)        this thread's share of row wrow (wrow1: the
 //                                     row in the second plane, NVFP4) for step s
-//   decode(r, s, part, trow, srow)    tile values of the share into the LDS row
-//                                     trow, (s, t) of the row's sub-blocks into srow
+//   decode(r, s, part, trow, plane, srow)
+//                  tile values of the share into the LDS row trow (the second
+//                  plane's row plane bytes further on), the s (then t) of the
+//                  row's sub-blocks into srow
 template <int F> struct KqFmt;
 
 // Q4_K / Q5_K: step s is quarter g = s & 3 of super-block s >> 2: sub-blocks
 // 2g (low nibbles of code bytes 32g..32g+31) and 2g + 1 (high nibbles).  Part
 // p decodes code bytes 8p..8p+7 of the quarter: positions 8p..8p+7 of both.
+// Q5_K puts 16 f (f the fifth bit) in the second plane.
 template <int BB, int CODES, int HIGH> struct KqFmtK4 {
     static constexpr int SUB = 32;
     static constexpr bool ROWSCALE = false;
+    static constexpr int PLANES = HIGH >= 0 ? 2 : 1;
+    static constexpr bool MINS = true;
     struct Ring {
         u32x4 hdr;  // d, dmin, 12 scale bytes
         u32x2 q;    // 8 code bytes
@@ -73,22 +88,25 @@ template <int BB, int CODES, int HIGH> struct KqFmtK4 {
         if constexpr (HIGH >= 0) r.f = ld_global64(blk + HIGH + 8 * part);
         return r;
     }
-    __device__ static void decode(const Ring& r, int s, int part, lds_u8* trow, lds_f32* srow) {
+    __device__ static void decode(const Ring& r, int s, int part, lds_u8* trow, int plane, lds_f32* srow) {
         const int g = s & 3;
-        uint32_t l0 = r.q.x & 0x0F0F0F0Fu, l1 = r.q.y & 0x0F0F0F0Fu;
-        uint32_t h0 = (r.q.x >> 4) & 0x0F0F0F0Fu, h1 = (r.q.y >> 4) & 0x0F0F0F0Fu;
+        const uint32_t l0 = r.q.x & 0x0F0F0F0Fu, l1 = r.q.y & 0x0F0F0F0Fu;
+        const uint32_t h0 = (r.q.x >> 4) & 0x0F0F0F0Fu, h1 = (r.q.y >> 4) & 0x0F0F0F0Fu;
+        *(lds_u32x4*)(trow + 16 * part) =
+            u32x4{int_pair_bf16<0>(l0), int_pair_bf16<1>(l0), int_pair_bf16<0>(l1), int_pair_bf16<1>(l1)};
+        *(lds_u32x4*)(trow + 64 + 16 * part) =
+            u32x4{int_pair_bf16<0>(h0), int_pair_bf16<1>(h0), int_pair_bf16<0>(h1), int_pair_bf16<1>(h1)};
         if constexpr (HIGH >= 0) {
-            // fifth bit of sub-block 2g + t at bit 2g + t of each H byte
+            // fifth bit of sub-block 2g + t at bit 2g + t of each H byte, as the
+            // E4M3 code 0x10 (16 * 2^-9) or 0
             const uint32_t f0 = r.f.x >> (2 * g), f1 = r.f.y >> (2 * g);
-            l0 |= (f0 << 4) & 0x10101010u;
-            l1 |= (f1 << 4) & 0x10101010u;
-            h0 |= (f0 << 3) & 0x10101010u;
-            h1 |= (f1 << 3) & 0x10101010u;
+            const uint32_t fl0 = (f0 << 4) & 0x10101010u, fl1 = (f1 << 4) & 0x10101010u;
+            const uint32_t fh0 = (f0 << 3) & 0x10101010u, fh1 = (f1 << 3) & 0x10101010u;
+            *(lds_u32x4*)(trow + plane + 16 * part) = u32x4{int_pair_bf16<0>(fl0), int_pair_bf16<1>(fl0),
+                                                            int_pair_bf16<0>(fl1), int_pair_bf16<1>(fl1)};
+            *(lds_u32x4*)(trow + plane + 64 + 16 * part) = u32x4{int_pair_bf16<0>(fh0), int_pair_bf16<1>(fh0),
+                                                                 int_pair_bf16<0>(fh1), int_pair_bf16<1>(fh1)};
         }
-        *(lds_u32x4*)(trow + 16 * part) = u32x4{bias128_pair(l0, kSelB0B1), bias128_pair(l0, kSelB2B3),
-                                                bias128_pair(l1, kSelB0B1), bias128_pair(l1, kSelB2B3)};
-        *(lds_u32x4*)(trow + 64 + 16 * part) = u32x4{bias128_pair(h0, kSelB0B1), bias128_pair(h0, kSelB2B3),
-                                                     bias128_pair(h1, kSelB0B1), bias128_pair(h1, kSelB2B3)};
         if (part < 2) {
             // 6-bit scale and min of sub-block jb = 2g + part (packing over
             // S[0..3], S[4..7], S[8..11]: jb < 4 whole in S[jb], S[jb + 4];
@@ -104,9 +122,8 @@ template <int BB, int CODES, int HIGH> struct KqFmtK4 {
                 m = __builtin_amdgcn_ubfe(S2, o + 4, 4) | (__builtin_amdgcn_ubfe(S1, o + 6, 2) << 4);
             }
             const float d = f16_to_f32(r.hdr.x), dmin = f16_to_f32(r.hdr.x >> 16);
-            const float sv = d * (float)sc;
-            srow[part] = sv;
-            srow[2 + part] = -fmaf(dmin, (float)m, 128.f * sv);
+            srow[part] = d * (float)sc;
+            srow[2 + part] = -(dmin * (float)m);
         }
     }
 };
@@ -118,6 +135,8 @@ template <> struct KqFmt<QG_Q5_K> : KqFmtK4<176, 48, 16> {};  // fifth bits at [
 template <> struct KqFmt<QG_Q8_0> {
     static constexpr int SUB = 32;
     static constexpr bool ROWSCALE = false;
+    static constexpr int PLANES = 1;
+    static constexpr bool MINS = false;
     struct Ring {
         u32x4 q;     // 16 codes
         uint32_t d;  // fp16 d of the block
@@ -131,24 +150,23 @@ template <> struct KqFmt<QG_Q8_0> {
         r.d = ld_global16(blk);
         return r;
     }
-    __device__ static void decode(const Ring& r, int s, int part, lds_u8* trow, lds_f32* srow) {
-        // v = q + 128: the code with its sign bit flipped, read unsigned (0..255, exact in bf16)
-        const uint32_t w0 = r.q.x ^ 0x80808080u, w1 = r.q.y ^ 0x80808080u, w2 = r.q.z ^ 0x80808080u,
-                       w3 = r.q.w ^ 0x80808080u;
-        const uint32_t w[4] = {w0, w1, w2, w3};
+    __device__ static void decode(const Ring& r, int, int part, lds_u8* trow, int, lds_f32* srow) {
+        // the signed codes, exact in bf16: (q + 128) - 128 with q + 128 the code
+        // byte with its sign bit flipped, read unsigned.  (A sign-extending
+        // bit-field extract converted to float was compiled into an unsigned
+        // conversion of the sign-extended byte, which turns -1 into 2^32 - 1.)
+        const uint32_t w[4] = {r.q.x ^ 0x80808080u, r.q.y ^ 0x80808080u, r.q.z ^ 0x80808080u,
+                               r.q.w ^ 0x80808080u};
         uint32_t o[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            o[2 * e] = bf16_pair_from_exact((float)(w[e] & 0xFFu), (float)((w[e] >> 8) & 0xFFu));
-            o[2 * e + 1] = bf16_pair_from_exact((float)((w[e] >> 16) & 0xFFu), (float)(w[e] >> 24));
+            o[2 * e] = bf16_pair_from_exact((float)(w[e] & 0xFFu) - 128.f, (float)((w[e] >> 8) & 0xFFu) - 128.f);
+            o[2 * e + 1] =
+                bf16_pair_from_exact((float)((w[e] >> 16) & 0xFFu) - 128.f, (float)(w[e] >> 24) - 128.f);
         }
         *(lds_u32x4*)(trow + 32 * part) = u32x4{o[0], o[1], o[2], o[3]};
         *(lds_u32x4*)(trow + 32 * part + 16) = u32x4{o[4], o[5], o[6], o[7]};
-        if ((part & 1) == 0) {
-            const float d = f16_to_f32(r.d);
-            srow[part >> 1] = d;
-            srow[2 + (part >> 1)] = -128.f * d;
-        }
+        if ((part & 1) == 0) srow[part >> 1] = f16_to_f32(r.d);
     }
 };
 
@@ -159,10 +177,13 @@ template <> struct KqFmt<QG_Q8_0> {
 // n = (s >> 1) & 1 and l in [16 h, 16 h + 16), h = s & 1: its 64 values are
 // four sub-blocks of 16 (tile columns 16 j .. 16 j + 15 hold quadrant j), and
 // every code byte of the super-block is read by exactly one step.  Part p
-// decodes l = 16 h + 4 p .. + 3 of the four quadrants.
+// decodes l = 16 h + 4 p .. + 3 of the four quadrants: the low nibbles into
+// the first plane, 16 (hi - 2) into the second.
 template <> struct KqFmt<QG_Q6_K> {
     static constexpr int SUB = 16;
     static constexpr bool ROWSCALE = false;
+    static constexpr int PLANES = 2;
+    static constexpr bool MINS = false;
     struct Ring {
         uint32_t qa, qb, qh;  // low-bit bytes (quadrants 0/2, 1/3) and high-bit bytes of 4 positions
         u32x2 sc;             // scales 8n .. 8n + 7
@@ -181,22 +202,21 @@ template <> struct KqFmt<QG_Q6_K> {
         r.d = ld_global16(blk + 208);
         return r;
     }
-    __device__ static void decode(const Ring& r, int s, int part, lds_u8* trow, lds_f32* srow) {
-        const uint32_t q0 = (r.qa & 0x0F0F0F0Fu) | ((r.qh << 4) & 0x30303030u);
-        const uint32_t q1 = (r.qb & 0x0F0F0F0Fu) | ((r.qh << 2) & 0x30303030u);
-        const uint32_t q2 = ((r.qa >> 4) & 0x0F0F0F0Fu) | (r.qh & 0x30303030u);
-        const uint32_t q3 = ((r.qb >> 4) & 0x0F0F0F0Fu) | ((r.qh >> 2) & 0x30303030u);
-        *(lds_u32x2*)(trow + 8 * part) = u32x2{bias128_pair(q0, kSelB0B1), bias128_pair(q0, kSelB2B3)};
-        *(lds_u32x2*)(trow + 32 + 8 * part) = u32x2{bias128_pair(q1, kSelB0B1), bias128_pair(q1, kSelB2B3)};
-        *(lds_u32x2*)(trow + 64 + 8 * part) = u32x2{bias128_pair(q2, kSelB0B1), bias128_pair(q2, kSelB2B3)};
-        *(lds_u32x2*)(trow + 96 + 8 * part) = u32x2{bias128_pair(q3, kSelB0B1), bias128_pair(q3, kSelB2B3)};
-        // this part writes (s, t) of quadrant j = part: scale byte 2 part + h of sc
+    __device__ static void decode(const Ring& r, int s, int part, lds_u8* trow, int plane, lds_f32* srow) {
+        const uint32_t lo[4] = {r.qa & 0x0F0F0F0Fu, r.qb & 0x0F0F0F0Fu, (r.qa >> 4) & 0x0F0F0F0Fu,
+                                (r.qb >> 4) & 0x0F0F0F0Fu};
+        const uint32_t hi[4] = {q6_high_codes(r.qh & 0x03030303u), q6_high_codes((r.qh >> 2) & 0x03030303u),
+                                q6_high_codes((r.qh >> 4) & 0x03030303u), q6_high_codes((r.qh >> 6) & 0x03030303u)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            *(lds_u32x2*)(trow + 32 * j + 8 * part) = u32x2{int_pair_bf16<0>(lo[j]), int_pair_bf16<1>(lo[j])};
+            *(lds_u32x2*)(trow + plane + 32 * j + 8 * part) = u32x2{int_pair_bf16<0>(hi[j]), int_pair_bf16<1>(hi[j])};
+        }
+        // this part writes s of quadrant j = part: scale byte 2 part + h of sc
         const int idx = 2 * part + (s & 1);
         const uint32_t word = (idx >> 2) ? r.sc.y : r.sc.x;
         const int sc = __builtin_amdgcn_sbfe((int)word, 8 * (idx & 3), 8);
-        const float c = f16_to_f32(r.d) * (float)sc;
-        srow[part] = c;
-        srow[4 + part] = -160.f * c;
+        srow[part] = f16_to_f32(r.d) * (float)sc;
     }
 };
 
@@ -205,6 +225,8 @@ template <> struct KqFmt<QG_Q6_K> {
 template <> struct KqFmt<QG_FP8> {
     static constexpr int SUB = 64;
     static constexpr bool ROWSCALE = true;
+    static constexpr int PLANES = 1;
+    static constexpr bool MINS = false;
     struct Ring {
         u32x4 q;  // 16 codes
     };
@@ -217,7 +239,7 @@ template <> struct KqFmt<QG_FP8> {
     __device__ static float out_scale(const KqArgs& a, int n) {
         return *(const QG_GLOBAL float*)(uintptr_t)(a.w1 + 4 * (size_t)n);
     }
-    __device__ static void decode(const Ring& r, int, int part, lds_u8* trow, lds_f32*) {
+    __device__ static void decode(const Ring& r, int, int part, lds_u8* trow, int, lds_f32*) {
         const uint32_t c0 = r.q.x, c1 = r.q.y, c2 = r.q.z, c3 = r.q.w;
         *(lds_u32x4*)(trow + 32 * part) = u32x4{e4m3x2_to_bf16x2<0>(c0), e4m3x2_to_bf16x2<1>(c0),
                                                 e4m3x2_to_bf16x2<0>(c1), e4m3x2_to_bf16x2<1>(c1)};
@@ -233,6 +255,8 @@ template <> struct KqFmt<QG_FP8> {
 template <> struct KqFmt<QG_NVFP4> {
     static constexpr int SUB = 64;
     static constexpr bool ROWSCALE = true;
+    static constexpr int PLANES = 1;
+    static constexpr bool MINS = false;
     struct Ring {
         u32x2 q;      // 16 codes
         uint32_t sc;  // the scale bytes of blocks 4s .. 4s + 3
@@ -245,7 +269,7 @@ template <> struct KqFmt<QG_NVFP4> {
         r.sc = *(const QG_GLOBAL uint32_t*)(uintptr_t)(wrow1 + 4 * (size_t)s);
         return r;
     }
-    __device__ static void decode(const Ring& r, int, int part, lds_u8* trow, lds_f32*) {
+    __device__ static void decode(const Ring& r, int, int part, lds_u8* trow, int, lds_f32*) {
         uint32_t o[8];
         decode_nvfp4_block_bf16(r.q.x, r.q.y, __builtin_amdgcn_cvt_f32_fp8(r.sc >> (8 * part), 0), o);
         *(lds_u32x4*)(trow + 32 * part) = u32x4{o[0], o[1], o[2], o[3]};
@@ -272,10 +296,12 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
     constexpr int CPS = Fmt::SUB / 8;            // 8-value chunks per sub-block
     constexpr int FM = BM / 64, FN = BN / 64;    // 32x32 fragments per wave
     constexpr int XCH = BM * 8 / kMfmaThreads;   // 16-byte activation chunks per thread per step
-    constexpr int TILE_X = BM * kMfmaRowBytes;   // activations (bf16, padded rows)
-    constexpr int TILE_W = BN * kMfmaRowBytes;   // tile values v (bf16)
-    constexpr int TILE_S = Fmt::ROWSCALE ? 0 : BN * 8 * NSUB;   // per weight row: s of each sub-block, then t
-    constexpr int TILE_XS = Fmt::ROWSCALE ? 0 : NSUB * BM * 4;  // per sub-block and activation row: X
+    constexpr int SROW = Fmt::ROWSCALE ? 0 : NSUB * (Fmt::MINS ? 2 : 1);  // floats per weight row: s, then t
+    constexpr int PLANE = BN * kMfmaRowBytes;     // bytes of one tile plane
+    constexpr int TILE_X = BM * kMfmaRowBytes;    // activations (bf16, padded rows)
+    constexpr int TILE_W = Fmt::PLANES * PLANE;   // tile values v (bf16), one or two planes
+    constexpr int TILE_S = BN * 4 * SROW;         // per weight row: s of each sub-block, then t
+    constexpr int TILE_XS = Fmt::MINS ? NSUB * BM * 4 : 0;  // per sub-block and activation row: X
     constexpr int BUF = TILE_X + TILE_W + TILE_S + TILE_XS;
     __shared__ __attribute__((aligned(16))) uint8_t smem_generic[2 * BUF];
     lds_u8* smem = (lds_u8*)smem_generic;
@@ -325,7 +351,7 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
             const int i = tid + c * kMfmaThreads;
             const int r = i >> 3, q = i & 7;
             *(lds_u32x4*)(tx + r * kMfmaRowBytes + q * 16) = xr[j][c];
-            if constexpr (Fmt::ROWSCALE) continue;
+            if constexpr (!Fmt::MINS) continue;
             // sum of this chunk's 8 values (pairs dotted with (1, 1)), then over
             // the chunks of the sub-block: lanes xor 1 (and xor 2) of a quad
             // (element copies first: a bit cast of a vector element reads element 0)
@@ -340,11 +366,11 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
         }
 #pragma unroll
         for (int q = 0; q < QPT; ++q)
-            Fmt::decode(wring[j][q], s, part0 + q, tw + wrow_i * kMfmaRowBytes, ts + wrow_i * 2 * NSUB);
+            Fmt::decode(wring[j][q], s, part0 + q, tw + wrow_i * kMfmaRowBytes, PLANE, ts + wrow_i * SROW);
     };
 
     // One fp32 accumulator per fragment takes both terms: t * X from the
-    // matrix cores, s * D from the vector unit.  (At most 256 registers per
+    // matrix cores (formats with mins), s * D from the vector unit.  (At most 256 registers per
     // lane, two waves per SIMD: the compiler then keeps matrix-core results in
     // ordinary VGPRs, which the vector unit can read without copies.)
     f32x16 acc[FM][FN];
@@ -380,30 +406,33 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
             }
             return;
         }
-        // t * X of two sub-blocks per 32x32x2 fp32 product:
-        // A[m][k] = X(row m, sub-block 2p + k), lane l holds m = l % 32, k = l / 32;
-        // B[k][n] = t(row n, sub-block 2p + k), same lane mapping.
+        if constexpr (Fmt::MINS) {
+            // t * X of two sub-blocks per 32x32x2 fp32 product:
+            // A[m][k] = X(row m, sub-block 2p + k), lane l holds m = l % 32, k = l / 32;
+            // B[k][n] = t(row n, sub-block 2p + k), same lane mapping.
 #pragma unroll
-        for (int pp = 0; pp < NSUB / 2; ++pp) {
-            float xa[FM], tb[FN];
+            for (int pp = 0; pp < NSUB / 2; ++pp) {
+                float xa[FM], tb[FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) xa[i] = txs[(2 * pp + half) * BM + wm + 32 * i + frow];
+                for (int i = 0; i < FM; ++i) xa[i] = txs[(2 * pp + half) * BM + wm + 32 * i + frow];
 #pragma unroll
-            for (int j = 0; j < FN; ++j) tb[j] = ts[(wn + 32 * j + frow) * 2 * NSUB + NSUB + 2 * pp + half];
+                for (int j = 0; j < FN; ++j) tb[j] = ts[(wn + 32 * j + frow) * SROW + NSUB + 2 * pp + half];
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa[i], tb[j], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa[i], tb[j], acc[i][j], 0, 0, 0);
+            }
         }
         float sv[FN][NSUB];
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int sb = 0; sb < NSUB; ++sb) sv[j][sb] = ts[(wn + 32 * j + frow) * 2 * NSUB + sb];
+            for (int sb = 0; sb < NSUB; ++sb) sv[j][sb] = ts[(wn + 32 * j + frow) * SROW + sb];
+        constexpr int PL = Fmt::PLANES;
 #pragma unroll
         for (int sb = 0; sb < NSUB; ++sb) {
-            bf16x8_t fa[FM][KPS], fb[FN][KPS];
+            bf16x8_t fa[FM][KPS], fb[FN][PL][KPS];
 #pragma unroll
             for (int h = 0; h < KPS; ++h) {
                 const int kk = KPS * sb + h;
@@ -413,18 +442,25 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
                         bf16x8_t, lds_ld128(tx + (wm + 32 * i + frow) * kMfmaRowBytes + kk * 32 + fcol));
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    fb[j][h] = __builtin_bit_cast(
-                        bf16x8_t, lds_ld128(tw + (wn + 32 * j + frow) * kMfmaRowBytes + kk * 32 + fcol));
+#pragma unroll
+                    for (int pl = 0; pl < PL; ++pl)
+                        fb[j][pl][h] = __builtin_bit_cast(
+                            bf16x8_t,
+                            lds_ld128(tw + pl * PLANE + (wn + 32 * j + frow) * kMfmaRowBytes + kk * 32 + fcol));
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    // D = sum v x over the sub-block, then acc += s * D
-                    f32x16 dsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][0], fb[j][0], f32x16{}, 0, 0, 0);
+                    // D = sum v x over the sub-block (the planes' products chained
+                    // in one fp32 sum), then acc += s * D
+                    f32x16 dsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][0], fb[j][0][0], f32x16{}, 0, 0, 0);
 #pragma unroll
-                    for (int h = 1; h < KPS; ++h)
-                        dsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][h], fb[j][h], dsum, 0, 0, 0);
+                    for (int pl = 0; pl < PL; ++pl)
+#pragma unroll
+                        for (int h = 0; h < KPS; ++h)
+                            if (pl > 0 || h > 0)
+                                dsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][h], fb[j][pl][h], dsum, 0, 0, 0);
                     const float s = sv[j][sb];
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(s, dsum[r], acc[i][j][r]);

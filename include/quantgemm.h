@@ -31,8 +31,8 @@
  *  - Weight reads are whole aligned 16-byte granules: the last granule of a
  *    weight plane may be read past the plane's final byte (never past the
  *    granule, so never onto another page); those bytes are not used.
- *  - Shapes: N, M, E >= 0; K > 0 and a multiple of the format's block
- *    (QG_ESHAPE otherwise).  M == 0 or N == 0 is a valid no-op.
+ *  - Shapes: N, M, E >= 0; 0 < K <= 2^24 and a multiple of the format's
+ *    block (QG_ESHAPE otherwise).  M == 0 or N == 0 is a valid no-op.
  *
  * Packed layouts (all multi-byte fields little endian; rows contiguous, row r
  * of weight[R, K] holding K / QK blocks in K order):
@@ -68,9 +68,17 @@
  *  quant_packed_bytes() is the single source of truth for buffer sizes.
  *
  * Numerics: the dequantized weights of quant_dequantize are bit-exact fp32
- * (one rounding at most, round to nearest even).  Products accumulate in fp32
- * in a fixed order: results are deterministic run to run, row m of any
- * quant_gemm call with M <= 16 is bitwise equal to quant_gemv on x[m], and
+ * (one rounding at most, round to nearest even).  The products take each
+ * block's integer codes at their own value (never shifted by a constant that
+ * is subtracted again later), so a row whose weights are all zero gives
+ * exactly 0, and apply the block scales and mins in fp32 to per-block sums.
+ * The FP8 row scale and the NVFP4 tensor scale multiply finished fp32 sums,
+ * which matches summing the fp32 weights of quant_dequantize (to fp32
+ * rounding) while every product e4m3 * s, or e2m1 * e4m3 * g, lies in fp32's
+ * normal range: FP8 row scales in [2^-117, 2^119], NVFP4 g in [2^-116, 2^115].
+ * Products accumulate in fp32 in a fixed order: results are deterministic run
+ * to run, row m of any quant_gemm call with M <= 16 is bitwise equal to
+ * quant_gemv on x[m], and
  * such a call is bitwise equal to quant_grouped_gemm with E = 1 and ids =
  * NULL.  Calls with M >= 32 that run on the matrix cores (below) accumulate
  * in another (still fixed) order: their rows do not depend on M or on the
@@ -142,7 +150,10 @@ size_t quant_grouped_workspace_bytes(int64_t E, int64_t M);
  * element of that row of y is set to NaN.
  * workspace: device scratch of at least quant_grouped_workspace_bytes(E, M)
  * bytes, contents undefined between calls; calls sharing a workspace must be
- * ordered on one stream.  Limits: M <= 16384 (QG_ESHAPE beyond). */
+ * ordered on one stream.  Limits (QG_ESHAPE beyond, before anything is
+ * launched): M <= 16384; one activation row of K values must fit in the 160 KB
+ * of LDS with the kernel's other state: K <= 19200 for Q4_K and Q5_K, 20224
+ * for Q6_K, 20416 for NVFP4 and FP8 with K % 64 == 0. */
 qg_status quant_grouped_gemm(const void* w, qg_format fmt, int64_t E, int64_t N, int64_t K, int64_t M,
                              const uint16_t* x, const int32_t* ids, float* y, void* workspace,
                              size_t workspace_bytes, void* stream);
@@ -173,7 +184,8 @@ size_t quant_moe_workspace_bytes(qg_format fmt_gate_up, qg_format fmt_down, int6
  * workspace: device scratch of at least quant_moe_workspace_bytes(...) bytes,
  * contents undefined between calls; calls sharing it must be ordered on one
  * stream.  Limits: T * topk <= 16384; D and F multiples of the formats'
- * blocks (QG_ESHAPE otherwise).  T == 0 is a valid no-op.
+ * blocks and within quant_grouped_gemm's K limits (QG_ESHAPE otherwise).
+ * T == 0 is a valid no-op.
  * Alignment: w_gate_up, w_down, x, workspace 16 bytes; idx, wts, y 4 bytes. */
 qg_status quant_moe_block(const void* w_gate_up, qg_format fmt_gate_up, const void* w_down, qg_format fmt_down,
                           int64_t E, int64_t D, int64_t F, int64_t T, int64_t topk, const uint16_t* x,

@@ -79,6 +79,9 @@ def test_validation_rejects_before_launch():
     assert gemm(ctypes.c_void_p(0x100008), qg.Q4_K, 4, 256, 1, FAKE_X, FAKE_Y, None) == qg.QG_EALIGN
     assert gemm(FAKE_W, qg.Q4_K, 4, 256, 1, ctypes.c_void_p(0x200004), FAKE_Y, None) == qg.QG_EALIGN
     assert gemm(FAKE_W, qg.Q4_K, 4, 256, 1, FAKE_X, ctypes.c_void_p(0x300002), None) == qg.QG_EALIGN
+    # K above 2^24: the kernels' LDS arithmetic is int (rejected before any launch)
+    assert gemm(FAKE_W, qg.FP8, 4, (1 << 24) + 64, 1, FAKE_X, FAKE_Y, None) == qg.QG_ESHAPE
+    assert gemm(FAKE_W, qg.NVFP4, 4, 1 << 29, 1, FAKE_X, FAKE_Y, None) == qg.QG_ESHAPE
     gemv = _raw("quant_gemv")
     assert gemv(FAKE_W, qg.Q8_0, 4, 48, FAKE_X, FAKE_Y, None) == qg.QG_ESHAPE
     deq = _raw("quant_dequantize")
@@ -115,6 +118,24 @@ def test_grouped_validation():
     assert grouped(*args(ids=ctypes.c_void_p(0x500002))) == qg.QG_EALIGN
     assert grouped(*args(M=0, ws=None, wsb=0)) == qg.QG_OK
     assert grouped(*args(M=20000)) == qg.QG_ESHAPE
+
+
+def test_grouped_k_beyond_lds_is_rejected_before_launch():
+    """The grouped product stages a whole activation row in LDS: a K whose row
+    cannot fit is rejected with QG_ESHAPE before the bucketing is launched
+    (a launch would need a GPU; this container has none)."""
+    grouped = _raw("quant_grouped_gemm")
+    ws = ctypes.c_void_p(0x400000)
+    for fmt, K in ((qg.Q4_K, 19456), (qg.Q5_K, 19456), (qg.Q6_K, 20480), (qg.FP8, 20480), (qg.NVFP4, 20480),
+                   (qg.Q8_0, 81920)):
+        wsb = qg.quant_grouped_workspace_bytes(2, 3)
+        assert grouped(FAKE_W, fmt, 2, 8, K, 3, FAKE_X, None, FAKE_Y, ws, wsb, None) == qg.QG_ESHAPE, (fmt, K)
+    moe = _raw("quant_moe_block")
+    for D, F in ((19456, 256), (256, 19456)):
+        wsb = qg.quant_moe_workspace_bytes(qg.Q4_K, qg.Q4_K, 4, D, F, 2, 2)
+        assert wsb == 0, (D, F)
+        assert moe(FAKE_W, qg.Q4_K, ctypes.c_void_p(0x700000), qg.Q4_K, 4, D, F, 2, 2, FAKE_X,
+                   ctypes.c_void_p(0x500000), ctypes.c_void_p(0x600000), FAKE_Y, ws, 1 << 30, None) == qg.QG_ESHAPE
 
 
 def test_moe_block_validation():

@@ -78,13 +78,12 @@ def test_grouped_e1_is_dense_bitwise(fmt, K):
 
 
 @pytest.mark.parametrize("N,K", [(2048, 4096), (4096, 2048)])
-def test_grouped_moe_layer_sampled(N, K):
-    """288 stacked Q4_K experts, 16 tokens each routed to 8 distinct experts."""
+def test_grouped_moe_layer(N, K):
+    """288 stacked Q4_K experts, 16 tokens each routed to 8 distinct experts: every output."""
     E, T, topk = 288, 16, 8
     w = synth.weights(qg.Q4_K, synth.rng(5, 0 if K == 4096 else 4), E * N, K, E=E)
     x = synth.x_bf16(synth.rng(5, 1 if K == 4096 else 3), T * topk, K)
     ids = synth.routing(synth.rng(5, 2), T, topk, E)
     y = qg.quant_grouped_gemm(dev_bytes(w), qg.Q4_K, E, N, K, T * topk, dev_x(x), _ids_dev(ids)).cpu().numpy()
-    cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(1).integers(0, N, 62)]))
-    y_ref, bound = oracle.gemm(qg.Q4_K, w, N, K, x, E=E, ids=ids, cols=cols)
-    assert_band(y[:, cols], y_ref, bound, "moe N %d K %d" % (N, K))
+    y_ref, bound = oracle.gemm(qg.Q4_K, w, N, K, x, E=E, ids=ids)
+    assert_band(y, y_ref, bound, "moe N %d K %d" % (N, K))

@@ -24,10 +24,8 @@ def test_grouped_at_the_row_limit():
     x = synth.x_bf16(synth.rng(61, 1), M, K)
     ids = np.random.default_rng(61).integers(0, E, M).astype(np.int32)
     y = qg.quant_grouped_gemm(dev_bytes(w), fmt, E, N, K, M, dev_x(x), _dev(ids, np.int32)).cpu().numpy()
-    rows = np.unique(np.concatenate([np.arange(8), M - 1 - np.arange(8),
-                                     np.random.default_rng(62).integers(0, M, 200)]))
-    y_ref, bound = oracle.gemm(fmt, w, N, K, x[rows], E=E, ids=ids[rows])
-    assert_band(y[rows], y_ref, bound, "grouped M=16384")
+    y_ref, bound = oracle.gemm(fmt, w, N, K, x, E=E, ids=ids)
+    assert_band(y, y_ref, bound, "grouped M=16384")
 
 
 def test_moe_block_at_the_pair_limit():

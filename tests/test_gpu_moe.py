@@ -75,13 +75,11 @@ def test_moe_block_token_independent_of_batch():
         assert same_bits(yt[0], y[t]), t
 
 
-def test_moe_block_glm_shape_sampled():
+def test_moe_block_glm_shape():
     """D = 4096, F = 2048, 16 tokens x top-8 over 32 experts (the expert shape of
     the 288-expert layer; fewer experts keep the host copy small)."""
     fg, fd, E, D, F, T, topk = qg.Q4_K, qg.Q4_K, 32, 4096, 2048, 16, 8
     w_gu, w_dn, x, idx, wts = _case(fg, fd, E, D, F, T, topk, 42)
     y = _run(fg, w_gu, fd, w_dn, E, D, F, x, idx, wts)
-    cols = np.unique(np.concatenate([np.arange(4), D - 1 - np.arange(4),
-                                     np.random.default_rng(42).integers(0, D, 56)]))
-    y_ref, bound = oracle.moe_block(fg, w_gu, fd, w_dn, E, D, F, x, idx, wts, cols=cols)
-    assert_band(y[:, cols], y_ref, bound, "moe GLM shape")
+    y_ref, bound = oracle.moe_block(fg, w_gu, fd, w_dn, E, D, F, x, idx, wts)
+    assert_band(y, y_ref, bound, "moe GLM shape")
