@@ -8,6 +8,7 @@ in include/quantgemm.h:
     quant_gemv(w, fmt, N, K, x, y=None)                     -> y [N] fp32
     quant_gemm(w, fmt, N, K, M, x, y=None)                  -> y [M, N] fp32
     quant_grouped_gemm(w, fmt, E, N, K, M, x, ids, y=None, workspace=None) -> y [M, N]
+    quant_grouped_gemm_noalloc(w, fmt, E, N, K, M, x, ids, y=None)  -> y [M, N]
     quant_dequantize(w, fmt, rows, K, out=None)             -> out [rows, K] fp32
     quant_dequantize_stacked(w, fmt, E, N, K, out=None)     -> out [E*N, K] fp32
     quant_packed_bytes(fmt, E, N, K), quant_grouped_workspace_bytes(E, M),
@@ -58,6 +59,8 @@ def lib():
     L.quant_grouped_workspace_bytes.restype = sz
     L.quant_grouped_gemm.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     L.quant_grouped_gemm.restype = i32
+    L.quant_grouped_gemm_noalloc.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, vp]
+    L.quant_grouped_gemm_noalloc.restype = i32
     L.quant_dequantize.argtypes = [vp, i32, i64, i64, vp, vp]
     L.quant_dequantize.restype = i32
     L.quant_dequantize_stacked.argtypes = [vp, i32, i64, i64, i64, vp, vp]
@@ -176,6 +179,21 @@ def quant_grouped_gemm(w, fmt: int, E: int, N: int, K: int, M: int, x, ids=None,
                                   _dev_ptr(y, "y", 4 * M * N), _dev_ptr(workspace, "workspace"),
                                   workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "quant_grouped_gemm")
+    return y
+
+
+def quant_grouped_gemm_noalloc(w, fmt: int, E: int, N: int, K: int, M: int, x, ids=None, y=None, stream=None):
+    """quant_grouped_gemm with the library's static per-GPU scratch instead of a
+    workspace (nothing is allocated by the library; y is allocated here when
+    not given).  Calls on one GPU must be ordered on one stream."""
+    torch = _torch()
+    y = _out(y, (M, N), x.device)
+    if ids is not None and ids.dtype != torch.int32:
+        raise ValueError("ids must be int32")
+    st = lib().quant_grouped_gemm_noalloc(_dev_ptr(w, "w", quant_packed_bytes(fmt, E, N, K)), fmt, E, N, K, M,
+                                          _x_ptr(x, M, K), _dev_ptr(ids, "ids", 4 * M) if ids is not None else None,
+                                          _dev_ptr(y, "y", 4 * M * N), _stream(stream))
+    _check(st, "quant_grouped_gemm_noalloc")
     return y
 
 

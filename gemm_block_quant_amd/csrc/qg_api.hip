@@ -115,7 +115,42 @@ qg_status check_moe(int fmt_gu, int fmt_dn, int64_t E, int64_t D, int64_t F, int
     return check_grouped_k(fmt_dn, F);
 }
 
+// Validation shared by the grouped entry points (everything but the workspace).
+qg_status check_grouped(const void* w, int fmt, int64_t E, int64_t N, int64_t K, int64_t M, const uint16_t* x,
+                        const int32_t* ids, float* y) {
+    qg_status s = check_shape(fmt, E, N, K, M);
+    if (s != QG_OK) return s;
+    if (M > kGroupedMaxRows) return QG_ESHAPE;
+    s = check_grouped_k(fmt, K);
+    if (s != QG_OK) return s;
+    if (M == 0 || N == 0) return QG_OK;
+    if (!w || !x || !y) return QG_EINVAL;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4) || (ids && !aligned(ids, 4))) return QG_EALIGN;
+    return QG_OK;
+}
+
+// The grouped product of a validated call with its bucketing workspace ws.
+qg_status run_grouped(const void* w, int fmt, int64_t E, int64_t N, int64_t K, int64_t M, const uint16_t* x,
+                      const int32_t* ids, float* y, void* ws, void* stream) {
+    StreamArgs a = stream_args(w, fmt, E, 0, N, K);
+    a.x = x;
+    a.ldx = K;
+    a.y = y;
+    a.ldy = N;
+    const int64_t es0 = N * a.rb0, es1 = N * a.rb1;
+    return from_hip(launch_grouped(fmt, a, ids, E, M, (int32_t*)ws, es0, es1, (hipStream_t)stream));
+}
+
 }  // namespace
+
+// Scratch of quant_grouped_gemm_noalloc: the bucketing workspace of the
+// largest grouped call (16384 rows: (5 + 2 * 16384 + 16384) int32 = 196,628
+// bytes), one copy per GPU for the life of the process.  In host code this
+// name is only a handle for hipGetSymbolAddress: the device address of each
+// GPU's copy is resolved once per device and used everywhere else.
+static constexpr size_t kScratchBytes = 196864;
+static_assert(kScratchBytes >= ((5 + 3 * kGroupedMaxRows) * 4 + 15) / 16 * 16, "holds the largest bucketing");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace qg {
 
@@ -187,6 +222,30 @@ hipError_t kernel_residency(const void* fn, size_t lds, int* per_cu, int block) 
     *per_cu = fit;
     return hipSuccess;
 }
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch` per device (null until resolved)
+}  // namespace
+
+}  // namespace qg
+
+// Device address of the current device's copy of `scratch`, resolved on the
+// first call for that device (with the device current) and kept.
+static qg_status scratch_on_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= qg::kMaxDevices) return QG_EHIP;
+    std::lock_guard<std::mutex> lock(qg::g_scratch_mu);
+    if (!qg::g_scratch_dev[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QG_EHIP;
+        qg::g_scratch_dev[dev] = p;
+    }
+    *out = qg::g_scratch_dev[dev];
+    return QG_OK;
+}
+
+namespace qg {
 
 // Plain streaming read (measurement reference): every 16-byte granule of the
 // buffer once, non-temporal, eight loads in flight per thread, grid-stride.
@@ -294,24 +353,22 @@ size_t quant_grouped_workspace_bytes(int64_t E, int64_t M) {
 qg_status quant_grouped_gemm(const void* w, qg_format fmt, int64_t E, int64_t N, int64_t K, int64_t M,
                              const uint16_t* x, const int32_t* ids, float* y, void* workspace, size_t workspace_bytes,
                              void* stream) {
-    qg_status s = check_shape(fmt, E, N, K, M);
-    if (s != QG_OK) return s;
-    if (M > kGroupedMaxRows) return QG_ESHAPE;
-    s = check_grouped_k(fmt, K);
-    if (s != QG_OK) return s;
-    if (M == 0 || N == 0) return QG_OK;
-    if (!w || !x || !y) return QG_EINVAL;
+    qg_status s = check_grouped(w, fmt, E, N, K, M, x, ids, y);
+    if (s != QG_OK || M == 0 || N == 0) return s;
     if (!workspace || workspace_bytes < grouped_workspace_bytes(E, M)) return QG_EWORKSPACE;
-    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(workspace, 16) ||
-        (ids && !aligned(ids, 4)))
-        return QG_EALIGN;
-    StreamArgs a = stream_args(w, fmt, E, 0, N, K);
-    a.x = x;
-    a.ldx = K;
-    a.y = y;
-    a.ldy = N;
-    const int64_t es0 = N * a.rb0, es1 = N * a.rb1;
-    return from_hip(launch_grouped(fmt, a, ids, E, M, (int32_t*)workspace, es0, es1, (hipStream_t)stream));
+    if (!aligned(workspace, 16)) return QG_EALIGN;
+    return run_grouped(w, fmt, E, N, K, M, x, ids, y, workspace, stream);
+}
+
+qg_status quant_grouped_gemm_noalloc(const void* w, qg_format fmt, int64_t E, int64_t N, int64_t K, int64_t M,
+                                     const uint16_t* x, const int32_t* ids, float* y, void* stream) {
+    qg_status s = check_grouped(w, fmt, E, N, K, M, x, ids, y);
+    if (s != QG_OK || M == 0 || N == 0) return s;
+    if (grouped_workspace_bytes(E, M) > kScratchBytes) return QG_EWORKSPACE;
+    void* ws = nullptr;
+    s = scratch_on_current_device(&ws);
+    if (s != QG_OK) return s;
+    return run_grouped(w, fmt, E, N, K, M, x, ids, y, ws, stream);
 }
 
 size_t quant_moe_workspace_bytes(qg_format fmt_gate_up, qg_format fmt_down, int64_t E, int64_t D, int64_t F,

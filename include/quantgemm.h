@@ -158,6 +158,21 @@ qg_status quant_grouped_gemm(const void* w, qg_format fmt, int64_t E, int64_t N,
                              const uint16_t* x, const int32_t* ids, float* y, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* quant_grouped_gemm without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, results (bit for bit),
+ * limits and errors as quant_grouped_gemm; it allocates nothing and calls no
+ * allocating routine.  Its bucketing scratch is a static device array of
+ * 196,864 bytes inside the library (enough for the largest call, M = 16384;
+ * QG_EWORKSPACE if a call ever needed more), one copy per GPU, held until the
+ * process ends.  The first call on each device resolves that copy's address
+ * (a host-side query; make it outside graph capture).  Every call on one GPU
+ * shares the array and leaves its last contents there (each call writes all
+ * it reads first), so calls on one GPU must be ordered on one stream: calls
+ * that overlap on one GPU race. */
+qg_status quant_grouped_gemm_noalloc(const void* w, qg_format fmt, int64_t E, int64_t N, int64_t K, int64_t M,
+                                     const uint16_t* x, const int32_t* ids, float* y, void* stream);
+
 /* Bytes of workspace quant_moe_block needs (0 when the arguments would be
  * rejected by quant_moe_block's shape checks).  Host only. */
 size_t quant_moe_workspace_bytes(qg_format fmt_gate_up, qg_format fmt_down, int64_t E, int64_t D, int64_t F,
