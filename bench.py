@@ -1,19 +1,24 @@
 #!/usr/bin/env python
 """Weight-stream benchmark of the block-quantized decode GEMV on one MI355X.
 
-Default workload: Q4_K fused gate+up decode GEMV of Qwen3.8-27B's MLP
+Headline workload: Q4_K fused gate+up decode GEMV of Qwen3.8-27B's MLP
 (M = 1, N = 2 x 17,408, K = 5,120; 100,270,080 packed weight bytes per call),
 synthetic seeded weights and activations already resident in HBM.  A step is one
 call of the hot path (quant_gemv).  The weights are rotated over enough distinct
 copies (>= 1 GiB in total) that every call streams from HBM, not from the
 256 MB Infinity Cache.
 
-Printed: one JSON line with the weight-stream rate (GB/s of packed weight bytes),
-the kernel's roofline position against MI355X's 8 TB/s HBM peak and against a
-plain streaming read of 1 GiB on the same box, and the CPU oracle timed on a
-bounded sample of the same workload.  --all adds every workload shape (the
-parity configurations) as a "sweep" list; launch-bound shapes also report the
-rate of their rotated calls replayed from one HIP graph.
+Printed: one JSON line with the headline's weight-stream rate (GB/s of packed
+weight bytes), its roofline position against MI355X's 8 TB/s HBM peak, and a
+"configs" list with every workload configuration of the method, each timed the
+same way: Q8_0 1024 x 1024; Q4_K gate+up; Q6_K down projection and LM head at
+M = 1 and 8; NVFP4 MLP shapes at M = 1, 8 and 512; the Q4_K 288-expert MoE layer
+(gate, up, down grouped products over 16 tokens x top-8).  Each reports weight
+GB/s, % of 8 TB/s, % of a plain streaming read of the same byte count (a
+size-matched achievable ceiling), implied tokens/s, matrix-core TFLOP/s for
+M = 512 and the HBM traffic measured by counters.  GPU clocks are read before,
+under load and after; the CPU oracle is timed on a bounded sample, on all host
+threads and on one.  --all adds the remaining workload shapes as a "sweep".
 """
 from __future__ import annotations
 
@@ -33,7 +38,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 TOKEN_BYTES_GB = 16.39         # per-token weight read of the 27B Q4_K_M artifact, embedding gather excluded
 ROTATE_BYTES = 1 << 30
-LAUNCH_BOUND_BYTES = 16 << 20  # below this a call is dominated by launch latency
+GRAPH_BYTES = 16 << 20  # below this a call is launch-bound: also timed replayed from a HIP graph
+WARM_S = 0.1  # untimed back-to-back calls before each timed region, so the clocks have ramped up
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
 COPY_ELEMS = 64 << 20  # fp32 elements of the calibration copy: 256 MiB read, 256 MiB written
@@ -44,10 +50,11 @@ def log(*a):
 
 
 class Workload:
-    def __init__(self, name, fmt, N, K, M, seed, E=1, moe=None, block=None):
+    def __init__(self, name, fmt, N, K, M, seed, E=1, moe=None, block=None, layer=False):
         self.name, self.fmt, self.N, self.K, self.M, self.seed, self.E = name, fmt, N, K, M, seed, E
         self.moe = moe  # (tokens, topk) for the grouped workload
         self.block = block  # (down format, F, tokens, topk) for the MoE block: N = 2F, K = D
+        self.layer = layer  # grouped gate [E*N, K], up [E*N, K] and down [E*K, N] products per step
 
 
 def workloads():
@@ -84,7 +91,19 @@ def workloads():
                              moe=(16, 8)),
         "moe_block": Workload("Q4_K MoE block (gate|up, SwiGLU, down, combine), E=288 D=4096 F=2048, 16 tokens x "
                               "top-8", qg.Q4_K, 2 * 2048, 4096, 128, 5, E=288, block=(qg.Q4_K, 2048, 16, 8)),
+        "moe_layer": Workload("Q4_K grouped MoE layer (gate, up, down products), E=288 experts of 4096x2048, "
+                              "16 tokens x top-8", qg.Q4_K, 2048, 4096, 128, 5, E=288, moe=(16, 8), layer=True),
     }
+
+
+# The workload configurations of the method, in order: (config id, workload key).
+CONFIGS = [("1", "q8_0_1024"), ("2", "q4k_gateup"),
+           ("3", "q6k_down_m1"), ("3", "q6k_down_m8"), ("3", "q6k_head_m1"), ("3", "q6k_head_m8"),
+           ("4", "nvfp4_up_m1"), ("4", "nvfp4_up_m8"), ("4", "nvfp4_up_m512"),
+           ("4", "nvfp4_down_m1"), ("4", "nvfp4_down_m8"), ("4", "nvfp4_down_m512"),
+           ("5", "moe_layer")]
+HEADLINE = "q4k_gateup"
+LAYER_ROUTINGS = 8  # routing draws cycled by the MoE-layer workload
 
 
 class Prepared:
@@ -96,8 +115,12 @@ class Prepared:
         import gemm_block_quant_amd as qg
         import synth
         self.wl = wl
+        self.call_bytes = None  # bytes of call i (cycled), when calls differ
         if wl.block is not None:
             self._prepare_block(wl)
+            return
+        if wl.layer:
+            self._prepare_layer(wl)
             return
         tid_w = 0 if wl.moe is None or wl.K == 4096 else 4
         t0 = time.time()
@@ -180,6 +203,63 @@ class Prepared:
                 vp(self.wts), vp(self.y), vp(self.ws), wsb)
         self.calls = [lambda s: L.quant_moe_block(*args, s)]
 
+    def _prepare_layer(self, wl: Workload):
+        """The MoE layer: gate and up weight[E*N, K], down weight[E*K, N] (Q4_K), 16
+        tokens routed to 8 distinct experts each (M = 128 rows), three grouped
+        calls per step.  The routing cycles over LAYER_ROUTINGS draws so that
+        consecutive steps read different expert sets from the 4 GB tower.  As for
+        the MoE block, the first 32 experts are drawn and repeated for the others
+        (same distributions, distinct addresses)."""
+        import torch
+
+        import gemm_block_quant_amd as qg
+        import synth
+        E, N, K, M = wl.E, wl.N, wl.K, wl.M
+        tokens, topk = wl.moe
+        base = min(E, 32)
+        reps = -(-E // base)
+        t0 = time.time()
+        mats = []
+        for tid, (rows, cols) in enumerate(((N, K), (N, K), (K, N))):
+            hw = synth.weights(wl.fmt, synth.rng(wl.seed, 20 + tid), base * rows, cols)
+            mats.append(torch.from_numpy(hw).cuda().repeat(reps)[:qg.quant_packed_bytes(wl.fmt, E, rows,
+                                                                                          cols)].contiguous())
+        self.w_gate, self.w_up, self.w_down = mats
+        self.wbytes_total = sum(m.numel() for m in mats)
+        self.x = torch.from_numpy(synth.x_bf16(synth.rng(wl.seed, 1), M, K).view(np.int16)).cuda()
+        self.xd = torch.from_numpy(synth.x_bf16(synth.rng(wl.seed, 3), M, N).view(np.int16)).cuda()
+        self.ids_list = [synth.routing(synth.rng(wl.seed, 100 + r), tokens, topk, E) for r in range(LAYER_ROUTINGS)]
+        self.ids_dev = [torch.from_numpy(i).cuda() for i in self.ids_list]
+        per_expert = 2 * qg.quant_packed_bytes(wl.fmt, 1, N, K) + qg.quant_packed_bytes(wl.fmt, 1, K, N)
+        self.distinct_list = [len(np.unique(i)) for i in self.ids_list]
+        self.call_bytes = [d * per_expert for d in self.distinct_list]
+        self.bytes_per_call = sum(self.call_bytes) / len(self.call_bytes)
+        self.distinct = sum(self.distinct_list) / len(self.distinct_list)
+        self.copies = 1
+        self.y_gate = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        self.y_up = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        self.y_down = torch.empty((M, K), dtype=torch.float32, device="cuda")
+        wsb = qg.quant_grouped_workspace_bytes(E, M)
+        self.ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        log("[bench] %s: generated and placed %.1f MB in %.1f s" % (wl.name, self.wbytes_total / 1e6,
+                                                                      time.time() - t0))
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        L = qg.lib()
+        vp = lambda t: ctypes.c_void_p(t.data_ptr())
+        fmt = wl.fmt
+
+        def step(s, ids):
+            for w, xx, yy, n, k in ((self.w_gate, self.x, self.y_gate, N, K), (self.w_up, self.x, self.y_up, N, K),
+                                    (self.w_down, self.xd, self.y_down, K, N)):
+                st = L.quant_grouped_gemm(vp(w), fmt, E, n, k, M, vp(xx), vp(ids), vp(yy), vp(self.ws), wsb, s)
+                if st != 0:
+                    return st
+            return 0
+        self.calls = [lambda s, ids=ids: step(s, ids) for ids in self.ids_dev]
+
+    def bytes_of(self, i):
+        return self.call_bytes[i % len(self.call_bytes)] if self.call_bytes else self.bytes_per_call
+
     def call(self, i, stream=None):
         st = self.calls[i % len(self.calls)](self.stream if stream is None else stream)
         if st != 0:
@@ -197,6 +277,13 @@ def time_workload(p: Prepared, steps: int, warmup: int):
     import torch
     for i in range(warmup):
         p.call(i)
+    # and untimed calls until the clocks have ramped up (at least WARM_S of work)
+    t0, i = time.time(), warmup
+    while time.time() - t0 < WARM_S:
+        for _ in range(16):
+            p.call(i)
+            i += 1
+        torch.cuda.synchronize()
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -217,8 +304,8 @@ def time_workload(p: Prepared, steps: int, warmup: int):
 
 
 def graph_time(p: Prepared, reps: int = 5):
-    """A launch-bound workload: one call per rotated weight copy captured in one
-    HIP graph (torch's CUDAGraph), replayed `reps` times; seconds per call (the
+    """One call per rotated weight copy (at least 64 calls) captured in one HIP
+    graph (torch's CUDAGraph), replayed `reps` times; seconds per call (the
     median replay)."""
     import torch
     side = torch.cuda.Stream()
@@ -230,9 +317,10 @@ def graph_time(p: Prepared, reps: int = 5):
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
+    ncalls = max(64, len(p.calls))
     with torch.cuda.graph(g):
         st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        for i in range(len(p.calls)):
+        for i in range(ncalls):
             p.call(i, st)
     torch.cuda.synchronize()
     times = []
@@ -242,31 +330,106 @@ def graph_time(p: Prepared, reps: int = 5):
         g.replay()
         b.record()
         torch.cuda.synchronize()
-        times.append(a.elapsed_time(b) / 1e3 / len(p.calls))
+        times.append(a.elapsed_time(b) / 1e3 / ncalls)
     return float(np.median(times))
 
 
-def achievable_read_gbs(reps: int = 5):
-    """The plain streaming-read reference: quant_read_probe over 1 GiB (each
-    16-byte granule read once, non-temporal loads, nothing written); GB/s of the
-    median of `reps` runs."""
+class ReadProbe:
+    """The plain streaming-read reference (quant_read_probe: each 16-byte granule
+    read once, non-temporal loads, nothing written).  One device buffer serves
+    every size; a size is read from rotating slices of it (>= 1 GiB of distinct
+    bytes per cycle, as the workloads rotate their weights) so that the rate is
+    that of HBM, not of the last-level cache."""
+
+    def __init__(self, max_bytes: int):
+        import torch
+        self.cap = max(2 * ROTATE_BYTES, 2 * max_bytes + ROTATE_BYTES // 8)
+        self.buf = torch.ones(self.cap // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def gbs(self, nbytes: int, steps: int = 50, reps: int = 3) -> float:
+        import torch
+        import gemm_block_quant_amd as qg
+        nbytes = (int(nbytes) + 255) // 256 * 256
+        copies = max(2, -(-ROTATE_BYTES // nbytes))
+        copies = min(copies, self.cap // nbytes)
+        # raw C calls with prepared arguments, so that host overhead never limits the rate
+        L = qg.lib()
+        base = self.buf.data_ptr()
+        ptrs = [ctypes.c_void_p(base + c * nbytes) for c in range(copies)]
+        sink = ctypes.c_void_p(self.sink.data_ptr())
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        n = ctypes.c_size_t(nbytes)
+
+        def call(i, stream=st):
+            if L.quant_read_probe(ptrs[i % copies], n, sink, stream) != 0:
+                raise RuntimeError("quant_read_probe failed")
+        t0, i = time.time(), 0
+        while time.time() - t0 < WARM_S:
+            for _ in range(16):
+                call(i)
+                i += 1
+            torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(steps):
+                call(i)
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / 1e3 / steps
+            best = t if best is None else min(best, t)
+        return nbytes / best / 1e9
+
+
+def read_clocks():
+    """Current GPU shader and memory clock levels (MHz) from sysfs, or None."""
+    import glob
+    out = {}
+    for key, fname in (("sclk_MHz", "pp_dpm_sclk"), ("mclk_MHz", "pp_dpm_mclk")):
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/" + fname)):
+            try:
+                with open(path) as f:
+                    for line in f:
+                        if line.rstrip().endswith("*"):
+                            out[key] = int(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+            except (OSError, ValueError, IndexError):
+                continue
+            if key in out:
+                break
+    return out or None
+
+
+def clocks_under_load(p, seconds: float = 0.3):
+    """Clock levels sampled while the workload's calls run back to back (these
+    calls are outside every timed region)."""
+    import threading
     import torch
-    import gemm_block_quant_amd as qg
-    t = torch.ones(ROTATE_BYTES // 4, dtype=torch.float32, device="cuda")
-    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-    qg.quant_read_probe(t, sink)
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        qg.quant_read_probe(t, sink)
-        b.record()
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            c = read_clocks()
+            if c:
+                samples.append(c)
+            time.sleep(0.02)
+    th = threading.Thread(target=sampler)
+    th.start()
+    t0, i = time.time(), 0
+    while time.time() - t0 < seconds:
+        for _ in range(64):
+            p.call(i)
+            i += 1
         torch.cuda.synchronize()
-        times.append(a.elapsed_time(b) / 1e3)
-    del t
-    torch.cuda.empty_cache()
-    return ROTATE_BYTES / float(np.median(times)) / 1e9
+    stop.set()
+    th.join()
+    out = {}
+    for key in ("sclk_MHz", "mclk_MHz"):
+        v = [c[key] for c in samples if key in c]
+        if v:
+            out[key] = {"min": min(v), "max": max(v), "samples": len(v)}
+    return out or None
 
 
 def kernel_source_hash() -> str:
@@ -352,19 +515,42 @@ def pmc_summary(fetch_dir: str, write_dir: str, key: str, fetch_cmd: str, write_
     print(json.dumps(out))
 
 
-def cpu_baseline(p: Prepared, target_s: float = 12.0):
-    """The oracle (as it stands) on a bounded sample of the same workload: the first
-    output rows, doubling until one pass takes about target_s; when the whole
-    matrix takes less, whole passes are repeated until target_s has elapsed."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(p: Prepared, target_s: float = 10.0, single_s: float = 4.0):
+    """The oracle (as it stands) on a bounded sample of the same workload, on all
+    host threads and on one."""
+    import oracle
+    allt = _cpu_leg(p, target_s, 0)
+    one = _cpu_leg(p, single_s, 1)
+    allt["single_thread"] = {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"]}
+    allt["cpu_model"] = cpu_model()
+    allt["host_threads_available"] = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return allt
+
+
+def _cpu_leg(p: Prepared, target_s: float, nthreads_req: int):
+    """The first output rows, doubling until one pass takes about target_s; when
+    the whole matrix takes less, whole passes are repeated until target_s has
+    elapsed.  nthreads_req 0: every thread the oracle's OpenMP runtime uses."""
     import oracle
     wl = p.wl
-    nthreads = oracle.max_threads()
+    nthreads = oracle.max_threads() if nthreads_req <= 0 else nthreads_req
     ids = p.ids_host if wl.moe else None
     rows_try = 64
     while True:
         cols = np.arange(min(rows_try, wl.N))
         t0 = time.time()
-        oracle.gemm(wl.fmt, p.w_host, wl.N, wl.K, p.x_host, E=wl.E, cols=cols, ids=ids)
+        oracle.gemm(wl.fmt, p.w_host, wl.N, wl.K, p.x_host, E=wl.E, cols=cols, ids=ids, nthreads=nthreads)
         dt = time.time() - t0
         if dt >= target_s or rows_try >= wl.N:
             break
@@ -374,7 +560,7 @@ def cpu_baseline(p: Prepared, target_s: float = 12.0):
         t0 = time.time()
         passes = 0
         while time.time() - t0 < target_s:
-            oracle.gemm(wl.fmt, p.w_host, wl.N, wl.K, p.x_host, E=wl.E, cols=cols, ids=ids)
+            oracle.gemm(wl.fmt, p.w_host, wl.N, wl.K, p.x_host, E=wl.E, cols=cols, ids=ids, nthreads=nthreads)
             passes += 1
         dt = time.time() - t0
     # the workload's weight bytes in proportion to the outputs computed (same unit as the GPU figure)
@@ -384,25 +570,40 @@ def cpu_baseline(p: Prepared, target_s: float = 12.0):
                       "%d threads" % (len(cols), wl.N, wl.M, pass_bytes / 1e6, passes, dt, nthreads)}
 
 
-def result_for(p: Prepared, steps: int, warmup: int):
+def result_for(p: Prepared, steps: int, warmup: int, key: str = None, probe: ReadProbe = None):
+    """Time `steps` calls (whole job, events at the two ends) and the same calls
+    with an event pair around each launch; the rates, roofline fractions and
+    (when counters were taken on the current sources) the measured HBM traffic."""
     total, per_mean, per_med = time_workload(p, steps, warmup)
     wl = p.wl
-    gbs = p.bytes_per_call * steps / total / 1e9
+    job_bytes = sum(p.bytes_of(i) for i in range(steps))
+    gbs = job_bytes / total / 1e9
     kern_gbs = p.bytes_per_call / per_mean / 1e9
     r = {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "E": wl.E,
-         "weight_bytes_per_call": p.bytes_per_call, "rotated_copies": p.copies,
+         "weight_bytes_per_call": int(round(p.bytes_per_call)), "rotated_copies": p.copies,
          "ms_per_call": round(total / steps * 1e3, 5), "kernel_ms_mean": round(per_mean * 1e3, 5),
          "kernel_ms_median": round(per_med * 1e3, 5),
          "weight_GBps": round(gbs, 1), "kernel_weight_GBps": round(kern_gbs, 1),
-         "pct_hbm_peak": round(100 * kern_gbs / HBM_PEAK_GBS, 2),
+         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
          "implied_tok_s": round(wl.M * gbs / TOKEN_BYTES_GB, 1)}
     if wl.moe or wl.block:
         r["distinct_experts"] = p.distinct
-    if wl.M >= 32 and not wl.block:
+    if wl.layer:
+        r["grouped_calls_per_step"] = 3
+        r["routings_cycled"] = LAYER_ROUTINGS
+    if wl.M >= 32 and not wl.block and not wl.layer and not wl.moe:
         flops = 2.0 * wl.M * wl.N * wl.K
-        r["TFLOPs"] = round(flops / per_mean / 1e12, 1)
-        r["pct_bf16_mfma_peak"] = round(100 * flops / per_mean / 1e12 / BF16_MFMA_PEAK_TFLOPS, 2)
-    if p.bytes_per_call < LAUNCH_BOUND_BYTES:
+        r["TFLOPs"] = round(flops / (total / steps) / 1e12, 1)
+        r["pct_bf16_mfma_peak"] = round(100 * flops / (total / steps) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 2)
+    if probe is not None:
+        ach = probe.gbs(p.bytes_per_call)
+        r["achievable_read_GBps"] = round(ach, 1)
+        r["pct_of_achievable"] = round(100 * gbs / ach, 2)
+    if key is not None:
+        tr = traffic_for(key)
+        r["traffic_bytes_per_call"] = tr
+        r["traffic_ratio"] = round(tr / p.bytes_per_call, 4) if tr else None
+    if p.bytes_per_call < GRAPH_BYTES and not wl.layer and not wl.block:
         # launch-bound: the rotated calls replayed from one graph
         gt = graph_time(p)
         r["graph_ms_per_call"] = round(gt * 1e3, 5)
@@ -413,12 +614,13 @@ def result_for(p: Prepared, steps: int, warmup: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="q4k_gateup")
-    ap.add_argument("--all", action="store_true", help="also time every workload shape (sweep)")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, help="headline workload (default: the Q4_K gate+up GEMV)")
+    ap.add_argument("--only", action="store_true", help="time the headline workload only (no configs list)")
+    ap.add_argument("--all", action="store_true", help="also time every other workload shape (sweep)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--sweep-out", default=None, help="write the sweep as JSON lines to this file")
+    ap.add_argument("--sweep-out", default=None, help="write the configs and sweep as JSON lines to this file")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed regions, run the known-size copy the HBM counters are scaled by")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
@@ -438,45 +640,63 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     wls = workloads()
-    wl = wls[args.workload]
-    achievable = achievable_read_gbs()
+    clocks = {"before": read_clocks()}
+    probe = ReadProbe(1_042_944_000)
+    achievable = probe.gbs(ROTATE_BYTES, steps=10)
     log("[bench] plain streaming read of 1 GiB (quant_read_probe): %.1f GB/s" % achievable)
-    p = Prepared(wl)
+
+    # the headline first: its timed region is the JSON line's value
+    p = Prepared(wls[args.workload])
     torch.cuda.synchronize()
-    r, total, per_mean = result_for(p, args.steps, args.warmup)
-    r["pct_of_achievable"] = round(100 * r["weight_GBps"] / achievable, 2)
+    r, total, per_mean = result_for(p, args.steps, args.warmup, args.workload, probe)
+    clocks["under_load"] = clocks_under_load(p)
     log("[bench] %s" % json.dumps(r))
-    sweep = []
-    if args.all:
-        for key, w2 in wls.items():
-            if key == args.workload:
-                sweep.append(r)
-                continue
-            try:
-                p2 = Prepared(w2)
-                steps = max(10, min(args.steps, int(2.0 / max(1e-6, p2.bytes_per_call / 5e12))))
-                r2, _, _ = result_for(p2, steps, min(args.warmup, steps))
-                r2["pct_of_achievable"] = round(100 * r2["weight_GBps"] / achievable, 2)
-            except Exception as e:  # a workload the build cannot run yet is reported, not fatal
-                r2 = {"workload": w2.name, "M": w2.M, "error": str(e)}
-            log("[bench] %s" % json.dumps(r2))
-            sweep.append(r2)
-            del p2
-            torch.cuda.empty_cache()
-        if args.sweep_out:
-            with open(args.sweep_out, "w") as f:
-                for s in sweep:
-                    f.write(json.dumps(s) + "\n")
-    if args.calibrate_copy:
-        copy_calibration()
+    headline_bytes = p.bytes_per_call
     cpu = None
-    if not args.no_cpu and not wl.block:
+    if not args.no_cpu and not p.wl.block and not p.wl.layer:
         cpu = cpu_baseline(p)
         log("[bench] cpu baseline %s" % json.dumps(cpu))
-    value = p.bytes_per_call * args.steps / total / 1e9
+    if args.calibrate_copy:
+        copy_calibration()
+    del p
+    torch.cuda.empty_cache()
+
+    configs, sweep = [], []
+    keys = [] if args.only else [(c, k) for c, k in CONFIGS]
+    if args.all:
+        listed = {k for _, k in CONFIGS}
+        keys += [(None, k) for k in wls if k not in listed]
+    for cfg, key in keys:
+        if key == args.workload and cfg is not None:
+            r2 = dict(r)
+        else:
+            try:
+                p2 = Prepared(wls[key])
+                # enough calls for a stable time, a few tenths of a second at most
+                steps = max(20, min(args.steps, int(0.3 / max(1e-6, p2.bytes_per_call / 5e12))))
+                r2, _, _ = result_for(p2, steps, min(args.warmup, steps), key, probe)
+                del p2
+            except Exception as e:  # a workload the build cannot run is reported, not fatal
+                r2 = {"workload": wls[key].name, "M": wls[key].M, "error": str(e)}
+            torch.cuda.empty_cache()
+        r2["key"] = key
+        if cfg is not None:
+            r2["config"] = cfg
+            configs.append(r2)
+        else:
+            sweep.append(r2)
+        log("[bench] %s" % json.dumps(r2))
+    clocks["after"] = read_clocks()
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            for x in configs + sweep:
+                f.write(json.dumps(x) + "\n")
+
+    value = headline_bytes * args.steps / total / 1e9
     # the step is one launch of the product kernel: its average duration over the
     # timed region (events on the launch stream at the region's two ends)
-    achieved = p.bytes_per_call / (total / args.steps) / 1e9
+    achieved = headline_bytes / (total / args.steps) / 1e9
+    wl = wls[args.workload]
     out = {
         "metric": "weight-stream HBM GB/s and % of MI355X peak for quantized decode GEMV (M=1,8)",
         "value": round(value, 1),
@@ -491,14 +711,17 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "format": {v: k for k, v in qg.FORMATS.items()}[wl.fmt], "M": wl.M,
-                   "N": wl.N, "K": wl.K, "weight_bytes": p.bytes_per_call, "rotated_copies": p.copies,
+                   "N": wl.N, "K": wl.K, "weight_bytes": int(headline_bytes), "rotated_copies": r["rotated_copies"],
                    "implied_tok_s": r["implied_tok_s"],
                    "ms_per_launch_with_per_launch_events": round(per_mean * 1e3, 5),
-                   "achievable_read_GBps": round(achievable, 1),
-                   "pct_of_achievable": round(100 * achieved / achievable, 2)},
+                   "achievable_read_GBps_1GiB": round(achievable, 1),
+                   "achievable_read_GBps": r.get("achievable_read_GBps"),
+                   "pct_of_achievable": r.get("pct_of_achievable")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(args.workload)},
         "cpu_baseline": cpu,
+        "clocks": clocks,
+        "configs": configs,
     }
     if sweep:
         out["sweep"] = sweep

@@ -247,20 +247,26 @@ static qg_status scratch_on_current_device(void** out) {
 
 namespace qg {
 
-// Plain streaming read (measurement reference): every 16-byte granule of the
-// buffer once, non-temporal, eight loads in flight per thread, grid-stride.
-__global__ __launch_bounds__(256) void k_read_probe(const u32x4* __restrict__ p, size_t n16, uint32_t* sink) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+// Plain streaming read (measurement reference): workgroup b reads the b-th
+// contiguous chunk of the buffer, every 16-byte granule once, non-temporal,
+// four loads in flight per thread (the fastest of the shapes measured: one
+// 1024-thread workgroup per CU streaming its own chunk).
+constexpr int kProbeThreads = 1024;
+__global__ __launch_bounds__(kProbeThreads) void k_read_probe(const u32x4* __restrict__ p, size_t n16, size_t per,
+                                                              uint32_t* sink) {
+    const size_t beg = (size_t)blockIdx.x * per;
+    const size_t end = beg + per < n16 ? beg + per : n16;
     uint32_t acc = 0;
-    for (; i + 7 * stride < n16; i += 8 * stride) {
-        u32x4 v[8];
+    size_t i = beg + threadIdx.x;
+    for (; i + 3 * kProbeThreads < end; i += 4 * kProbeThreads) {
+        u32x4 v[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load((const QG_GLOBAL u32x4*)(p + i + u * stride));
+        for (int u = 0; u < 4; ++u)
+            v[u] = __builtin_nontemporal_load((const QG_GLOBAL u32x4*)(p + i + (size_t)u * kProbeThreads));
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
-    for (; i < n16; i += stride) {
+    for (; i < end; i += kProbeThreads) {
         const u32x4 v = __builtin_nontemporal_load((const QG_GLOBAL u32x4*)(p + i));
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
@@ -441,11 +447,12 @@ qg_status quant_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* 
     if (bytes % 16) return QG_ESHAPE;
     if (bytes == 0) return QG_OK;
     const size_t n16 = bytes / 16;
-    size_t grid = (size_t)qg::num_cus() * 64;  // 64 workgroups per CU: the fastest shape measured
-    const size_t need = (n16 + 255) / 256;
+    size_t grid = (size_t)qg::num_cus();  // one workgroup per CU
+    const size_t need = (n16 + qg::kProbeThreads - 1) / qg::kProbeThreads;
     if (grid > need) grid = need;
-    hipLaunchKernelGGL(qg::k_read_probe, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
-                       (const qg::u32x4*)buf, n16, sink);
+    const size_t per = (n16 + grid - 1) / grid;
+    hipLaunchKernelGGL(qg::k_read_probe, dim3((unsigned)grid), dim3(qg::kProbeThreads), 0, (hipStream_t)stream,
+                       (const qg::u32x4*)buf, n16, per, sink);
     return from_hip(hipGetLastError());
 }
 

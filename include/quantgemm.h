@@ -221,7 +221,8 @@ qg_status quant_dequantize_stacked(const void* w, qg_format fmt, int64_t E, int6
 const char* quant_status_string(qg_status s);
 
 /* Measurement reference, not part of the product path: a plain streaming read
- * of `bytes` bytes at `buf` (each 16-byte granule once, non-temporal loads),
+ * of `bytes` bytes at `buf` (each 16-byte granule once, non-temporal loads,
+ * one workgroup per CU streaming a contiguous chunk),
  * the achievable-bandwidth ceiling the streaming kernels are compared with
  * ("Qwen3.8-27B on one Tenstorrent P150", section "4. Measuring the ceiling,
  * and lots of dead ends": a validated read microbenchmark as the ceiling).
