@@ -27,7 +27,8 @@ FORMATS = {"Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K, "NVFP4": NVFP4, "Q5_K": Q5_
 
 QG_OK, QG_EINVAL, QG_EFORMAT, QG_EALIGN, QG_ESHAPE, QG_EHIP, QG_ENOTIMPL, QG_EWORKSPACE = range(8)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libquantgemm.so")
+# QUANTGEMM_LIB names another build of the library to load (e.g. the sanitizer build)
+LIB_PATH = os.environ.get("QUANTGEMM_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libquantgemm.so")
 
 _lib = None
 

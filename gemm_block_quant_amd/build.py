@@ -1,9 +1,12 @@
 """Build libquantgemm.so (HIP, gfx950) in the package directory.
 
-    python -m gemm_block_quant_amd.build [-v] [--incremental]
+    python -m gemm_block_quant_amd.build [-v] [--incremental] [--sanitize]
 
 Every call compiles from source (hipcc cross-compiles without a GPU).  With
 --incremental, objects newer than their source and every header are kept.
+--sanitize builds a copy whose host code is instrumented for AddressSanitizer
+and UndefinedBehaviorSanitizer (gemm_block_quant_amd/_asan/libquantgemm.so, for
+host-only tests; the device code is unchanged).
 """
 from __future__ import annotations
 
@@ -32,32 +35,41 @@ def _headers():
     return glob.glob(os.path.join(HERE, "csrc", "*.h")) + glob.glob(os.path.join(root, "include", "*.h"))
 
 
-def build(verbose: bool = False, jobs: int = 8, incremental: bool = False) -> str:
+# Host-side sanitizers (each -fsanitize= placed after -Xarch_host: device code is not instrumented).
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_DIR = os.path.join(HERE, "_asan")
+
+
+def build(verbose: bool = False, jobs: int = 8, incremental: bool = False, sanitize: bool = False) -> str:
     objs = []
     procs = []
-    os.makedirs(os.path.join(HERE, "_build"), exist_ok=True)
+    bdir = ASAN_DIR if sanitize else os.path.join(HERE, "_build")
+    lib = os.path.join(ASAN_DIR, "libquantgemm.so") if sanitize else LIB
+    os.makedirs(bdir, exist_ok=True)
     newest_header = max((os.path.getmtime(h) for h in _headers()), default=0.0)
     for src in sources():
-        obj = os.path.join(HERE, "_build", os.path.basename(src) + ".o")
+        obj = os.path.join(bdir, os.path.basename(src) + ".o")
         objs.append(obj)
         if incremental and os.path.exists(obj) and \
                 os.path.getmtime(obj) > max(os.path.getmtime(src), newest_header):
             continue
         cmd = [HIPCC, "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
-               "-Wno-unused-function", "-c", src, "-o", obj] + DEVICE_FLAGS
+               "-Wno-unused-function", "-c", src, "-o", obj] + DEVICE_FLAGS + (SANITIZE_FLAGS if sanitize else [])
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         if len(procs) >= jobs:
             _drain(procs)
     _drain(procs)
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs + \
+        (["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"] if sanitize else [])
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def _drain(procs):
@@ -75,4 +87,4 @@ def _drain(procs):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -94,7 +94,18 @@
 extern "C" {
 #endif
 
-typedef enum { QG_Q8_0 = 1, QG_Q4_K = 2, QG_Q6_K = 3, QG_NVFP4 = 4, QG_Q5_K = 5, QG_FP8 = 6 } qg_format;
+/* The *_MAX_ENUM members give both enums the full 32-bit int range: a caller
+ * may pass any int, and an unknown value is rejected (QG_EFORMAT, "unknown
+ * status") rather than being out of the enum's range. */
+typedef enum {
+    QG_Q8_0 = 1,
+    QG_Q4_K = 2,
+    QG_Q6_K = 3,
+    QG_NVFP4 = 4,
+    QG_Q5_K = 5,
+    QG_FP8 = 6,
+    QG_FORMAT_MAX_ENUM = 0x7FFFFFFF
+} qg_format;
 
 typedef enum {
     QG_OK = 0,
@@ -104,7 +115,8 @@ typedef enum {
     QG_ESHAPE = 4,   /* negative size, K not a positive multiple of the block, size overflow, limits */
     QG_EHIP = 5,     /* the HIP runtime reported an error on launch */
     QG_ENOTIMPL = 6, /* combination not implemented by this build */
-    QG_EWORKSPACE = 7 /* workspace missing or smaller than quant_grouped_workspace_bytes() */
+    QG_EWORKSPACE = 7, /* workspace missing or smaller than quant_grouped_workspace_bytes() */
+    QG_STATUS_MAX_ENUM = 0x7FFFFFFF
 } qg_status;
 
 /* Values per block (Q8_0 32, Q4_K / Q5_K / Q6_K 256, NVFP4 16; FP8 64, the

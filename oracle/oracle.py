@@ -17,27 +17,33 @@ FORMATS = {"Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K, "NVFP4": NVFP4, "Q5_K": Q5_
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# QG_ORACLE_LIB names another build of oracle.c to load (the sanitizer runs use it)
+_LIB = os.environ.get("QG_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 
-def build(verbose: bool = False) -> str:
-    """Compile oracle.c with gcc (plain -O2, no fast-math, no contraction)."""
-    tmp = _LIB + ".tmp%d" % os.getpid()
+
+def build(verbose: bool = False, out: str | None = None, sanitize: bool = False) -> str:
+    """Compile oracle.c with gcc (plain -O2, no fast-math, no contraction); with
+    sanitize, instrumented for AddressSanitizer and UndefinedBehaviorSanitizer."""
+    out = out or os.path.join(_HERE, "liboracle.so")
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-           "-shared", "-fPIC", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+           "-shared", "-fPIC", "-Wall", "-Wextra"] + (SANITIZE_FLAGS if sanitize else []) + ["-o", tmp, _SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.check_call(cmd)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, out)
+    return out
 
 
 def load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if not os.path.exists(_LIB) or (not os.environ.get("QG_ORACLE_LIB") and
+                                    os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
         build()
     lib = ctypes.CDLL(_LIB)
     ll, i32, vp = ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p
