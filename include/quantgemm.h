@@ -125,7 +125,11 @@ int64_t quant_block_values(qg_format fmt);
 
 /* Bytes of a packed weight[E*N, K] tensor in the layout above; 0 when the tag
  * is unknown, a size is negative or K is not a multiple of the block.  Host
- * only, touches no device. */
+ * only, touches no device.  The count a residency budget is made of: packed
+ * bytes per tensor (vllm.cpp issue #3030, issue body: the packed-versus-bf16
+ * byte inventory of the 27B artefact, 34- and 210-byte blocks), and the bytes
+ * a decode step must stream ("Qwen3.8-27B on one Tenstorrent P150", section
+ * "4. Measuring the ceiling"). */
 size_t quant_packed_bytes(qg_format fmt, int64_t E, int64_t N, int64_t K);
 
 /* Decode GEMV (M = 1): y[n] = sum_k W[n, k] * x[k].
@@ -146,7 +150,12 @@ qg_status quant_gemv(const void* w, qg_format fmt, int64_t N, int64_t K, const u
 qg_status quant_gemm(const void* w, qg_format fmt, int64_t N, int64_t K, int64_t M, const uint16_t* x, float* y,
                      void* stream);
 
-/* Bytes of workspace quant_grouped_gemm needs for E experts and M rows.  Host only. */
+/* Bytes of workspace quant_grouped_gemm needs for E experts and M rows: the
+ * device-side bucketing of rows by expert (per-expert counts and offsets, the
+ * row permutation), which is how each distinct expert is read once per call
+ * ("A 320B MoE on a free Kaggle TPU", section "Three things the README gets
+ * wrong": prefill groups the routed pairs by expert before the matvec).
+ * Host only; 0 for a negative size. */
 size_t quant_grouped_workspace_bytes(int64_t E, int64_t M);
 
 /* Grouped-expert product over stacked weights:
@@ -220,7 +229,12 @@ qg_status quant_moe_block(const void* w_gate_up, qg_format fmt_gate_up, const vo
                           void* stream);
 
 /* Dequantize rows [0, rows) of a packed weight[rows, K] to fp32 out[rows, K]
- * (bit-exact; a test and debugging aid, the products never call it).
+ * (bit-exact; a test and debugging aid, the products never call it).  It
+ * writes out the per-format block decode that the products do in registers,
+ * so that it can be compared with a dequantizer taken as the reference
+ * (vllm.cpp issue #3030, issue body: keep-quant matmuls gated against
+ * llama.cpp's own dequantization; "A 320B MoE on a free Kaggle TPU", section
+ * "What I actually ran": the kernel checked against gguf's dequantize).
  * For QG_NVFP4, `rows` is E*N of the tensor and all rows use g[0]; use
  * quant_dequantize_stacked for several stacked matrices. */
 qg_status quant_dequantize(const void* w, qg_format fmt, int64_t rows, int64_t K, float* out, void* stream);
@@ -229,7 +243,9 @@ qg_status quant_dequantize(const void* w, qg_format fmt, int64_t rows, int64_t K
 qg_status quant_dequantize_stacked(const void* w, qg_format fmt, int64_t E, int64_t N, int64_t K, float* out,
                                    void* stream);
 
-/* Static description of a status code; never NULL. */
+/* Static description of a status code, "unknown status" for any other value;
+ * never NULL.  Host only.  (A convenience of this ABI; the pages define no
+ * error codes.) */
 const char* quant_status_string(qg_status s);
 
 /* Measurement reference, not part of the product path: a plain streaming read
