@@ -144,12 +144,14 @@ qg_status run_grouped(const void* w, int fmt, int64_t E, int64_t N, int64_t K, i
 }  // namespace
 
 // Scratch of quant_grouped_gemm_noalloc: the bucketing workspace of the
-// largest grouped call (16384 rows: (5 + 2 * 16384 + 16384) int32 = 196,628
-// bytes), one copy per GPU for the life of the process.  In host code this
-// name is only a handle for hipGetSymbolAddress: the device address of each
-// GPU's copy is resolved once per device and used everywhere else.
-static constexpr size_t kScratchBytes = 196864;
-static_assert(kScratchBytes >= ((5 + 3 * kGroupedMaxRows) * 4 + 15) / 16 * 16, "holds the largest bucketing");
+// largest grouped call (16384 rows and as many slots: 5 + 2 * 16384 + 16384
+// int32, then two tile lists of 2 * 16384 / 32 int32 each: 204,820 bytes),
+// one copy per GPU for the life of the process.  In host code this name is
+// only a handle for hipGetSymbolAddress: the device address of each GPU's copy
+// is resolved once per device and used everywhere else.
+static constexpr size_t kScratchBytes = 204832;
+static_assert(kScratchBytes >= ((5 + 3 * kGroupedMaxRows + 4 * (kGroupedMaxRows / kMfmaMinRows)) * 4 + 15) / 16 * 16,
+              "holds the largest bucketing");
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace qg {

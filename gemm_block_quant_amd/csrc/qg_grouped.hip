@@ -16,13 +16,22 @@
 //     network in LDS (invalid ids sort last), mark where the id changes, scan,
 //     and write slot -> (expert, first sorted row) and the sorted row list.
 //     Rows whose id is outside [0, E) get NaN in every element of y.
+//     It also lists the row tiles of the experts with at least
+//     kMfmaMinRows rows, for 64- and for 128-row tiles.
 //  2. k_grouped: workgroup (slot, chunk) stages the slot's activation rows
 //     (16 at most per pass) in LDS and its 4 waves stream rows [chunk*RPC,
 //     ...) of the slot's expert through the same core as the dense product,
 //     writing y rows at the original row indices.  Workgroups whose slot is
-//     past the number of distinct experts exit at once.
+//     past the number of distinct experts exit at once, and so do those of a
+//     slot that the matrix-core tiles take.
+//  3. Experts with at least kMfmaMinRows rows (where the format has a tile
+//     path): the dense product's matrix-core tile kernel over the listed row
+//     tiles, each reading its expert's weights once per tile of rows, not once
+//     per 16 rows ("Qwen3.8-27B on one Tenstorrent P150", section "3. Porting
+//     the 9B stack to 27B geometry").
 // The per-row arithmetic is the dense kernel's, so E = 1 with ids = NULL
 // reproduces quant_gemm bit for bit.
+#include <climits>
 #include <type_traits>
 
 #include "qg_direct.h"
@@ -31,9 +40,18 @@ namespace qg {
 
 constexpr int kBucketThreads = 1024;
 
-// Workspace (int32): [0] slot count, [4 .. 4+S) slot expert, [4+S .. 5+2S)
-// slot start, then M sorted rows.  S = min(E, M).
+// Workspace (int32): [0] slot count, [1] and [2] the number of 64- and of
+// 128-row tiles listed, [4 .. 4+S) slot expert, [4+S .. 5+2S) slot start, then
+// M sorted rows, then the two tile lists (64-row tiles first), each entry the
+// pair (first sorted row, slot).  S = min(E, M).  A slot of c >= kMfmaMinRows
+// rows has ceil(c / 64) <= c / kMfmaMinRows tiles, so a list holds at most
+// M / kMfmaMinRows entries.
 __host__ __device__ inline int64_t ws_slots(int64_t E, int64_t M) { return E < M ? E : M; }
+__host__ __device__ inline int64_t ws_tile_cap(int64_t M) { return M / kMfmaMinRows; }
+// int offset of the list of bm-row tiles (bm 64 or 128)
+__host__ __device__ inline int64_t ws_tile_list(int64_t E, int64_t M, int bm) {
+    return 5 + 2 * ws_slots(E, M) + M + (bm == 128 ? 2 * ws_tile_cap(M) : 0);
+}
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int d) {
     const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, d, 64);
@@ -162,6 +180,55 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
         }
         slot_start[ws[0]] = lo;
     }
+    // row tiles of the slots with at least kMfmaMinRows rows: per thread a
+    // contiguous run of slots; 64-row counts in the low and 128-row counts in
+    // the high half of one scanned word (each total is at most M / 32)
+    __syncthreads();  // every slot start (and ws[0]) is written
+    const int nslots = ws[0];
+    const int sper = (nslots + nt - 1) / nt;
+    const int s0 = tid * sper, s1 = min(nslots, s0 + sper);
+    int tcnt = 0;
+    for (int q = s0; q < s1; ++q) {
+        const int c = slot_start[q + 1] - slot_start[q];
+        if (c >= kMfmaMinRows) tcnt += ((c + 63) >> 6) | (((c + 127) >> 7) << 16);
+    }
+    int tinc = tcnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(tinc, d, 64);
+        if (lane >= d) tinc += v;
+    }
+    if (lane == 63) part[wv] = tinc;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int t = 0; t < nt / 64; ++t) {
+            const int c = part[t];
+            part[t] = run;
+            run += c;
+        }
+        ws[1] = run & 0xFFFF;
+        ws[2] = run >> 16;
+    }
+    __syncthreads();
+    {
+        const int first = part[wv] + tinc - tcnt;
+        int o64 = first & 0xFFFF, o128 = first >> 16;
+        int32_t* list64 = perm + M;
+        int32_t* list128 = list64 + 2 * ws_tile_cap(M);
+        for (int q = s0; q < s1; ++q) {
+            const int r0 = slot_start[q], c = slot_start[q + 1] - r0;
+            if (c < kMfmaMinRows) continue;
+            for (int r = 0; r < c; r += 64, ++o64) {
+                list64[2 * o64] = r0 + r;
+                list64[2 * o64 + 1] = q;
+            }
+            for (int r = 0; r < c; r += 128, ++o128) {
+                list128[2 * o128] = r0 + r;
+                list128[2 * o128 + 1] = q;
+            }
+        }
+    }
     // NaN rows for ids outside [0, E)
     for (int i = M - 1; i >= 0; --i) {
         if ((uint32_t)(keys[i] >> 32) != 0x7fffffffu) break;
@@ -173,10 +240,11 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
 // Grouped streaming kernel.  MTMAX: activation rows per pass (LDS sized for
 // it); DIRECT: register-direct streaming (Q4_K, Q5_K, Q6_K, NVFP4 with K % 64 == 0) with SP
 // passes per ring slot, else the LDS row-buffer path with CPL/CPLS chunks.
+// Slots of tile_min rows or more are left to the matrix-core tiles.
 template <int F, int MTMAX, bool DIRECT, int CPL, int CPLS, int SP, int PF>
 __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32_t* __restrict__ ws, int64_t E,
                                                  int64_t M, int rpc, int nchunks, int64_t estride0,
-                                                 int64_t estride1) {
+                                                 int64_t estride1, int tile_min) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8* smem = (lds_u8*)smem_generic;
     const int K = a.K;
@@ -186,6 +254,7 @@ __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32
     const int64_t S = ws_slots(E, M);
     const int e = ws[4 + slot];
     const int r0 = ws[4 + S + slot], r1 = ws[4 + S + slot + 1];
+    if (r1 - r0 >= tile_min) return;  // uniform: the tile kernel takes this slot
     const int32_t* perm = ws + 5 + 2 * S;
 
     lds_u8* xl = smem;
@@ -253,8 +322,7 @@ __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32
 }
 
 size_t grouped_workspace_bytes(int64_t E, int64_t M) {
-    const int64_t S = ws_slots(E, M);
-    const int64_t ints = 5 + 2 * S + M;
+    const int64_t ints = ws_tile_list(E, M, 128) + 2 * ws_tile_cap(M);
     return (size_t)((ints * 4 + 15) / 16 * 16);
 }
 
@@ -264,7 +332,7 @@ size_t grouped_workspace_bytes(int64_t E, int64_t M) {
 // segments.
 template <class Kern>
 static hipError_t launch_grouped_one(Kern kern, size_t lds, const StreamArgs& a, const int32_t* ws, int64_t E,
-                                     int64_t M, int64_t estride0, int64_t estride1, hipStream_t st,
+                                     int64_t M, int64_t estride0, int64_t estride1, int tile_min, hipStream_t st,
                                      int seg_mt = 0) {
     int fit = 0;
     hipError_t e = kernel_residency((const void*)kern, lds, &fit);
@@ -287,13 +355,13 @@ static hipError_t launch_grouped_one(Kern kern, size_t lds, const StreamArgs& a,
     nchunks = (a.N + rpc - 1) / rpc;
     if (split) lds += direct_seg_lds_bytes(a.seg_S, rpc / 4, seg_mt);
     hipLaunchKernelGGL(kern, dim3((unsigned)(S * nchunks)), dim3(256), lds, st, a, ws, E, M, rpc, (int)nchunks,
-                       estride0, estride1);
+                       estride0, estride1, tile_min);
     return hipGetLastError();
 }
 
 template <int F, int MTMAX>
 static hipError_t grouped_paths(StreamArgs a, const int32_t* ws, int64_t E, int64_t M, int64_t es0, int64_t es1,
-                                hipStream_t st) {
+                                int tm, hipStream_t st) {
     if constexpr (F == QG_Q4_K || F == QG_Q5_K || F == QG_Q6_K || F == QG_NVFP4 || F == QG_FP8) {
         if (direct_eligible(F, a.K)) {
             // E = 1 splits rows exactly as the dense product does (so the two
@@ -306,7 +374,7 @@ static hipError_t grouped_paths(StreamArgs a, const int32_t* ws, int64_t E, int6
             a.seg_PS = sg.PS;
             const size_t lds = direct_lds_bytes(F, MTMAX, a.K);
             constexpr int SP = 1, PF = 3;
-            return launch_grouped_one(k_grouped<F, MTMAX, true, 1, 0, SP, PF>, lds, a, ws, E, M, es0, es1, st,
+            return launch_grouped_one(k_grouped<F, MTMAX, true, 1, 0, SP, PF>, lds, a, ws, E, M, es0, es1, tm, st,
                                       MTMAX);
         }
     }
@@ -318,11 +386,11 @@ static hipError_t grouped_paths(StreamArgs a, const int32_t* ws, int64_t E, int6
         constexpr int S = (F == QG_NVFP4) ? 1 : 0;
         const size_t lds = gemv_lds_bytes(MTMAX, a.K, cpl, S);
         switch (cpl) {
-            case 1: return launch_grouped_one(k_grouped<F, MTMAX, false, 1, S, 1, 4>, lds, a, ws, E, M, es0, es1, st);
-            case 2: return launch_grouped_one(k_grouped<F, MTMAX, false, 2, S, 1, 4>, lds, a, ws, E, M, es0, es1, st);
-            case 3: return launch_grouped_one(k_grouped<F, MTMAX, false, 3, S, 1, 4>, lds, a, ws, E, M, es0, es1, st);
-            case 4: return launch_grouped_one(k_grouped<F, MTMAX, false, 4, S, 1, 3>, lds, a, ws, E, M, es0, es1, st);
-            default: return launch_grouped_one(k_grouped<F, MTMAX, false, 6, S, 1, 2>, lds, a, ws, E, M, es0, es1, st);
+            case 1: return launch_grouped_one(k_grouped<F, MTMAX, false, 1, S, 1, 4>, lds, a, ws, E, M, es0, es1, tm, st);
+            case 2: return launch_grouped_one(k_grouped<F, MTMAX, false, 2, S, 1, 4>, lds, a, ws, E, M, es0, es1, tm, st);
+            case 3: return launch_grouped_one(k_grouped<F, MTMAX, false, 3, S, 1, 4>, lds, a, ws, E, M, es0, es1, tm, st);
+            case 4: return launch_grouped_one(k_grouped<F, MTMAX, false, 4, S, 1, 3>, lds, a, ws, E, M, es0, es1, tm, st);
+            default: return launch_grouped_one(k_grouped<F, MTMAX, false, 6, S, 1, 2>, lds, a, ws, E, M, es0, es1, tm, st);
         }
     }
     return hipErrorInvalidValue;
@@ -330,13 +398,13 @@ static hipError_t grouped_paths(StreamArgs a, const int32_t* ws, int64_t E, int6
 
 template <int F>
 static hipError_t grouped_mt(const StreamArgs& a, int mtmax, const int32_t* ws, int64_t E, int64_t M, int64_t es0,
-                             int64_t es1, hipStream_t st) {
+                             int64_t es1, int tm, hipStream_t st) {
     switch (mtmax) {
-        case 1: return grouped_paths<F, 1>(a, ws, E, M, es0, es1, st);
-        case 2: return grouped_paths<F, 2>(a, ws, E, M, es0, es1, st);
-        case 4: return grouped_paths<F, 4>(a, ws, E, M, es0, es1, st);
-        case 8: return grouped_paths<F, 8>(a, ws, E, M, es0, es1, st);
-        default: return grouped_paths<F, 16>(a, ws, E, M, es0, es1, st);
+        case 1: return grouped_paths<F, 1>(a, ws, E, M, es0, es1, tm, st);
+        case 2: return grouped_paths<F, 2>(a, ws, E, M, es0, es1, tm, st);
+        case 4: return grouped_paths<F, 4>(a, ws, E, M, es0, es1, tm, st);
+        case 8: return grouped_paths<F, 8>(a, ws, E, M, es0, es1, tm, st);
+        default: return grouped_paths<F, 16>(a, ws, E, M, es0, es1, tm, st);
     }
 }
 
@@ -357,19 +425,40 @@ hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int6
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    // 2. rows per pass: room for the expected rows per distinct expert (twice the
-    // mean, at least 1), as LDS allows
+    // 2. the matrix-core tiles take the experts with at least kMfmaMinRows rows
+    // (none can have as many when M is smaller)
+    const bool tiles = M >= kMfmaMinRows && mfma_kquant_supported(fmt, a.K);
+    const int tm = tiles ? kMfmaMinRows : INT_MAX;
     const int64_t S = ws_slots(E, M);
+    if (tiles) {
+        // tile height from the mean rows per distinct expert
+        const int bm = M / S >= 128 ? 128 : 64;
+        KqGroup g;
+        g.ws = ws;
+        g.S = (int)S;
+        g.list = (int)ws_tile_list(E, M, bm);
+        g.count = bm == 128 ? 2 : 1;
+        g.cap = (int)ws_tile_cap(M);
+        g.es0 = estride0;
+        g.es1 = estride1;
+        g.xdiv = a.xdiv > 1 ? a.xdiv : 1;
+        hipError_t e = launch_mfma_kquant_grouped(fmt, a.w0, a.w1, a.gbytes, a.N, a.K, a.x, a.ldx, a.y, a.ldy, g,
+                                                  bm, st);
+        if (e != hipSuccess) return e;
+    }
+    // 3. rows per pass of the streaming kernel: room for the expected rows per
+    // distinct expert (twice the mean, at least 1, below the tiles' threshold),
+    // as LDS allows
     int64_t want = 2 * ((M + S - 1) / S);
     int mtmax = want <= 1 ? 1 : want <= 2 ? 2 : want <= 4 ? 4 : want <= 8 ? 8 : 16;
     while (mtmax > 1 && stream_lds_bytes(fmt, a.K, mtmax) > (size_t)kLdsBytes) mtmax >>= 1;
     switch (fmt) {
-        case QG_Q8_0: return grouped_mt<QG_Q8_0>(a, mtmax, ws, E, M, estride0, estride1, st);
-        case QG_Q4_K: return grouped_mt<QG_Q4_K>(a, mtmax, ws, E, M, estride0, estride1, st);
-        case QG_Q5_K: return grouped_mt<QG_Q5_K>(a, mtmax, ws, E, M, estride0, estride1, st);
-        case QG_Q6_K: return grouped_mt<QG_Q6_K>(a, mtmax, ws, E, M, estride0, estride1, st);
-        case QG_FP8: return grouped_mt<QG_FP8>(a, mtmax, ws, E, M, estride0, estride1, st);
-        default: return grouped_mt<QG_NVFP4>(a, mtmax, ws, E, M, estride0, estride1, st);
+        case QG_Q8_0: return grouped_mt<QG_Q8_0>(a, mtmax, ws, E, M, estride0, estride1, tm, st);
+        case QG_Q4_K: return grouped_mt<QG_Q4_K>(a, mtmax, ws, E, M, estride0, estride1, tm, st);
+        case QG_Q5_K: return grouped_mt<QG_Q5_K>(a, mtmax, ws, E, M, estride0, estride1, tm, st);
+        case QG_Q6_K: return grouped_mt<QG_Q6_K>(a, mtmax, ws, E, M, estride0, estride1, tm, st);
+        case QG_FP8: return grouped_mt<QG_FP8>(a, mtmax, ws, E, M, estride0, estride1, tm, st);
+        default: return grouped_mt<QG_NVFP4>(a, mtmax, ws, E, M, estride0, estride1, tm, st);
     }
 }
 

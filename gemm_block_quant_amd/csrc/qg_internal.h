@@ -54,6 +54,22 @@ bool mfma_kquant_supported(int fmt, int K);
 // tensor scale (unused otherwise).
 hipError_t launch_mfma_kquant(int fmt, const uint8_t* w, const uint8_t* w1, const uint8_t* gbytes, int N, int K,
                               const uint16_t* x, int64_t ldx, int M, float* y, int64_t ldy, hipStream_t st);
+// The same tiles over the row tiles of a grouped product's bucketing
+// workspace: tile t of the list at ws[list ..] (count at ws[count], at most
+// cap entries) is rows [p, p + bm) of the sorted rows of slot q, (p, q) =
+// ws[list + 2 t], ws[list + 2 t + 1], cut at the slot's end; x row perm / xdiv
+// in, y row perm out, the weights of the slot's expert (es0 and es1 bytes per
+// expert in the two planes; NVFP4: 4 bytes of tensor scale per expert).
+struct KqGroup {
+    const int32_t* ws;
+    int S;             // slots of the layout
+    int list, count, cap;
+    int64_t es0, es1;
+    int xdiv;          // 1: x row = sorted row's original index
+};
+hipError_t launch_mfma_kquant_grouped(int fmt, const uint8_t* w, const uint8_t* w1, const uint8_t* gbytes, int N,
+                                      int K, const uint16_t* x, int64_t ldx, float* y, int64_t ldy, const KqGroup& g,
+                                      int bm, hipStream_t st);
 int num_cus();
 
 // Element-wise steps of the mixture-of-experts block (qg_moe.hip).

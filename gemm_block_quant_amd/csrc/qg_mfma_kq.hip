@@ -285,8 +285,10 @@ template <> struct KqFmt<QG_NVFP4> {
 
 // D: K steps of loads in flight in the register ring (an even number).
 // BN: 64, or 128 for the formats without per-sub-block terms.
-template <int F, int BM, int BN, int D>
-__global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
+// G: grouped product, row tile blockIdx.y of g's list (rows through the
+// bucketing permutation, the weights of the tile's expert).
+template <int F, int BM, int BN, int D, bool G>
+__global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a_in, const KqGroup g) {
     using Fmt = KqFmt<F>;
     constexpr int TPR = kMfmaThreads / BN;  // threads per weight row (4 or 2)
     constexpr int QPT = 4 / TPR;            // quarters of a row's step decoded per thread
@@ -306,10 +308,26 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem_generic[2 * BUF];
     lds_u8* smem = (lds_u8*)smem_generic;
 
+    KqArgs a = a_in;
+    int m0 = blockIdx.y * BM, M = a.M;
+    const int32_t* prow = nullptr;  // grouped: original index of the tile's row i at prow[i]
+    if constexpr (G) {
+        const int t = blockIdx.y;
+        if (t >= g.ws[g.count]) return;  // uniform: past the listed tiles
+        const int p = g.ws[g.list + 2 * t], q = g.ws[g.list + 2 * t + 1];
+        const int e = g.ws[4 + q];
+        const int r1 = g.ws[4 + g.S + q + 1];
+        a.w += (size_t)e * g.es0;
+        if (a.w1) a.w1 += (size_t)e * g.es1;
+        if (a.gbytes) a.gbytes += 4 * (size_t)e;
+        prow = g.ws + 5 + 2 * g.S + p;
+        m0 = 0;
+        M = min(BM, r1 - p);
+    }
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int n0 = blockIdx.x * BN;
     const int wm = (wid >> 1) * (BM / 2), wn = (wid & 1) * (BN / 2);
-    const int M = a.M, N = a.N;
+    const int N = a.N;
     const int nsteps = a.K / kMfmaKStep;  // K is a multiple of 64
 
     // Register ring: activation chunks and this thread's weight share.
@@ -324,7 +342,9 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
 #pragma unroll
     for (int c = 0; c < XCH; ++c) {
         const int i = tid + c * kMfmaThreads;
-        xp[c] = a.x + (size_t)min(m0 + (i >> 3), M - 1) * a.ldx + Fmt::x_chunk(i & 7);
+        const int r = min(m0 + (i >> 3), M - 1);
+        const int64_t xrow = G ? prow[r] / g.xdiv : r;
+        xp[c] = a.x + (size_t)xrow * a.ldx + Fmt::x_chunk(i & 7);
     }
     const size_t wrow_n = (size_t)(n0 + wrow_i < N ? n0 + wrow_i : 0);
     const uint8_t* wrow = a.w + wrow_n * a.rb;
@@ -514,8 +534,10 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m < M && n < N)
-                    st_global_f32(a.y + (size_t)m * a.ldy + n, Fmt::ROWSCALE ? acc[i][j][r] * rs : acc[i][j][r]);
+                if (m < M && n < N) {
+                    const int64_t yrow = G ? prow[m] : m;
+                    st_global_f32(a.y + (size_t)yrow * a.ldy + n, Fmt::ROWSCALE ? acc[i][j][r] * rs : acc[i][j][r]);
+                }
             }
     }
 }
@@ -528,16 +550,31 @@ template <int F>
 static hipError_t launch_kq(const KqArgs& a, hipStream_t st) {
     const long cus = num_cus();
     auto tiles = [&](int bm, int bn) { return (long)((a.N + bn - 1) / bn) * ((a.M + bm - 1) / bm); };
+    const KqGroup none{};
     if (KqFmt<F>::ROWSCALE && tiles(128, 128) >= 2 * cus) {
         dim3 grid((a.N + 127) / 128, (a.M + 127) / 128);
-        hipLaunchKernelGGL((k_mfma_kq<F, 128, KqFmt<F>::ROWSCALE ? 128 : 64, 2>), grid, dim3(kMfmaThreads), 0, st, a);
+        hipLaunchKernelGGL((k_mfma_kq<F, 128, KqFmt<F>::ROWSCALE ? 128 : 64, 2, false>), grid, dim3(kMfmaThreads), 0,
+                           st, a, none);
     } else if (tiles(128, 64) >= cus) {
         dim3 grid((a.N + 63) / 64, (a.M + 127) / 128);
-        hipLaunchKernelGGL((k_mfma_kq<F, 128, 64, 2>), grid, dim3(kMfmaThreads), 0, st, a);
+        hipLaunchKernelGGL((k_mfma_kq<F, 128, 64, 2, false>), grid, dim3(kMfmaThreads), 0, st, a, none);
     } else {
         dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
-        hipLaunchKernelGGL((k_mfma_kq<F, 64, 64, 4>), grid, dim3(kMfmaThreads), 0, st, a);
+        hipLaunchKernelGGL((k_mfma_kq<F, 64, 64, 4, false>), grid, dim3(kMfmaThreads), 0, st, a, none);
     }
+    return hipGetLastError();
+}
+
+// Grouped: one row of workgroups per possible list entry (g.cap); those past
+// the listed count exit at once.
+template <int F>
+static hipError_t launch_kq_grouped(const KqArgs& a, const KqGroup& g, int bm, hipStream_t st) {
+    if (g.cap <= 0) return hipSuccess;
+    dim3 grid((a.N + 63) / 64, g.cap);
+    if (bm == 128)
+        hipLaunchKernelGGL((k_mfma_kq<F, 128, 64, 2, true>), grid, dim3(kMfmaThreads), 0, st, a, g);
+    else
+        hipLaunchKernelGGL((k_mfma_kq<F, 64, 64, 4, true>), grid, dim3(kMfmaThreads), 0, st, a, g);
     return hipGetLastError();
 }
 
@@ -553,17 +590,45 @@ bool mfma_kquant_supported(int fmt, int K) {
     }
 }
 
+// Bytes per weight row in the format's first plane (and, for NVFP4, the second).
+static bool kq_row_bytes(int fmt, int K, KqArgs& a) {
+    switch (fmt) {
+        case QG_Q4_K: a.rb = (int64_t)(K / 256) * 144; return true;
+        case QG_Q5_K: a.rb = (int64_t)(K / 256) * 176; return true;
+        case QG_Q6_K: a.rb = (int64_t)(K / 256) * 210; return true;
+        case QG_Q8_0: a.rb = (int64_t)(K / 32) * 34; return true;
+        case QG_FP8: a.rb = K; return true;
+        case QG_NVFP4: a.rb = K / 2; a.rb1 = K / 16; return true;
+        default: return false;
+    }
+}
+
 hipError_t launch_mfma_kquant(int fmt, const uint8_t* w, const uint8_t* w1, const uint8_t* gbytes, int N, int K,
                               const uint16_t* x, int64_t ldx, int M, float* y, int64_t ldy, hipStream_t st) {
     KqArgs a = {x, ldx, w, w1, gbytes, 0, 0, y, ldy, M, N, K};
+    if (!kq_row_bytes(fmt, K, a)) return hipErrorInvalidValue;
     switch (fmt) {
-        case QG_Q4_K: a.rb = (int64_t)(K / 256) * 144; return launch_kq<QG_Q4_K>(a, st);
-        case QG_Q5_K: a.rb = (int64_t)(K / 256) * 176; return launch_kq<QG_Q5_K>(a, st);
-        case QG_Q6_K: a.rb = (int64_t)(K / 256) * 210; return launch_kq<QG_Q6_K>(a, st);
-        case QG_Q8_0: a.rb = (int64_t)(K / 32) * 34; return launch_kq<QG_Q8_0>(a, st);
-        case QG_FP8: a.rb = K; return launch_kq<QG_FP8>(a, st);
-        case QG_NVFP4: a.rb = K / 2; a.rb1 = K / 16; return launch_kq<QG_NVFP4>(a, st);
-        default: return hipErrorInvalidValue;
+        case QG_Q4_K: return launch_kq<QG_Q4_K>(a, st);
+        case QG_Q5_K: return launch_kq<QG_Q5_K>(a, st);
+        case QG_Q6_K: return launch_kq<QG_Q6_K>(a, st);
+        case QG_Q8_0: return launch_kq<QG_Q8_0>(a, st);
+        case QG_FP8: return launch_kq<QG_FP8>(a, st);
+        default: return launch_kq<QG_NVFP4>(a, st);
+    }
+}
+
+hipError_t launch_mfma_kquant_grouped(int fmt, const uint8_t* w, const uint8_t* w1, const uint8_t* gbytes, int N,
+                                      int K, const uint16_t* x, int64_t ldx, float* y, int64_t ldy, const KqGroup& g,
+                                      int bm, hipStream_t st) {
+    KqArgs a = {x, ldx, w, w1, gbytes, 0, 0, y, ldy, 0, N, K};
+    if (!kq_row_bytes(fmt, K, a)) return hipErrorInvalidValue;
+    switch (fmt) {
+        case QG_Q4_K: return launch_kq_grouped<QG_Q4_K>(a, g, bm, st);
+        case QG_Q5_K: return launch_kq_grouped<QG_Q5_K>(a, g, bm, st);
+        case QG_Q6_K: return launch_kq_grouped<QG_Q6_K>(a, g, bm, st);
+        case QG_Q8_0: return launch_kq_grouped<QG_Q8_0>(a, g, bm, st);
+        case QG_FP8: return launch_kq_grouped<QG_FP8>(a, g, bm, st);
+        default: return launch_kq_grouped<QG_NVFP4>(a, g, bm, st);
     }
 }
 

@@ -82,7 +82,8 @@
  * such a call is bitwise equal to quant_grouped_gemm with E = 1 and ids =
  * NULL.  Calls with M >= 32 that run on the matrix cores (below) accumulate
  * in another (still fixed) order: their rows do not depend on M or on the
- * other rows.
+ * other rows, and they too equal quant_grouped_gemm with E = 1 and ids = NULL
+ * bit for bit (QG_NVFP4 with K % 64 != 0 aside).
  */
 #ifndef QUANTGEMM_H
 #define QUANTGEMM_H
@@ -166,7 +167,11 @@ size_t quant_grouped_workspace_bytes(int64_t E, int64_t M);
  * Rows are bucketed by expert on the device so that each distinct expert's
  * weights are read once per call, whatever the number of rows routed to it
  * ("A 320B MoE on a free Kaggle TPU", section "The decode kernel's cost is not
- * distinct experts").
+ * distinct experts"): an expert with fewer than 32 rows streams its weights
+ * once for all its rows; one with 32 or more runs on the matrix-core tiles of
+ * quant_gemm over its rows (64- or 128-row tiles; the weights are read once
+ * per tile of rows, the repeats from cache), except for QG_NVFP4 with
+ * K % 64 != 0 and QG_Q8_0 with K % 64 == 32, which always stream.
  * An id outside [0, E) cannot be reported without a synchronization: every
  * element of that row of y is set to NaN.
  * workspace: device scratch of at least quant_grouped_workspace_bytes(E, M)
@@ -184,7 +189,7 @@ qg_status quant_grouped_gemm(const void* w, qg_format fmt, int64_t E, int64_t N,
  * harnesses that forbid allocation.  Same arguments, results (bit for bit),
  * limits and errors as quant_grouped_gemm; it allocates nothing and calls no
  * allocating routine.  Its bucketing scratch is a static device array of
- * 196,864 bytes inside the library (enough for the largest call, M = 16384;
+ * 204,832 bytes inside the library (enough for the largest call, M = 16384;
  * QG_EWORKSPACE if a call ever needed more), one copy per GPU, held until the
  * process ends.  The first call on each device resolves that copy's address
  * (a host-side query; make it outside graph capture).  Every call on one GPU

@@ -87,3 +87,74 @@ def test_grouped_moe_layer(N, K):
     y = qg.quant_grouped_gemm(dev_bytes(w), qg.Q4_K, E, N, K, T * topk, dev_x(x), _ids_dev(ids)).cpu().numpy()
     y_ref, bound = oracle.gemm(qg.Q4_K, w, N, K, x, E=E, ids=ids)
     assert_band(y, y_ref, bound, "moe N %d K %d" % (N, K))
+
+
+def _slot_ids(sizes, E, seed, invalid=2):
+    """ids giving expert e sizes[e] rows (shuffled), plus `invalid` rows with bad ids."""
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(sizes)] +
+                         [np.array([-1, E] * (invalid // 2), np.int32)])
+    return ids[np.random.default_rng(seed).permutation(len(ids))]
+
+
+def _expert_weights(fmt, w, E, N, K, e):
+    """Packed bytes of expert e alone (the planes of a stacked tensor cut out)."""
+    R = E * N
+    if fmt == qg.NVFP4:
+        codes = w[e * N * K // 2:(e + 1) * N * K // 2]
+        sc = w[R * K // 2 + e * N * K // 16: R * K // 2 + (e + 1) * N * K // 16]
+        gs = w[R * K // 2 + R * K // 16 + 4 * e: R * K // 2 + R * K // 16 + 4 * e + 4]
+        return np.concatenate([codes, sc, gs])
+    if fmt == qg.FP8:
+        return np.concatenate([w[e * N * K:(e + 1) * N * K], w[R * K + 4 * e * N: R * K + 4 * (e + 1) * N]])
+    eb = oracle.packed_bytes(fmt, 1, N, K)
+    return w[e * eb:(e + 1) * eb]
+
+
+# slot sizes around the tile threshold (32) and the tile heights (64, 128):
+# the mean rows per expert picks 64-row tiles in the first shape, 128 in the second
+@pytest.mark.parametrize("sizes", [(32, 31, 64, 65, 129, 1, 0), (300, 140, 40, 7)])
+@pytest.mark.parametrize("fmt,K", [(qg.Q4_K, 512), (qg.Q6_K, 512), (qg.Q8_0, 512), (qg.NVFP4, 512), (qg.FP8, 512),
+                                   (qg.Q5_K, 512), (qg.NVFP4, 528), (qg.Q8_0, 544)])
+def test_grouped_large_experts_on_tiles(fmt, K, sizes):
+    """Experts with 32 or more rows run on the matrix-core tiles (each expert's
+    weights read once per tile of rows), the others stream; every output
+    against the oracle, and the tiled experts' rows bit for bit equal to the
+    dense product over that expert's rows.  (NVFP4 with K % 64 = 16 and Q8_0
+    with K % 64 = 32 have no grouped tile path: all their experts stream; the
+    dense Q8_0 product then streams too, the dense NVFP4 one has a tile kernel
+    of its own.)"""
+    import torch
+    E, N = len(sizes), 96
+    w = synth.weights(fmt, synth.rng(25, fmt), E * N, K, E=E)
+    ids = _slot_ids(sizes, E, 26 + fmt)
+    M = len(ids)
+    x = synth.x_bf16(synth.rng(25, 10 + fmt), M, K)
+    wd, xd = dev_bytes(w), dev_x(x)
+    y = qg.quant_grouped_gemm(wd, fmt, E, N, K, M, xd, _ids_dev(ids)).cpu().numpy()
+    bad = (ids < 0) | (ids >= E)
+    assert np.isnan(y[bad]).all()
+    y_ref, bound = oracle.gemm(fmt, w, N, K, x, E=E, ids=ids)
+    assert_band(y[~bad], y_ref[~bad], bound[~bad], "grouped tiles fmt %d K %d" % (fmt, K))
+    if fmt == qg.NVFP4 and K % 64:
+        return  # the dense product has its own NVFP4 tile kernel for such K: equal in band only
+    for e, c in enumerate(sizes):
+        if c < 32:
+            continue
+        rows = np.nonzero(ids == e)[0]
+        we = dev_bytes(_expert_weights(fmt, w, E, N, K, e))
+        yd = qg.quant_gemm(we, fmt, N, K, c, xd[torch.from_numpy(rows).cuda()].contiguous()).cpu().numpy()
+        assert same_bits(y[rows], yd), (fmt, K, e, c)
+
+
+@pytest.mark.parametrize("fmt,K", [(qg.Q4_K, 1024), (qg.Q6_K, 512), (qg.NVFP4, 512), (qg.Q8_0, 512)])
+def test_grouped_e1_is_dense_bitwise_on_tiles(fmt, K):
+    """E = 1 with ids = NULL and M >= 32 is the dense matrix-core product bit
+    for bit (both take the tiles), at tile heights 64 and 128."""
+    N = 200
+    w = synth.weights(fmt, synth.rng(27, fmt), N, K)
+    for M in (45, 300):
+        x = synth.x_bf16(synth.rng(27, M), M, K)
+        wd, xd = dev_bytes(w), dev_x(x)
+        yd = qg.quant_gemm(wd, fmt, N, K, M, xd).cpu().numpy()
+        yg = qg.quant_grouped_gemm(wd, fmt, 1, N, K, M, xd, None).cpu().numpy()
+        assert same_bits(yg, yd), (fmt, K, M)

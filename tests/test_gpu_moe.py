@@ -83,3 +83,18 @@ def test_moe_block_glm_shape():
     y = _run(fg, w_gu, fd, w_dn, E, D, F, x, idx, wts)
     y_ref, bound = oracle.moe_block(fg, w_gu, fd, w_dn, E, D, F, x, idx, wts)
     assert_band(y, y_ref, bound, "moe GLM shape")
+
+
+@pytest.mark.parametrize("fg,fd", [(qg.Q4_K, qg.Q6_K), (qg.NVFP4, qg.FP8)])
+def test_moe_block_prefill_large_experts(fg, fd):
+    """Prefill-sized routing: 64 tokens x top-4 over 8 experts, so most experts
+    get 32 or more pairs (the matrix-core tiles) and some fewer (streaming);
+    every output against the oracle."""
+    E, D, F, T, topk = 8, 256, 512, 64, 4
+    w_gu, w_dn, x, idx, wts = _case(fg, fd, E, D, F, T, topk, 90 + fg)
+    idx[5] = [0, 1, 2, 3]  # make sure expert 0..3 are shared widely
+    counts = np.bincount(idx.ravel(), minlength=E)
+    assert counts.max() >= 32
+    y = _run(fg, w_gu, fd, w_dn, E, D, F, x, idx, wts)
+    y_ref, bound = oracle.moe_block(fg, w_gu, fd, w_dn, E, D, F, x, idx, wts)
+    assert_band(y, y_ref, bound, "moe prefill %d/%d" % (fg, fd))
