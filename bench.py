@@ -486,8 +486,11 @@ def _counter_means(out_dir: str, counter: str):
 def pmc_summary(fetch_dir: str, write_dir: str, key: str, fetch_cmd: str, write_cmd: str):
     """Turn a FETCH_SIZE run and a WRITE_SIZE run (each over bench.py --calibrate-copy)
     into calibrated bytes per call, stored under `key` in profiles/traffic.json."""
+    # a step of the MoE-layer workload is three grouped calls (gate, up, down), each
+    # dispatching the same kernels: the per-dispatch means count one of the three
+    calls = 3 if workloads()[key].layer else 1
     out = {"source_hash": kernel_source_hash(), "fetch_command": fetch_cmd, "write_command": write_cmd,
-           "copy_bytes_each_way": COPY_ELEMS * 4}
+           "copy_bytes_each_way": COPY_ELEMS * 4, "calls_per_step": calls}
     for name, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         means = _counter_means(d, counter)
         # the product kernels of one call (not the streaming-read reference)
@@ -496,7 +499,7 @@ def pmc_summary(fetch_dir: str, write_dir: str, key: str, fetch_cmd: str, write_
         if not ours or not copy:
             raise SystemExit("pmc summary: no %s rows for %s in %s" % (counter, "our kernels" if not ours else "the copy", d))
         factor = COPY_ELEMS * 4 / (copy[0] * 1024)
-        per_call_kib = sum(ours.values())
+        per_call_kib = calls * sum(ours.values())
         out[name + "_kib_per_call_raw"] = round(per_call_kib, 3)
         out[name + "_copy_kib_raw"] = round(copy[0], 3)
         out[name + "_factor"] = round(factor, 5)

@@ -16,8 +16,9 @@
 //     network in LDS (invalid ids sort last), mark where the id changes, scan,
 //     and write slot -> (expert, first sorted row) and the sorted row list.
 //     Rows whose id is outside [0, E) get NaN in every element of y.
-//     It also lists the row tiles of the experts with at least
-//     kMfmaMinRows rows, for 64- and for 128-row tiles.
+//     When the call has at least 4 rows per possible distinct expert it also
+//     lists the row tiles of the experts with at least kMfmaMinRows rows, for
+//     64- and for 128-row tiles.
 //  2. k_grouped: workgroup (slot, chunk) stages the slot's activation rows
 //     (16 at most per pass) in LDS and its 4 waves stream rows [chunk*RPC,
 //     ...) of the slot's expert through the same core as the dense product,
@@ -60,9 +61,11 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int d) {
 }
 
 // P: sort keys, a power of two >= max(M, 128); P == 128 sorts in one wave's registers.
+// lists: also list the row tiles of the slots with at least kMfmaMinRows rows
+// (else their counts are 0).
 __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __restrict__ ids, int E, int M, int P,
                                                            int32_t* __restrict__ ws, float* __restrict__ y, int N,
-                                                           int64_t ldy) {
+                                                           int64_t ldy, int lists) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     QG_LDS uint64_t* keys = (QG_LDS uint64_t*)smem_generic;                       // P keys
     QG_LDS int32_t* part = (QG_LDS int32_t*)(smem_generic + (size_t)P * 8);      // per-wave partial counts
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
     // contiguous run of slots; 64-row counts in the low and 128-row counts in
     // the high half of one scanned word (each total is at most M / 32)
     __syncthreads();  // every slot start (and ws[0]) is written
-    const int nslots = ws[0];
+    const int nslots = lists ? ws[0] : 0;
     const int sper = (nslots + nt - 1) / nt;
     const int s0 = tid * sper, s1 = min(nslots, s0 + sper);
     int tcnt = 0;
@@ -420,16 +423,23 @@ hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int6
         hipError_t e = allow_full_lds((const void*)k_bucket);
         if (e != hipSuccess) return e;
     }
+    // Row-tile lists only where an expert may plausibly reach kMfmaMinRows rows:
+    // at least 4 rows per possible distinct expert on average (a decode batch,
+    // 128 rows over 288 experts, skips the lists and the tile launch; any expert
+    // that still has that many rows then streams in passes of 16).  The choice
+    // depends on (E, M) only, so a bucketing reused by a later call (bucket ==
+    // false, same ids) matches that call's choice.
+    const int64_t S = ws_slots(E, M);
+    const bool lists = M >= kMfmaMinRows && M >= 4 * S;
     if (bucket) {
-        hipLaunchKernelGGL(k_bucket, dim3(1), dim3(nt), lds, st, ids, (int)E, (int)M, P, ws, a.y, a.N, a.ldy);
+        hipLaunchKernelGGL(k_bucket, dim3(1), dim3(nt), lds, st, ids, (int)E, (int)M, P, ws, a.y, a.N, a.ldy,
+                           (int)lists);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     // 2. the matrix-core tiles take the experts with at least kMfmaMinRows rows
-    // (none can have as many when M is smaller)
-    const bool tiles = M >= kMfmaMinRows && mfma_kquant_supported(fmt, a.K);
+    const bool tiles = lists && mfma_kquant_supported(fmt, a.K);
     const int tm = tiles ? kMfmaMinRows : INT_MAX;
-    const int64_t S = ws_slots(E, M);
     if (tiles) {
         // tile height from the mean rows per distinct expert
         const int bm = M / S >= 128 ? 128 : 64;

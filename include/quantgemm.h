@@ -167,11 +167,13 @@ size_t quant_grouped_workspace_bytes(int64_t E, int64_t M);
  * Rows are bucketed by expert on the device so that each distinct expert's
  * weights are read once per call, whatever the number of rows routed to it
  * ("A 320B MoE on a free Kaggle TPU", section "The decode kernel's cost is not
- * distinct experts"): an expert with fewer than 32 rows streams its weights
- * once for all its rows; one with 32 or more runs on the matrix-core tiles of
- * quant_gemm over its rows (64- or 128-row tiles; the weights are read once
- * per tile of rows, the repeats from cache), except for QG_NVFP4 with
- * K % 64 != 0 and QG_Q8_0 with K % 64 == 32, which always stream.
+ * distinct experts").  When the call has at least 4 rows per possible
+ * distinct expert (M >= 32 and M >= 4 * min(E, M)), an expert with 32 or more
+ * rows runs on the matrix-core tiles of quant_gemm over its rows (64- or
+ * 128-row tiles; its weights are read once per tile of rows, the repeats from
+ * cache), except for QG_NVFP4 with K % 64 != 0 and QG_Q8_0 with K % 64 == 32.
+ * Every other expert streams its weights for up to 16 of its rows per pass
+ * (once for all its rows when it has at most 16).
  * An id outside [0, E) cannot be reported without a synchronization: every
  * element of that row of y is set to NaN.
  * workspace: device scratch of at least quant_grouped_workspace_bytes(E, M)
