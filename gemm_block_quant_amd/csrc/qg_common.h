@@ -129,6 +129,27 @@ __device__ __forceinline__ u32x2 ld_global64_a2(const void* p) {
     return u32x2{v.x, v.y};
 }
 __device__ __forceinline__ uint32_t ld_global32_a2(const void* p) { return *(const QG_GLOBAL u32_a2*)(uintptr_t)p; }
+// 16 / 8 bytes at a 2-byte aligned address p, read as 4-byte aligned loads
+// of the 20 / 12 bytes from p rounded down to 4 bytes and shifted into place
+// (reads at most 4 bytes past p + 16 / p + 8, all inside the same 4-byte words
+// as those up to p + 18 / p + 10).
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+__device__ __forceinline__ u32x4 ld_global128_a2dw(const void* p) {
+    const uintptr_t a = (uintptr_t)p, b = a & ~(uintptr_t)3;
+    const uint32_t sh = (uint32_t)(a & 3);
+    const u32x4_a4 v = *(const QG_GLOBAL u32x4_a4*)b;
+    const uint32_t e = *(const QG_GLOBAL uint32_t*)(b + 16);
+    return u32x4{__builtin_amdgcn_alignbyte(v.y, v.x, sh), __builtin_amdgcn_alignbyte(v.z, v.y, sh),
+                 __builtin_amdgcn_alignbyte(v.w, v.z, sh), __builtin_amdgcn_alignbyte(e, v.w, sh)};
+}
+__device__ __forceinline__ u32x2 ld_global64_a2dw(const void* p) {
+    const uintptr_t a = (uintptr_t)p, b = a & ~(uintptr_t)3;
+    const uint32_t sh = (uint32_t)(a & 3);
+    const u32x2_a4 v = *(const QG_GLOBAL u32x2_a4*)b;
+    const uint32_t e = *(const QG_GLOBAL uint32_t*)(b + 8);
+    return u32x2{__builtin_amdgcn_alignbyte(v.y, v.x, sh), __builtin_amdgcn_alignbyte(e, v.y, sh)};
+}
 __device__ __forceinline__ uint32_t ld_global16(const void* p) { return *(const QG_GLOBAL uint16_t*)(uintptr_t)p; }
 __device__ __forceinline__ void st_global_f32(float* p, float v) { *(QG_GLOBAL float*)(uintptr_t)p = v; }
 

@@ -516,11 +516,17 @@ template <> struct Direct<QG_Q6_K> {
     __device__ static Offs pick(bool c, const Offs& x, const Offs& y) {
         return Offs{c ? x.a : y.a, c ? x.b : y.b, c ? x.c : y.c, c ? x.d : y.d};
     }
+    // DW: the 16- and 8-byte fields (2-byte aligned: 210-byte blocks) read as
+    // 4-byte aligned loads shifted into place.  Measured: the LM head (whole
+    // rows, 1 GB) 238 -> 210 us, its loads being address-unit bound; the
+    // 5120-row down projections (K segments, latency-bound) 25.6 -> 28.0 us,
+    // so those keep the unaligned 16-byte loads.
+    template <bool DW = false>
     __device__ static void load_at(uint32_t (&r)[REGS], const uint8_t* b0, const uint8_t*, const Offs& o) {
-        const u32x4 qa = ld_global128_a2(b0 + o.a);
-        const u32x4 qb = ld_global128_a2(b0 + o.a + 32);
-        const u32x4 qh = ld_global128_a2(b0 + o.b);
-        const u32x2 sc = ld_global64_a2(b0 + o.c);
+        const u32x4 qa = DW ? ld_global128_a2dw(b0 + o.a) : ld_global128_a2(b0 + o.a);
+        const u32x4 qb = DW ? ld_global128_a2dw(b0 + o.a + 32) : ld_global128_a2(b0 + o.a + 32);
+        const u32x4 qh = DW ? ld_global128_a2dw(b0 + o.b) : ld_global128_a2(b0 + o.b);
+        const u32x2 sc = DW ? ld_global64_a2dw(b0 + o.c) : ld_global64_a2(b0 + o.c);
         r[0] = qa.x; r[1] = qa.y; r[2] = qa.z; r[3] = qa.w;
         r[4] = qb.x; r[5] = qb.y; r[6] = qb.z; r[7] = qb.w;
         r[8] = qh.x; r[9] = qh.y; r[10] = qh.z; r[11] = qh.w;
@@ -844,8 +850,11 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
             const bool partial = (pass + 1) * G > U;
             // no work: every lane loads the first bytes of the last row group
             // (one line; nothing streams for a dead slot)
-            D::load_at(r[p], cur_b0 + (size_t)pass * D::PASS0, cur_b1 + (size_t)pass * D::PASS1,
-                       D::pick(live, D::pick(partial, cur_ol, cur_o), typename D::Offs{}));
+            const typename D::Offs o = D::pick(live, D::pick(partial, cur_ol, cur_o), typename D::Offs{});
+            if constexpr (F == QG_Q6_K && !SEG)
+                D::template load_at<true>(r[p], cur_b0 + (size_t)pass * D::PASS0, cur_b1 + (size_t)pass * D::PASS1, o);
+            else
+                D::load_at(r[p], cur_b0 + (size_t)pass * D::PASS0, cur_b1 + (size_t)pass * D::PASS1, o);
         }
         slast = false;
         if (live) {
