@@ -470,8 +470,8 @@ def copy_calibration():
     torch.cuda.synchronize()
 
 
-def _counter_means(out_dir: str, counter: str):
-    """{kernel name: mean counter value per dispatch} from rocprofv3 counter CSVs under out_dir."""
+def _counter_values(out_dir: str, counter: str):
+    """{kernel name: [counter value of each dispatch]} from rocprofv3 counter CSVs under out_dir."""
     import csv
     import glob
     vals = {}
@@ -480,31 +480,37 @@ def _counter_means(out_dir: str, counter: str):
             for row in csv.DictReader(fh):
                 if row["Counter_Name"] == counter:
                     vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in vals.items()}
+    return vals
 
 
 def pmc_summary(fetch_dir: str, write_dir: str, key: str, fetch_cmd: str, write_cmd: str):
     """Turn a FETCH_SIZE run and a WRITE_SIZE run (each over bench.py --calibrate-copy)
     into calibrated bytes per call, stored under `key` in profiles/traffic.json."""
-    # a step of the MoE-layer workload is three grouped calls (gate, up, down), each
-    # dispatching the same kernels: the per-dispatch means count one of the three
-    calls = 3 if workloads()[key].layer else 1
+    # Per step: the counters of every dispatch of the product kernels, divided by
+    # the number of steps profiled.  A grouped call dispatches the bucketing once,
+    # so the bucketing's dispatch count is the number of grouped calls; a step of
+    # the MoE-layer workload is three of them (gate, up, down), a step of the MoE
+    # block one.  Dense products dispatch one kernel per call.
+    wl = workloads().get(key)
+    calls = 3 if wl is not None and wl.layer else 1
     out = {"source_hash": kernel_source_hash(), "fetch_command": fetch_cmd, "write_command": write_cmd,
            "copy_bytes_each_way": COPY_ELEMS * 4, "calls_per_step": calls}
     for name, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
-        means = _counter_means(d, counter)
-        # the product kernels of one call (not the streaming-read reference)
-        ours = {k: v for k, v in means.items() if "qg::" in k and "k_read_probe" not in k}
-        copy = [v for k, v in means.items() if "neg" in k.lower() and "qg::" not in k]
+        vals = _counter_values(d, counter)
+        # the product kernels (not the streaming-read reference)
+        ours = {k: v for k, v in vals.items() if "qg::" in k and "k_read_probe" not in k}
+        copy = [sum(v) / len(v) for k, v in vals.items() if "neg" in k.lower() and "qg::" not in k]
         if not ours or not copy:
             raise SystemExit("pmc summary: no %s rows for %s in %s" % (counter, "our kernels" if not ours else "the copy", d))
         factor = COPY_ELEMS * 4 / (copy[0] * 1024)
-        per_call_kib = calls * sum(ours.values())
+        bucket = [len(v) for k, v in ours.items() if "k_bucket" in k]
+        steps = (bucket[0] / calls) if bucket else max(len(v) for v in ours.values())
+        per_call_kib = sum(sum(v) for v in ours.values()) / steps
         out[name + "_kib_per_call_raw"] = round(per_call_kib, 3)
         out[name + "_copy_kib_raw"] = round(copy[0], 3)
         out[name + "_factor"] = round(factor, 5)
         out[name + "_bytes"] = int(round(per_call_kib * 1024 * factor))
-        out[name + "_kernels"] = {k: round(v, 3) for k, v in ours.items()}
+        out[name + "_kernels"] = {k: round(sum(v) / steps, 3) for k, v in ours.items()}
     try:
         with open(TRAFFIC_FILE) as f:
             allt = json.load(f)

@@ -67,6 +67,32 @@ def test_traffic_summary_scales_by_the_copy_and_is_gated_by_the_source_hash(tmp_
     assert b.traffic_for("shape") is None
 
 
+def test_traffic_summary_counts_every_dispatch_of_a_grouped_step(tmp_path, monkeypatch):
+    """A MoE-layer step is three grouped calls, each one bucketing and one
+    product dispatch: the traffic of a step is every dispatch's counter over
+    the number of steps (bucketing dispatches / 3)."""
+    b = _bench()
+    monkeypatch.setattr(b, "PROFILES", str(tmp_path))
+    monkeypatch.setattr(b, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    bucket = "qg::k_bucket(int const*, int, int, int, int*, float*, int, long, int)"
+    grouped = "void qg::k_grouped<2, 2, true, 1, 0, 1, 3>(qg::StreamArgs, int const*, long, long, int, int, long, long, int)"
+    neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>"
+    copy_kib = b.COPY_ELEMS * 4 / 1024
+    # two steps: gate, up and down products of 100, 200 and 300 KiB, 1 KiB per bucketing
+    rows = []
+    for _ in range(2):
+        for kib in (100.0, 200.0, 300.0):
+            rows += [(bucket, "FETCH_SIZE", 1.0), (grouped, "FETCH_SIZE", kib)]
+    _counter_csv(str(tmp_path / "fetch"), rows + [(neg, "FETCH_SIZE", copy_kib)])
+    _counter_csv(str(tmp_path / "write"), [(bucket, "WRITE_SIZE", 0.0)] * 6 + [(grouped, "WRITE_SIZE", 2.0)] * 6 +
+                 [(neg, "WRITE_SIZE", copy_kib)])
+    b.pmc_summary(str(tmp_path / "fetch"), str(tmp_path / "write"), "moe_layer", "", "")
+    d = json.load(open(tmp_path / "traffic.json"))["moe_layer"]
+    assert d["calls_per_step"] == 3
+    assert d["fetch_bytes"] == (600 + 3) * 1024
+    assert d["write_bytes"] == 6 * 1024
+
+
 def test_traffic_summary_without_the_copy_is_an_error(tmp_path, monkeypatch):
     b = _bench()
     monkeypatch.setattr(b, "PROFILES", str(tmp_path))
