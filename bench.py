@@ -89,6 +89,8 @@ def workloads():
                              moe=(16, 8)),
         "moe_down": Workload("Q4_K grouped experts down, E=288 N=4096 K=2048", qg.Q4_K, 4096, 2048, 128, 5, E=288,
                              moe=(16, 8)),
+        "moe_prefill": Workload("Q4_K grouped experts prefill, E=8 N=2048 K=4096, 4096 tokens x top-4 "
+                                "(about 2,048 rows per expert)", qg.Q4_K, 2048, 4096, 16384, 8, E=8, moe=(4096, 4)),
         "moe_block": Workload("Q4_K MoE block (gate|up, SwiGLU, down, combine), E=288 D=4096 F=2048, 16 tokens x "
                               "top-8", qg.Q4_K, 2 * 2048, 4096, 128, 5, E=288, block=(qg.Q4_K, 2048, 16, 8)),
         "moe_layer": Workload("Q4_K grouped MoE layer (gate, up, down products), E=288 experts of 4096x2048, "
@@ -600,7 +602,7 @@ def result_for(p: Prepared, steps: int, warmup: int, key: str = None, probe: Rea
     if wl.layer:
         r["grouped_calls_per_step"] = 3
         r["routings_cycled"] = LAYER_ROUTINGS
-    if wl.M >= 32 and not wl.block and not wl.layer and not wl.moe:
+    if wl.M >= 32 and not wl.block and not wl.layer:
         flops = 2.0 * wl.M * wl.N * wl.K
         r["TFLOPs"] = round(flops / (total / steps) / 1e12, 1)
         r["pct_bf16_mfma_peak"] = round(100 * flops / (total / steps) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 2)

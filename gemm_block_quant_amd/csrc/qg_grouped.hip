@@ -12,10 +12,11 @@
 // pair that selects it; its prefill path sorts slots by expert, which is what
 // the bucketing kernel below does.
 //
-//  1. k_bucket (one workgroup): sort the keys (id << 32 | row) with a bitonic
-//     network in LDS (invalid ids sort last), mark where the id changes, scan,
-//     and write slot -> (expert, first sorted row) and the sorted row list.
-//     Rows whose id is outside [0, E) get NaN in every element of y.
+//  1. k_bucket (one workgroup): group the rows by expert id -- a counting sort
+//     for calls of more than 128 rows, else a bitonic sort of the keys
+//     (id << 32 | row) -- with invalid ids last, and write slot -> (expert,
+//     first sorted row) and the sorted row list.  Rows whose id is outside
+//     [0, E) get NaN in every element of y.
 //     When the call has at least 4 rows per possible distinct expert it also
 //     lists the row tiles of the experts with at least kMfmaMinRows rows, for
 //     64- and for 128-row tiles.
@@ -60,88 +61,48 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int d) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// P: sort keys, a power of two >= max(M, 128); P == 128 sorts in one wave's registers.
-// lists: also list the row tiles of the slots with at least kMfmaMinRows rows
-// (else their counts are 0).
-__global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __restrict__ ids, int E, int M, int P,
-                                                           int32_t* __restrict__ ws, float* __restrict__ y, int N,
-                                                           int64_t ldy, int lists) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
-    QG_LDS uint64_t* keys = (QG_LDS uint64_t*)smem_generic;                       // P keys
-    QG_LDS int32_t* part = (QG_LDS int32_t*)(smem_generic + (size_t)P * 8);      // per-wave partial counts
-    const int tid = threadIdx.x, nt = blockDim.x;  // nt: a multiple of 64, at most kBucketThreads
+// Counting sort by expert id (calls of more than 128 rows with E <= kCountMaxExperts):
+// one LDS counter per id (and one for invalid ids, bin E); each row takes its
+// rank inside its bin from an LDS atomic, the bins' exclusive scan gives the
+// slots and their starts, and each row lands at start + rank.  The order of the
+// rows inside a bin follows the atomics and can differ from call to call; no
+// result depends on it (every row's arithmetic is independent of which rows
+// share its pass or tile).  Rows with invalid ids sort last and get NaN rows.
+// Writes ws[0], the slots and the permutation; part: 16 ints of LDS.
+constexpr int kCountMaxExperts = 16384;
+__device__ __forceinline__ void bucket_by_counting(const int32_t* __restrict__ ids, int E, int M,
+                                                   int32_t* __restrict__ ws, float* __restrict__ y, int N,
+                                                   int64_t ldy, QG_LDS int32_t* hist, QG_LDS int32_t* part) {
+    constexpr int R = kGroupedMaxRows / kBucketThreads;  // rows per thread at most
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wv = tid >> 6;
     const int64_t S = ws_slots(E, M);
     int32_t* slot_expert = ws + 4;
     int32_t* slot_start = ws + 4 + S;
     int32_t* perm = ws + 5 + 2 * S;
-
-    for (int i = tid; i < P; i += nt) {
-        uint64_t k = ~0ull;
+    for (int b = tid; b <= E; b += nt) hist[b] = 0;
+    __syncthreads();
+    int key[R], rank[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = tid + r * nt;
+        key[r] = E;
+        rank[r] = 0;
         if (i < M) {
             const int id = ids ? ids[i] : 0;
-            const uint32_t hi = (id >= 0 && id < E) ? (uint32_t)id : 0x7fffffffu;
-            k = ((uint64_t)hi << 32) | (uint32_t)i;
+            key[r] = (id >= 0 && id < E) ? id : E;
+            rank[r] = __hip_atomic_fetch_add(hist + key[r], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-        keys[i] = k;
     }
     __syncthreads();
-    if (P == 128) {
-        // one wave (nt == 64): keys 2 t and 2 t + 1 in lane t's registers and
-        // the same bitonic network by lane shuffles (no barriers)
-        uint64_t k0 = keys[2 * tid], k1 = keys[2 * tid + 1];
-        for (int size = 2; size <= P; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                const bool up = ((2 * tid) & size) == 0;
-                if (stride == 1) {
-                    if ((k0 > k1) == up) {
-                        const uint64_t t = k0;
-                        k0 = k1;
-                        k1 = t;
-                    }
-                } else {
-                    // partner of position 2 t + e is 2 (t ^ d) + e, d = stride / 2
-                    const int d = stride >> 1;
-                    const uint64_t p0 = shfl_xor_u64(k0, d), p1 = shfl_xor_u64(k1, d);
-                    const bool keep_min = ((tid & d) == 0) == up;  // lower position of an ascending pair, or upper of a descending one
-                    k0 = keep_min ? (k0 < p0 ? k0 : p0) : (k0 > p0 ? k0 : p0);
-                    k1 = keep_min ? (k1 < p1 ? k1 : p1) : (k1 > p1 ? k1 : p1);
-                }
-            }
-        }
-        keys[2 * tid] = k0;
-        keys[2 * tid + 1] = k1;
-        __syncthreads();
-    } else {
-        // bitonic sort in LDS, ascending
-        for (int size = 2; size <= P; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int i = tid; i < P / 2; i += nt) {
-                    const int lo = 2 * i - (i & (stride - 1));
-                    const int hi = lo + stride;
-                    const bool up = (lo & size) == 0;
-                    const uint64_t a = keys[lo], b = keys[hi];
-                    if ((a > b) == up) {
-                        keys[lo] = b;
-                        keys[hi] = a;
-                    }
-                }
-                __syncthreads();
-            }
-        }
-    }
-    // heads of runs of equal valid ids -> slots (block scan over contiguous chunks)
-    const int per = (M + nt - 1) / nt;
-    const int b0 = tid * per, b1 = min(M, b0 + per);
+    // exclusive scan over the E + 1 bins of (rows, non-empty valid bins), packed
+    // as rows | bins << 16 (each total at most 16384)
+    const int per = (E + 1 + nt - 1) / nt;
+    const int b0 = tid * per, b1 = min(E + 1, b0 + per);
     int cnt = 0;
-    for (int i = b0; i < b1; ++i) {
-        const uint32_t id = (uint32_t)(keys[i] >> 32);
-        const bool valid = id != 0x7fffffffu;
-        const bool head = valid && (i == 0 || (uint32_t)(keys[i - 1] >> 32) != id);
-        cnt += head;
+    for (int b = b0; b < b1; ++b) {
+        const int c = hist[b];
+        cnt += c | ((b < E && c > 0) ? 1 << 16 : 0);
     }
-    // exclusive scan of the counts: inclusive within each wave (shuffles),
-    // then the waves' totals in order
-    const int lane = tid & 63, wv = tid >> 6;
     int inc = cnt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -157,32 +118,173 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
             part[t] = run;
             run += c;
         }
-        ws[0] = run;
+        ws[0] = run >> 16;
     }
     __syncthreads();
-    int slot = part[wv] + inc - cnt;
-    for (int i = b0; i < b1; ++i) {
-        const uint64_t k = keys[i];
-        const uint32_t id = (uint32_t)(k >> 32);
-        const bool valid = id != 0x7fffffffu;
-        const bool head = valid && (i == 0 || (uint32_t)(keys[i - 1] >> 32) != id);
-        perm[i] = (int32_t)(uint32_t)k;
-        if (head) {
-            slot_expert[slot] = (int32_t)id;
-            slot_start[slot] = i;
+    int off = (part[wv] + inc - cnt) & 0xFFFF, slot = (part[wv] + inc - cnt) >> 16;
+    for (int b = b0; b < b1; ++b) {
+        const int c = hist[b];
+        hist[b] = off;
+        if (b < E && c > 0) {
+            slot_expert[slot] = b;
+            slot_start[slot] = off;
             ++slot;
         }
+        if (b == E) slot_start[slot] = off;  // the last slot ends where the invalid rows start
+        off += c;
     }
-    if (tid == 0) {
-        // the last slot ends at the first invalid sorted position (or M)
-        int lo = 0, hi = M;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if ((uint32_t)(keys[mid] >> 32) == 0x7fffffffu) hi = mid;
-            else lo = mid + 1;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = tid + r * nt;
+        if (i < M) perm[hist[key[r]] + rank[r]] = i;
+    }
+    // NaN rows for ids outside [0, E): the last sorted positions
+    __syncthreads();
+    const int valid = hist[E];
+    for (int p = valid; p < M; ++p) {
+        const int row = perm[p];
+        for (int n = tid; n < N; n += nt) y[(int64_t)row * ldy + n] = __builtin_nanf("");
+    }
+}
+
+// P: sort keys, a power of two >= max(M, 128); P == 128 sorts in one wave's
+// registers; P == 0: counting sort (bucket_by_counting).
+// lists: also list the row tiles of the slots with at least kMfmaMinRows rows
+// (else their counts are 0).
+__global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __restrict__ ids, int E, int M, int P,
+                                                           int32_t* __restrict__ ws, float* __restrict__ y, int N,
+                                                           int64_t ldy, int lists) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
+    const int tid = threadIdx.x, nt = blockDim.x;  // nt: a multiple of 64, at most kBucketThreads
+    const int lane = tid & 63, wv = tid >> 6;
+    const int64_t S = ws_slots(E, M);
+    int32_t* slot_start = ws + 4 + S;
+    int32_t* perm = ws + 5 + 2 * S;
+    QG_LDS int32_t* part;
+    if (P == 0) {
+        QG_LDS int32_t* hist = (QG_LDS int32_t*)smem_generic;  // E + 1 bins
+        part = hist + ((E + 1 + 3) & ~3);
+        bucket_by_counting(ids, E, M, ws, y, N, ldy, hist, part);
+    } else {
+        QG_LDS uint64_t* keys = (QG_LDS uint64_t*)smem_generic;  // P keys
+        part = (QG_LDS int32_t*)(smem_generic + (size_t)P * 8);  // per-wave partial counts
+        int32_t* slot_expert = ws + 4;
+
+        for (int i = tid; i < P; i += nt) {
+            uint64_t k = ~0ull;
+            if (i < M) {
+                const int id = ids ? ids[i] : 0;
+                const uint32_t hi = (id >= 0 && id < E) ? (uint32_t)id : 0x7fffffffu;
+                k = ((uint64_t)hi << 32) | (uint32_t)i;
+            }
+            keys[i] = k;
         }
-        slot_start[ws[0]] = lo;
-    }
+        __syncthreads();
+        if (P == 128) {
+            // one wave (nt == 64): keys 2 t and 2 t + 1 in lane t's registers and
+            // the same bitonic network by lane shuffles (no barriers)
+            uint64_t k0 = keys[2 * tid], k1 = keys[2 * tid + 1];
+            for (int size = 2; size <= P; size <<= 1) {
+                for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                    const bool up = ((2 * tid) & size) == 0;
+                    if (stride == 1) {
+                        if ((k0 > k1) == up) {
+                            const uint64_t t = k0;
+                            k0 = k1;
+                            k1 = t;
+                        }
+                    } else {
+                        // partner of position 2 t + e is 2 (t ^ d) + e, d = stride / 2
+                        const int d = stride >> 1;
+                        const uint64_t p0 = shfl_xor_u64(k0, d), p1 = shfl_xor_u64(k1, d);
+                        const bool keep_min = ((tid & d) == 0) == up;  // lower position of an ascending pair, or upper of a descending one
+                        k0 = keep_min ? (k0 < p0 ? k0 : p0) : (k0 > p0 ? k0 : p0);
+                        k1 = keep_min ? (k1 < p1 ? k1 : p1) : (k1 > p1 ? k1 : p1);
+                    }
+                }
+            }
+            keys[2 * tid] = k0;
+            keys[2 * tid + 1] = k1;
+            __syncthreads();
+        } else {
+            // bitonic sort in LDS, ascending
+            for (int size = 2; size <= P; size <<= 1) {
+                for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                    for (int i = tid; i < P / 2; i += nt) {
+                        const int lo = 2 * i - (i & (stride - 1));
+                        const int hi = lo + stride;
+                        const bool up = (lo & size) == 0;
+                        const uint64_t a = keys[lo], b = keys[hi];
+                        if ((a > b) == up) {
+                            keys[lo] = b;
+                            keys[hi] = a;
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+        }
+        // heads of runs of equal valid ids -> slots (block scan over contiguous chunks)
+        const int per = (M + nt - 1) / nt;
+        const int b0 = tid * per, b1 = min(M, b0 + per);
+        int cnt = 0;
+        for (int i = b0; i < b1; ++i) {
+            const uint32_t id = (uint32_t)(keys[i] >> 32);
+            const bool valid = id != 0x7fffffffu;
+            const bool head = valid && (i == 0 || (uint32_t)(keys[i - 1] >> 32) != id);
+            cnt += head;
+        }
+        // exclusive scan of the counts: inclusive within each wave (shuffles),
+        // then the waves' totals in order
+        int inc = cnt;
+    #pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(inc, d, 64);
+            if (lane >= d) inc += v;
+        }
+        if (lane == 63) part[wv] = inc;
+        __syncthreads();
+        if (tid == 0) {
+            int run = 0;
+            for (int t = 0; t < nt / 64; ++t) {
+                const int c = part[t];
+                part[t] = run;
+                run += c;
+            }
+            ws[0] = run;
+        }
+        __syncthreads();
+        int slot = part[wv] + inc - cnt;
+        for (int i = b0; i < b1; ++i) {
+            const uint64_t k = keys[i];
+            const uint32_t id = (uint32_t)(k >> 32);
+            const bool valid = id != 0x7fffffffu;
+            const bool head = valid && (i == 0 || (uint32_t)(keys[i - 1] >> 32) != id);
+            perm[i] = (int32_t)(uint32_t)k;
+            if (head) {
+                slot_expert[slot] = (int32_t)id;
+                slot_start[slot] = i;
+                ++slot;
+            }
+        }
+        if (tid == 0) {
+            // the last slot ends at the first invalid sorted position (or M)
+            int lo = 0, hi = M;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if ((uint32_t)(keys[mid] >> 32) == 0x7fffffffu) hi = mid;
+                else lo = mid + 1;
+            }
+            slot_start[ws[0]] = lo;
+        }
+        // NaN rows for ids outside [0, E)
+        for (int i = M - 1; i >= 0; --i) {
+            if ((uint32_t)(keys[i] >> 32) != 0x7fffffffu) break;
+            const int row = (int)(uint32_t)keys[i];
+            for (int n = tid; n < N; n += nt) y[(int64_t)row * ldy + n] = __builtin_nanf("");
+        }
+    }  // bitonic
     // row tiles of the slots with at least kMfmaMinRows rows: per thread a
     // contiguous run of slots; 64-row counts in the low and 128-row counts in
     // the high half of one scanned word (each total is at most M / 32)
@@ -231,12 +333,6 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
                 list128[2 * o128 + 1] = q;
             }
         }
-    }
-    // NaN rows for ids outside [0, E)
-    for (int i = M - 1; i >= 0; --i) {
-        if ((uint32_t)(keys[i] >> 32) != 0x7fffffffu) break;
-        const int row = (int)(uint32_t)keys[i];
-        for (int n = tid; n < N; n += nt) y[(int64_t)row * ldy + n] = __builtin_nanf("");
     }
 }
 
@@ -413,12 +509,19 @@ static hipError_t grouped_mt(const StreamArgs& a, int mtmax, const int32_t* ws, 
 
 hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int64_t E, int64_t M, int32_t* ws,
                           int64_t estride0, int64_t estride1, hipStream_t st, bool bucket) {
-    // 1. bucketing
+    // 1. bucketing: a counting sort by id for calls of more than 128 rows (a
+    // bitonic sort of 16,384 keys took 176 us), else a bitonic sort of (id, row)
+    // keys (one wave up to 128 rows)
     int P = 128;
     while (P < M) P <<= 1;
     // one thread per compare-exchange of the sort (P / 2), whole waves, 64..1024
-    const int nt = P / 2 < 64 ? 64 : (P / 2 > kBucketThreads ? kBucketThreads : P / 2);
-    const size_t lds = (size_t)P * 8 + (kBucketThreads / 64) * 4;
+    int nt = P / 2 < 64 ? 64 : (P / 2 > kBucketThreads ? kBucketThreads : P / 2);
+    size_t lds = (size_t)P * 8 + (kBucketThreads / 64) * 4;
+    if (M > 128 && E <= kCountMaxExperts) {
+        P = 0;
+        nt = kBucketThreads;
+        lds = (size_t)((E + 1 + 3) & ~3) * 4 + (kBucketThreads / 64) * 4;
+    }
     {
         hipError_t e = allow_full_lds((const void*)k_bucket);
         if (e != hipSuccess) return e;

@@ -158,3 +158,33 @@ def test_grouped_e1_is_dense_bitwise_on_tiles(fmt, K):
         yd = qg.quant_gemm(wd, fmt, N, K, M, xd).cpu().numpy()
         yg = qg.quant_grouped_gemm(wd, fmt, 1, N, K, M, xd, None).cpu().numpy()
         assert same_bits(yg, yd), (fmt, K, M)
+
+
+@pytest.mark.parametrize("E,M,mode", [(20000, 300, "random"), (5000, 200, "random"), (7, 200, "invalid"),
+                                      (1, 129, "null"), (64, 129, "one"), (3, 4096, "random")])
+def test_grouped_bucketing_paths(E, M, mode):
+    """Calls of more than 128 rows bucket by counting sort (E <= 16384) or by
+    a bitonic sort of (id, row) keys (larger E): every output against the
+    oracle for many experts, all ids invalid, ids = NULL, one expert, and a
+    large call over few experts."""
+    fmt, N, K = qg.Q4_K, 8, 256
+    w = synth.weights(fmt, synth.rng(28, E % 97), E * N, K, E=E)
+    x = synth.x_bf16(synth.rng(28, M), M, K)
+    g = np.random.default_rng(E + M)
+    if mode == "random":
+        ids = g.integers(0, E, M).astype(np.int32)
+        ids[::17] = E + 3  # some invalid
+    elif mode == "invalid":
+        ids = np.full(M, -1, np.int32)
+    elif mode == "one":
+        ids = np.full(M, E - 1, np.int32)
+    else:
+        ids = None
+    y = qg.quant_grouped_gemm(dev_bytes(w), fmt, E, N, K, M, dev_x(x), None if ids is None else _ids_dev(ids))
+    y = y.cpu().numpy()
+    ids_ref = np.zeros(M, np.int32) if ids is None else ids
+    bad = (ids_ref < 0) | (ids_ref >= E)
+    assert np.isnan(y[bad]).all()
+    if (~bad).any():
+        y_ref, bound = oracle.gemm(fmt, w, N, K, x, E=E, ids=ids_ref)
+        assert_band(y[~bad], y_ref[~bad], bound[~bad], "bucketing E %d M %d %s" % (E, M, mode))
