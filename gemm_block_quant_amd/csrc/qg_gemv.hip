@@ -65,9 +65,11 @@ __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
 // about one item of the others.  The order in which waves take items does not
 // change any row's arithmetic.
 // 16 waves per workgroup; 8 where the accumulators of many activation rows
-// need more registers than 4 waves per SIMD allow.
+// need more registers than 4 waves per SIMD allow, and for one activation row
+// (two workgroups per CU then: measured 5 % faster on the Q6_K LM head and
+// down projection, 1-2 % on Q4_K and FP8, 1 % slower on NVFP4, which keeps 16).
 template <int F, int MT> constexpr int direct_waves() {
-    return MT >= 16 || ((F == QG_Q6_K || F == QG_Q5_K) && MT >= 8) ? 8 : 16;
+    return MT >= 16 || ((F == QG_Q6_K || F == QG_Q5_K) && MT >= 8) || (MT == 1 && F != QG_NVFP4) ? 8 : 16;
 }
 
 // SEG false: one K segment and one phase (the launch guarantees it).
