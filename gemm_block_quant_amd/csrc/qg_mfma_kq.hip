@@ -310,10 +310,23 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a_in, 
 
     KqArgs a = a_in;
     int m0 = blockIdx.y * BM, M = a.M;
+    int nt = blockIdx.x;  // column tile
     const int32_t* prow = nullptr;  // grouped: original index of the tile's row i at prow[i]
     if constexpr (G) {
-        const int t = blockIdx.y;
-        if (t >= g.ws[g.count]) return;  // uniform: past the listed tiles
+        // Workgroups are dealt to the 8 XCDs in turn (workgroup i on XCD
+        // i % 8); each XCD takes a contiguous band of the listed (row tile,
+        // column tile) items, row tile major, so the tiles of one expert -- its
+        // weights and its activation rows -- stay in one XCD's L2 instead of
+        // being fetched by all of them.  Only the placement changes.
+        constexpr int kXcds = 8;
+        const int nx = gridDim.x;
+        const int items = g.ws[g.count] * nx;
+        const int per_xcd = (items + kXcds - 1) / kXcds;
+        const int lin = blockIdx.y * nx + blockIdx.x;
+        const int it = (lin % kXcds) * per_xcd + lin / kXcds;
+        if (it >= items || lin / kXcds >= per_xcd) return;  // uniform: past the listed tiles
+        const int t = it / nx;
+        nt = it - t * nx;
         const int p = g.ws[g.list + 2 * t], q = g.ws[g.list + 2 * t + 1];
         const int e = g.ws[4 + q];
         const int r1 = g.ws[4 + g.S + q + 1];
@@ -325,7 +338,7 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a_in, 
         M = min(BM, r1 - p);
     }
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int n0 = blockIdx.x * BN;
+    const int n0 = nt * BN;
     const int wm = (wid >> 1) * (BM / 2), wn = (wid & 1) * (BN / 2);
     const int N = a.N;
     const int nsteps = a.K / kMfmaKStep;  // K is a multiple of 64
@@ -565,12 +578,16 @@ static hipError_t launch_kq(const KqArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Grouped: one row of workgroups per possible list entry (g.cap); those past
-// the listed count exit at once.
+// Grouped: one row of workgroups per possible list entry (g.cap), rounded up
+// so that the grid holds a whole number of rounds over the 8 XCDs (every
+// item of the kernel's XCD bands then has a workgroup); those past the listed
+// items exit at once.
 template <int F>
 static hipError_t launch_kq_grouped(const KqArgs& a, const KqGroup& g, int bm, hipStream_t st) {
     if (g.cap <= 0) return hipSuccess;
-    dim3 grid((a.N + 63) / 64, g.cap);
+    const long nx = (a.N + 63) / 64;
+    const long total = (nx * g.cap + 7) / 8 * 8;
+    dim3 grid((unsigned)nx, (unsigned)((total + nx - 1) / nx));
     if (bm == 128)
         hipLaunchKernelGGL((k_mfma_kq<F, 128, 64, 2, true>), grid, dim3(kMfmaThreads), 0, st, a, g);
     else
