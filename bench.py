@@ -117,6 +117,7 @@ class Prepared:
         import gemm_block_quant_amd as qg
         import synth
         self.wl = wl
+        self.entry = None  # the entry point timed, where it is not the workload's usual one
         self.call_bytes = None  # bytes of call i (cycled), when calls differ
         if wl.block is not None:
             self._prepare_block(wl)
@@ -161,8 +162,19 @@ class Prepared:
             fn = L.quant_gemv
             self.calls = [lambda s, wp=wp: fn(wp, fmt, N, K, xp, yp, s) for wp in wps]
         else:
-            fn = L.quant_gemm
-            self.calls = [lambda s, wp=wp: fn(wp, fmt, N, K, M, xp, yp, s) for wp in wps]
+            # the 5120-row down projections at 512 rows leave resident workgroups
+            # idle on the plain tile grid: the stream-K entry deals their work
+            # evenly (quant_gemm_streamk is quant_gemm where it needs no workspace)
+            wsb = qg.quant_gemm_streamk_workspace_bytes(fmt, N, K, M)
+            if wsb > 0:
+                self.entry = "quant_gemm_streamk"
+                self.ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+                wsp = ctypes.c_void_p(self.ws.data_ptr())
+                fn = L.quant_gemm_streamk
+                self.calls = [lambda s, wp=wp: fn(wp, fmt, N, K, M, xp, yp, wsp, wsb, s) for wp in wps]
+            else:
+                fn = L.quant_gemm
+                self.calls = [lambda s, wp=wp: fn(wp, fmt, N, K, M, xp, yp, s) for wp in wps]
 
     def _prepare_block(self, wl: Workload):
         """The MoE block: gate|up weight[E*2F, D], down weight[E*D, F].  Only the
@@ -597,6 +609,8 @@ def result_for(p: Prepared, steps: int, warmup: int, key: str = None, probe: Rea
          "weight_GBps": round(gbs, 1), "kernel_weight_GBps": round(kern_gbs, 1),
          "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
          "implied_tok_s": round(wl.M * gbs / TOKEN_BYTES_GB, 1)}
+    if p.entry:
+        r["entry"] = p.entry
     if wl.moe or wl.block:
         r["distinct_experts"] = p.distinct
     if wl.layer:

@@ -7,11 +7,13 @@ in include/quantgemm.h:
 
     quant_gemv(w, fmt, N, K, x, y=None)                     -> y [N] fp32
     quant_gemm(w, fmt, N, K, M, x, y=None)                  -> y [M, N] fp32
+    quant_gemm_streamk(w, fmt, N, K, M, x, y=None, workspace=None) -> y [M, N] fp32
     quant_grouped_gemm(w, fmt, E, N, K, M, x, ids, y=None, workspace=None) -> y [M, N]
     quant_grouped_gemm_noalloc(w, fmt, E, N, K, M, x, ids, y=None)  -> y [M, N]
     quant_dequantize(w, fmt, rows, K, out=None)             -> out [rows, K] fp32
     quant_dequantize_stacked(w, fmt, E, N, K, out=None)     -> out [E*N, K] fp32
     quant_packed_bytes(fmt, E, N, K), quant_grouped_workspace_bytes(E, M),
+    quant_gemm_streamk_workspace_bytes(fmt, N, K, M),
     quant_block_values(fmt), quant_status_string(status)
 
 w is a uint8 tensor holding the packed bytes; x holds bf16 activations
@@ -58,6 +60,10 @@ def lib():
     L.quant_gemm.restype = i32
     L.quant_grouped_workspace_bytes.argtypes = [i64, i64]
     L.quant_grouped_workspace_bytes.restype = sz
+    L.quant_gemm_streamk_workspace_bytes.argtypes = [i32, i64, i64, i64]
+    L.quant_gemm_streamk_workspace_bytes.restype = sz
+    L.quant_gemm_streamk.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, sz, vp]
+    L.quant_gemm_streamk.restype = i32
     L.quant_grouped_gemm.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     L.quant_grouped_gemm.restype = i32
     L.quant_grouped_gemm_noalloc.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, vp]
@@ -153,6 +159,26 @@ def quant_gemm(w, fmt: int, N: int, K: int, M: int, x, y=None, stream=None):
     st = lib().quant_gemm(_dev_ptr(w, "w", quant_packed_bytes(fmt, 1, N, K)), fmt, N, K, M, _x_ptr(x, M, K),
                           _dev_ptr(y, "y", 4 * M * N), _stream(stream))
     _check(st, "quant_gemm")
+    return y
+
+
+def quant_gemm_streamk_workspace_bytes(fmt: int, N: int, K: int, M: int) -> int:
+    return int(lib().quant_gemm_streamk_workspace_bytes(fmt, N, K, M))
+
+
+def quant_gemm_streamk(w, fmt: int, N: int, K: int, M: int, x, y=None, workspace=None, stream=None):
+    """quant_gemm with the matrix-core tiles dealt evenly over the GPU (stream-K);
+    workspace: uint8 device tensor of quant_gemm_streamk_workspace_bytes bytes
+    (allocated here when None)."""
+    torch = _torch()
+    y = _out(y, (M, N), x.device)
+    wsb = quant_gemm_streamk_workspace_bytes(fmt, N, K, M)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=x.device)
+    st = lib().quant_gemm_streamk(_dev_ptr(w, "w", quant_packed_bytes(fmt, 1, N, K)), fmt, N, K, M, _x_ptr(x, M, K),
+                                  _dev_ptr(y, "y", 4 * M * N), _dev_ptr(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "quant_gemm_streamk")
     return y
 
 

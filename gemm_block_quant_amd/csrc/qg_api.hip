@@ -353,6 +353,31 @@ qg_status quant_gemv(const void* w, qg_format fmt, int64_t N, int64_t K, const u
     return quant_gemm(w, fmt, N, K, 1, x, y, stream);
 }
 
+// Stream-K variant of quant_gemm: the workspace it needs (0 where the plain
+// schedule is as balanced or the call does not take the matrix-core tiles).
+static size_t streamk_bytes(qg_format fmt, int64_t N, int64_t K, int64_t M) {
+    if (check_shape(fmt, 1, N, K, M) != QG_OK || M < kMfmaMinRows || M > ((int64_t)1 << 21) || N == 0) return 0;
+    return mfma_streamk_bytes(fmt, (int)N, (int)K, (int)M);
+}
+
+size_t quant_gemm_streamk_workspace_bytes(qg_format fmt, int64_t N, int64_t K, int64_t M) {
+    return streamk_bytes(fmt, N, K, M);
+}
+
+qg_status quant_gemm_streamk(const void* w, qg_format fmt, int64_t N, int64_t K, int64_t M, const uint16_t* x,
+                             float* y, void* workspace, size_t workspace_bytes, void* stream) {
+    const size_t need = streamk_bytes(fmt, N, K, M);
+    if (need == 0) return quant_gemm(w, fmt, N, K, M, x, y, stream);
+    if (!w || !x || !y) return QG_EINVAL;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
+    if (!workspace || workspace_bytes < need) return QG_EWORKSPACE;
+    if (!aligned(workspace, 16)) return QG_EALIGN;
+    const StreamArgs a = stream_args(w, fmt, 1, 0, N, K);
+    const hipError_t e = launch_mfma_kquant_streamk(fmt, a.w0, a.w1, a.gbytes, (int)N, (int)K, x, K, (int)M, y, N,
+                                                    workspace, workspace_bytes, (hipStream_t)stream);
+    return e == hipSuccess ? QG_OK : QG_EHIP;
+}
+
 size_t quant_grouped_workspace_bytes(int64_t E, int64_t M) {
     if (E < 1 || M < 0) return 0;
     return grouped_workspace_bytes(E, M);

@@ -54,6 +54,14 @@ bool mfma_kquant_supported(int fmt, int K);
 // tensor scale (unused otherwise).
 hipError_t launch_mfma_kquant(int fmt, const uint8_t* w, const uint8_t* w1, const uint8_t* gbytes, int N, int K,
                               const uint16_t* x, int64_t ldx, int M, float* y, int64_t ldy, hipStream_t st);
+// The same product with the (tile, K step) iterations dealt evenly over one
+// workgroup per resident slot (stream-K), where the tile count is not a whole
+// number of rounds; ws holds per-tile counters and partial tiles
+// (mfma_streamk_bytes; 0: the plain launch is taken and ws is not used).
+size_t mfma_streamk_bytes(int fmt, int N, int K, int M);
+hipError_t launch_mfma_kquant_streamk(int fmt, const uint8_t* w, const uint8_t* w1, const uint8_t* gbytes, int N,
+                                      int K, const uint16_t* x, int64_t ldx, int M, float* y, int64_t ldy, void* ws,
+                                      size_t ws_bytes, hipStream_t st);
 // The same tiles over the row tiles of a grouped product's bucketing
 // workspace: tile t of the list at ws[list ..] (count at ws[count], at most
 // cap entries) is rows [p, p + bm) of the sorted rows of slot q, (p, q) =

@@ -283,12 +283,27 @@ template <> struct KqFmt<QG_NVFP4> {
     }
 };
 
+// Stream-K: the (tile, K step) iterations of the whole product, tiles row
+// tile major (t = row tile * ntiles + column tile), are dealt to the grid in
+// equal contiguous ranges, so every workgroup gets the same number of products
+// whatever the tile count.  A tile whose steps fall to several workgroups is
+// finished by the last of them to arrive: each writes its partial sums to its
+// slot (two per workgroup: the first and the last tile of its range), counts
+// itself in at the tile's counter, and the last one adds the parts in
+// workgroup order and stores the tile.  Nothing waits on another workgroup.
+struct KqSplit {
+    int32_t* counters;  // per tile, zero on entry
+    float* partials;    // 2 slots of BM * BN floats per workgroup
+    int tiles, ntiles;  // all tiles; column tiles
+};
+
 // D: K steps of loads in flight in the register ring (an even number).
 // BN: 64, or 128 for the formats without per-sub-block terms.
 // G: grouped product, row tile blockIdx.y of g's list (rows through the
 // bucketing permutation, the weights of the tile's expert).
-template <int F, int BM, int BN, int D, bool G>
-__global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a_in, const KqGroup g) {
+// SK: stream-K over sp (dense products only).
+template <int F, int BM, int BN, int D, bool G, bool SK = false>
+__global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a_in, const KqGroup g, const KqSplit sp) {
     using Fmt = KqFmt<F>;
     constexpr int TPR = kMfmaThreads / BN;  // threads per weight row (4 or 2)
     constexpr int QPT = 4 / TPR;            // quarters of a row's step decoded per thread
@@ -338,7 +353,7 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a_in, 
         M = min(BM, r1 - p);
     }
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int n0 = nt * BN;
+    int n0 = nt * BN;
     const int wm = (wid >> 1) * (BM / 2), wn = (wid & 1) * (BN / 2);
     const int N = a.N;
     const int nsteps = a.K / kMfmaKStep;  // K is a multiple of 64
@@ -352,16 +367,20 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a_in, 
     // read row M - 1 or row 0 instead: such rows feed only outputs that are
     // never written, so no select is needed.
     const uint16_t* xp[XCH];
+    const uint8_t* wrow;
+    const uint8_t* wrow1;
+    auto setup = [&]() {
 #pragma unroll
-    for (int c = 0; c < XCH; ++c) {
-        const int i = tid + c * kMfmaThreads;
-        const int r = min(m0 + (i >> 3), M - 1);
-        const int64_t xrow = G ? prow[r] / g.xdiv : r;
-        xp[c] = a.x + (size_t)xrow * a.ldx + Fmt::x_chunk(i & 7);
-    }
-    const size_t wrow_n = (size_t)(n0 + wrow_i < N ? n0 + wrow_i : 0);
-    const uint8_t* wrow = a.w + wrow_n * a.rb;
-    const uint8_t* wrow1 = a.w1 ? a.w1 + wrow_n * a.rb1 : nullptr;
+        for (int c = 0; c < XCH; ++c) {
+            const int i = tid + c * kMfmaThreads;
+            const int r = min(m0 + (i >> 3), M - 1);
+            const int64_t xrow = G ? prow[r] / g.xdiv : r;
+            xp[c] = a.x + (size_t)xrow * a.ldx + Fmt::x_chunk(i & 7);
+        }
+        const size_t wrow_n = (size_t)(n0 + wrow_i < N ? n0 + wrow_i : 0);
+        wrow = a.w + wrow_n * a.rb;
+        wrow1 = a.w1 ? a.w1 + wrow_n * a.rb1 : nullptr;
+    };
 
     // Loads without branches: a load under a branch makes the compiler wait
     // for every outstanding load.
@@ -407,10 +426,6 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a_in, 
     // lane, two waves per SIMD: the compiler then keeps matrix-core results in
     // ordinary VGPRs, which the vector unit can read without copies.)
     f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
     const int frow = lane & 31, fcol = (lane >> 5) * 16, half = lane >> 5;
     auto mma = [&](int buf) {
@@ -503,55 +518,157 @@ __global__ __launch_bounds__(kMfmaThreads, 2) void k_mfma_kq(const KqArgs a_in, 
         }
     };
 
-    // prologue: steps 0 .. D-1 in flight, step 0 in LDS, step D into the freed stage
-    static_for<D>([&](auto j) { load(min((int)decltype(j)::value, nsteps - 1), j); });
-    store(0, 0, std::integral_constant<int, 0>{});
-    load(min(D, nsteps - 1), std::integral_constant<int, 0>{});
-    __syncthreads();
-    // main loop over whole groups of D steps: no branches, so the compiler
-    // waits only for the loads each store needs
-    int s0 = 0;
-    for (; s0 + D < nsteps; s0 += D) {
+    // Steps [sb, se) of the current tile into acc.  The LDS buffers alternate
+    // from buffer 0 at step sb; the last step ends with a barrier, so the next
+    // range may restage at once.
+    auto run = [&](int sb, int se) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+        // prologue: steps sb .. sb+D-1 in flight, step sb in LDS, step sb+D into the freed stage
+        static_for<D>([&](auto j) { load(min(sb + (int)decltype(j)::value, se - 1), j); });
+        store(0, sb, std::integral_constant<int, 0>{});
+        load(min(sb + D, se - 1), std::integral_constant<int, 0>{});
+        __syncthreads();
+        // main loop over whole groups of D steps: no branches, so the compiler
+        // waits only for the loads each store needs
+        int s0 = sb;
+        for (; s0 + D < se; s0 += D) {
+            static_for<D>([&](auto jt) {
+                constexpr int j = decltype(jt)::value;
+                constexpr int nj = (j + 1) % D;
+                const int s = s0 + j;
+                // (no scheduling fences between the three: the compiler interleaves
+                // the next step's decode and loads with this step's products, 2-6 %
+                // faster than keeping them apart)
+                mma(j & 1);  // s0 - sb is a multiple of D (even), so (s - sb) & 1 == j & 1
+                store((j + 1) & 1, s + 1, std::integral_constant<int, nj>{});
+                load(min(s + 1 + D, se - 1), std::integral_constant<int, nj>{});  // (past the end: a harmless reload)
+                __syncthreads();
+            });
+        }
+        // the last (up to D) steps
         static_for<D>([&](auto jt) {
             constexpr int j = decltype(jt)::value;
             constexpr int nj = (j + 1) % D;
             const int s = s0 + j;
-            // (no scheduling fences between the three: the compiler interleaves
-            // the next step's decode and loads with this step's products, 2-6 %
-            // faster than keeping them apart)
-            mma(j & 1);  // s0 is a multiple of D (even), so s & 1 == j & 1
-            store((j + 1) & 1, s + 1, std::integral_constant<int, nj>{});
-            load(min(s + 1 + D, nsteps - 1), std::integral_constant<int, nj>{});  // (past the end: a harmless reload)
-            __syncthreads();
-        });
-    }
-    // the last (up to D) steps
-    static_for<D>([&](auto jt) {
-        constexpr int j = decltype(jt)::value;
-        constexpr int nj = (j + 1) % D;
-        const int s = s0 + j;
-        if (s < nsteps) {
-            mma(j & 1);
-            if (s + 1 < nsteps) store((j + 1) & 1, s + 1, std::integral_constant<int, nj>{});
-            __syncthreads();
-        }
-    });
-
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int n = n0 + wn + 32 * j + (lane & 31);
-        float rs = 1.f;
-        if constexpr (Fmt::ROWSCALE) rs = Fmt::out_scale(a, n < N ? n : 0);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m < M && n < N) {
-                    const int64_t yrow = G ? prow[m] : m;
-                    st_global_f32(a.y + (size_t)yrow * a.ldy + n, Fmt::ROWSCALE ? acc[i][j][r] * rs : acc[i][j][r]);
-                }
+            if (s < se) {
+                mma(j & 1);
+                if (s + 1 < se) store((j + 1) & 1, s + 1, std::integral_constant<int, nj>{});
+                __syncthreads();
             }
+        });
+    };
+
+    auto store_y = [&](const f32x16 (&v)[FM][FN]) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn + 32 * j + (lane & 31);
+            float rs = 1.f;
+            if constexpr (Fmt::ROWSCALE) rs = Fmt::out_scale(a, n < N ? n : 0);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (m < M && n < N) {
+                        const int64_t yrow = G ? prow[m] : m;
+                        st_global_f32(a.y + (size_t)yrow * a.ldy + n,
+                                      Fmt::ROWSCALE ? v[i][j][r] * rs : v[i][j][r]);
+                    }
+                }
+        }
+    };
+
+    if constexpr (!SK) {
+        setup();
+        run(0, nsteps);
+        store_y(acc);
+    } else {
+        __shared__ int last_part;
+        const int64_t iters = (int64_t)sp.tiles * nsteps;
+        const int grid = (int)gridDim.x;
+        auto begin = [&](int b) { return (int64_t)b * iters / grid; };
+        // logical workgroup: workgroups are dealt to the 8 XCDs in turn, and
+        // each XCD takes a contiguous band of logical ranges, so that the row
+        // tiles of one weight column and the parts of one split tile mostly
+        // share an L2 (placement only: nothing below depends on it)
+        constexpr int kXcds = 8;
+        const int per_xcd = grid / kXcds;  // the grid is a multiple of 8
+        const int me = ((int)blockIdx.x % kXcds) * per_xcd + (int)blockIdx.x / kXcds;
+        const int64_t it0 = begin(me), it1 = begin(me + 1);
+        for (int64_t it = it0; it < it1;) {
+            const int t = (int)(it / nsteps);
+            const int64_t tb = (int64_t)t * nsteps;
+            const int sb = (int)(it - tb), se = (int)min<int64_t>(nsteps, it1 - tb);
+            const int mt = t / sp.ntiles;  // row tile major, as the plain launch
+            nt = t - mt * sp.ntiles;
+            m0 = mt * BM;
+            n0 = nt * BN;
+            setup();
+            run(sb, se);
+            it = tb + se;
+            if (sb == 0 && se == nsteps) {
+                store_y(acc);
+                continue;
+            }
+            // workgroups b_lo .. b_hi hold the parts of tile t (first and last
+            // whose ranges meet [tb, tb + nsteps))
+            int b_lo = (int)(tb * grid / iters), b_hi = (int)((tb + nsteps) * grid / iters);
+            while (b_lo + 1 < grid && begin(b_lo + 1) <= tb) ++b_lo;
+            while (b_lo > 0 && begin(b_lo) > tb) --b_lo;
+            while (b_hi > 0 && begin(b_hi) >= tb + nsteps) --b_hi;
+            while (b_hi + 1 < grid && begin(b_hi + 1) < tb + nsteps) ++b_hi;
+            auto slot = [&](int b) {
+                const int sl = (int)(begin(b) / nsteps) == t ? 0 : 1;  // 0: the first tile of b's range
+                return sp.partials + ((size_t)b * 2 + sl) * (BM * BN) + ((size_t)wid * FM * FN * 16) * 64 + lane;
+            };
+            // The partials go through agent-scope atomic stores and loads, which
+            // write through and read at the device's coherence point one access
+            // at a time; every store has completed (s_waitcnt 0) before this part
+            // counts in, and the last part reads them only after its count.  No
+            // cache-wide fence: a release writes back, and an acquire invalidates,
+            // the XCD's whole L2, which holds the activations every tile rereads
+            // (each cost more than the balance gained).
+            float* mine = slot(me);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        __hip_atomic_store(mine + (size_t)(((i * FN + j) * 16 + r) * 64), acc[i][j][r],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
+            __syncthreads();
+            int parts = 0;  // workgroups with a non-empty range among b_lo .. b_hi
+            for (int b = b_lo; b <= b_hi; ++b) parts += begin(b + 1) > begin(b);
+            if (tid == 0) {
+                const int before = __hip_atomic_fetch_add(sp.counters + t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last_part = before == parts - 1;
+            }
+            __syncthreads();
+            if (!last_part) continue;
+            // every part from its slot (this workgroup's too), in workgroup order
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+            for (int b = b_lo; b <= b_hi; ++b) {
+                if (begin(b + 1) == begin(b)) continue;  // (no part)
+                const float* p = slot(b);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            acc[i][j][r] += __hip_atomic_load(p + (size_t)(((i * FN + j) * 16 + r) * 64),
+                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            store_y(acc);
+        }
     }
 }
 
@@ -564,17 +681,80 @@ static hipError_t launch_kq(const KqArgs& a, hipStream_t st) {
     const long cus = num_cus();
     auto tiles = [&](int bm, int bn) { return (long)((a.N + bn - 1) / bn) * ((a.M + bm - 1) / bm); };
     const KqGroup none{};
+    const KqSplit plain{};
+    // (column tile fastest: the row tiles of one weight column land on one
+    // XCD whenever the column tile count is a multiple of 8 -- measured 3-7 %
+    // faster than bands of row tiles per XCD)
     if (KqFmt<F>::ROWSCALE && tiles(128, 128) >= 2 * cus) {
         dim3 grid((a.N + 127) / 128, (a.M + 127) / 128);
         hipLaunchKernelGGL((k_mfma_kq<F, 128, KqFmt<F>::ROWSCALE ? 128 : 64, 2, false>), grid, dim3(kMfmaThreads), 0,
-                           st, a, none);
+                           st, a, none, plain);
     } else if (tiles(128, 64) >= cus) {
         dim3 grid((a.N + 63) / 64, (a.M + 127) / 128);
-        hipLaunchKernelGGL((k_mfma_kq<F, 128, 64, 2, false>), grid, dim3(kMfmaThreads), 0, st, a, none);
+        hipLaunchKernelGGL((k_mfma_kq<F, 128, 64, 2, false>), grid, dim3(kMfmaThreads), 0, st, a, none, plain);
     } else {
         dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
-        hipLaunchKernelGGL((k_mfma_kq<F, 64, 64, 4, false>), grid, dim3(kMfmaThreads), 0, st, a, none);
+        hipLaunchKernelGGL((k_mfma_kq<F, 64, 64, 4, false>), grid, dim3(kMfmaThreads), 0, st, a, none, plain);
     }
+    return hipGetLastError();
+}
+
+// Stream-K plan of a dense product: the tile shape the plain launch would
+// take at two workgroups per CU, one workgroup per resident slot.  Taken when
+// the tiles would leave slots idle but number at least half of them (a tile
+// is then shared by at most three workgroups): the 5120-row down projections
+// at 512 rows, 320 tiles for 512 slots, measured 11 % (NVFP4) and 22 % (Q6_K)
+// faster.  With more tiles than slots the plain launch measured faster
+// (1.06-2.1 rounds: the partial sums' traffic and the split tiles' second
+// pipeline fill cost more than the balance gains).
+struct SkPlan {
+    int bm, bn, tiles, ntiles, grid;
+    size_t counter_bytes, bytes;
+};
+
+template <int F>
+static bool sk_plan(int N, int M, SkPlan* p) {
+    const long slots = 2L * num_cus() / 8 * 8;  // a multiple of the 8 XCDs
+    if (slots < 8) return false;
+    auto tiles = [&](int bm, int bn) { return (long)((N + bn - 1) / bn) * ((M + bm - 1) / bm); };
+    const int bn = KqFmt<F>::ROWSCALE && tiles(128, 128) >= slots / 2 ? 128 : 64;
+    const long t = tiles(128, bn);
+    if (t < slots / 2 || t >= slots) return false;
+    p->bm = 128;
+    p->bn = bn;
+    p->tiles = (int)t;
+    p->ntiles = (N + bn - 1) / bn;
+    p->grid = (int)slots;
+    p->counter_bytes = ((size_t)t * 4 + 255) / 256 * 256;
+    p->bytes = p->counter_bytes + (size_t)p->grid * 2 * 128 * bn * sizeof(float);
+    return true;
+}
+
+__global__ void k_zero_i32(int32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+template <int F>
+static hipError_t launch_kq_sk(const KqArgs& a, const SkPlan& pl, void* ws, hipStream_t st) {
+    KqSplit sp;
+    sp.counters = (int32_t*)ws;
+    sp.partials = (float*)((uint8_t*)ws + pl.counter_bytes);
+    sp.tiles = pl.tiles;
+    sp.ntiles = pl.ntiles;
+    // the counters start at zero in every call (a fill kernel, not a memset:
+    // the call may be captured into a graph)
+    hipLaunchKernelGGL(k_zero_i32, dim3((pl.tiles + 255) / 256), dim3(256), 0, st, sp.counters, pl.tiles);
+    const KqGroup none{};
+    if constexpr (KqFmt<F>::ROWSCALE) {
+        if (pl.bn == 128) {
+            hipLaunchKernelGGL((k_mfma_kq<F, 128, 128, 2, false, true>), dim3(pl.grid), dim3(kMfmaThreads), 0, st, a,
+                               none, sp);
+            return hipGetLastError();
+        }
+    }
+        hipLaunchKernelGGL((k_mfma_kq<F, 128, 64, 2, false, true>), dim3(pl.grid), dim3(kMfmaThreads), 0, st, a, none,
+                           sp);
     return hipGetLastError();
 }
 
@@ -589,9 +769,9 @@ static hipError_t launch_kq_grouped(const KqArgs& a, const KqGroup& g, int bm, h
     const long total = (nx * g.cap + 7) / 8 * 8;
     dim3 grid((unsigned)nx, (unsigned)((total + nx - 1) / nx));
     if (bm == 128)
-        hipLaunchKernelGGL((k_mfma_kq<F, 128, 64, 2, true>), grid, dim3(kMfmaThreads), 0, st, a, g);
+        hipLaunchKernelGGL((k_mfma_kq<F, 128, 64, 2, true>), grid, dim3(kMfmaThreads), 0, st, a, g, KqSplit{});
     else
-        hipLaunchKernelGGL((k_mfma_kq<F, 64, 64, 4, true>), grid, dim3(kMfmaThreads), 0, st, a, g);
+        hipLaunchKernelGGL((k_mfma_kq<F, 64, 64, 4, true>), grid, dim3(kMfmaThreads), 0, st, a, g, KqSplit{});
     return hipGetLastError();
 }
 
@@ -631,6 +811,43 @@ hipError_t launch_mfma_kquant(int fmt, const uint8_t* w, const uint8_t* w1, cons
         case QG_Q8_0: return launch_kq<QG_Q8_0>(a, st);
         case QG_FP8: return launch_kq<QG_FP8>(a, st);
         default: return launch_kq<QG_NVFP4>(a, st);
+    }
+}
+
+static bool sk_plan_fmt(int fmt, int N, int M, SkPlan* p) {
+    switch (fmt) {
+        case QG_Q4_K: return sk_plan<QG_Q4_K>(N, M, p);
+        case QG_Q5_K: return sk_plan<QG_Q5_K>(N, M, p);
+        case QG_Q6_K: return sk_plan<QG_Q6_K>(N, M, p);
+        case QG_Q8_0: return sk_plan<QG_Q8_0>(N, M, p);
+        case QG_FP8: return sk_plan<QG_FP8>(N, M, p);
+        case QG_NVFP4: return sk_plan<QG_NVFP4>(N, M, p);
+        default: return false;
+    }
+}
+
+size_t mfma_streamk_bytes(int fmt, int N, int K, int M) {
+    SkPlan pl;
+    if (M < kMfmaMinRows || !mfma_kquant_supported(fmt, K) || !sk_plan_fmt(fmt, N, M, &pl)) return 0;
+    return pl.bytes;
+}
+
+hipError_t launch_mfma_kquant_streamk(int fmt, const uint8_t* w, const uint8_t* w1, const uint8_t* gbytes, int N,
+                                      int K, const uint16_t* x, int64_t ldx, int M, float* y, int64_t ldy, void* ws,
+                                      size_t ws_bytes, hipStream_t st) {
+    SkPlan pl;
+    if (!sk_plan_fmt(fmt, N, M, &pl))
+        return launch_mfma_kquant(fmt, w, w1, gbytes, N, K, x, ldx, M, y, ldy, st);
+    if (!ws || ws_bytes < pl.bytes) return hipErrorInvalidValue;
+    KqArgs a = {x, ldx, w, w1, gbytes, 0, 0, y, ldy, M, N, K};
+    if (!kq_row_bytes(fmt, K, a)) return hipErrorInvalidValue;
+    switch (fmt) {
+        case QG_Q4_K: return launch_kq_sk<QG_Q4_K>(a, pl, ws, st);
+        case QG_Q5_K: return launch_kq_sk<QG_Q5_K>(a, pl, ws, st);
+        case QG_Q6_K: return launch_kq_sk<QG_Q6_K>(a, pl, ws, st);
+        case QG_Q8_0: return launch_kq_sk<QG_Q8_0>(a, pl, ws, st);
+        case QG_FP8: return launch_kq_sk<QG_FP8>(a, pl, ws, st);
+        default: return launch_kq_sk<QG_NVFP4>(a, pl, ws, st);
     }
 }
 

@@ -190,3 +190,27 @@ def test_missing_library_raises_instead_of_falling_back():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, cwd=root)
     assert r.returncode == 0, r.stderr
     assert r.stdout.startswith("raised:") and "not built" in r.stdout
+
+
+def test_streamk_validation():
+    """quant_gemm_streamk: workspace sizing and the checks made before any launch."""
+    sk = _raw("quant_gemm_streamk")
+    fmt, N, K, M = qg.NVFP4, 5120, 17408, 512  # 320 tiles of 128 x 64 for 2 workgroups per CU
+    wsb = qg.quant_gemm_streamk_workspace_bytes(fmt, N, K, M)
+    # per-tile counters and two 128 x 64 fp32 partial tiles per workgroup
+    assert wsb > 2 * 128 * 64 * 4, wsb
+    assert qg.quant_gemm_streamk_workspace_bytes(fmt, N, K, 16) == 0  # not on the tiles
+    assert qg.quant_gemm_streamk_workspace_bytes(fmt, 17408, 5120, 4096) == 0  # more tiles than slots
+    assert qg.quant_gemm_streamk_workspace_bytes(qg.Q4_K, 200, 256, 300) == 0  # few tiles: plain schedule
+    assert qg.quant_gemm_streamk_workspace_bytes(9, N, K, M) == 0
+    assert qg.quant_gemm_streamk_workspace_bytes(fmt, N, 100, M) == 0
+    ws = ctypes.c_void_p(0x400000)
+    args = lambda **kw: [kw.get("w", FAKE_W), kw.get("fmt", fmt), N, K, kw.get("M", M), FAKE_X, FAKE_Y,
+                         kw.get("ws", ws), kw.get("wsb", wsb), None]
+    assert sk(*args(ws=None)) == qg.QG_EWORKSPACE
+    assert sk(*args(wsb=wsb - 1)) == qg.QG_EWORKSPACE
+    assert sk(*args(ws=ctypes.c_void_p(0x400008))) == qg.QG_EALIGN
+    assert sk(*args(w=None)) == qg.QG_EINVAL
+    assert sk(*args(w=ctypes.c_void_p(0x100008))) == qg.QG_EALIGN
+    assert sk(*args(fmt=9)) == qg.QG_EFORMAT
+    assert sk(*args(M=0, ws=None, wsb=0)) == qg.QG_OK
