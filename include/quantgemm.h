@@ -282,7 +282,8 @@ const char* quant_status_string(qg_status s);
 
 /* Measurement reference, not part of the product path: a plain streaming read
  * of `bytes` bytes at `buf` (each 16-byte granule once, non-temporal loads,
- * one workgroup per CU streaming a contiguous chunk),
+ * eight 256-thread workgroups per CU striding over the buffer with eight
+ * loads in flight per thread: the fastest read shape measured),
  * the achievable-bandwidth ceiling the streaming kernels are compared with
  * ("Qwen3.8-27B on one Tenstorrent P150", section "4. Measuring the ceiling,
  * and lots of dead ends": a validated read microbenchmark as the ceiling).
