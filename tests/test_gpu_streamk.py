@@ -27,6 +27,9 @@ SPLIT_CASES = [
     (qg.Q8_0, 4160, 1024, 512),
     # ragged rows (300) and columns (N % 64 != 0), 12 K steps: 330 and 258 tiles
     (qg.Q4_K, 7000, 768, 300), (qg.NVFP4, 11000, 768, 300),
+    # one K step per tile (fewer iterations than workgroups: empty ranges, no
+    # tile split) and two (splits of two parts only)
+    (qg.FP8, 8320, 64, 512), (qg.Q8_0, 4160, 64, 512), (qg.NVFP4, 8320, 128, 512),
 ]
 
 
