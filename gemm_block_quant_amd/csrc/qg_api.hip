@@ -355,10 +355,14 @@ qg_status quant_gemv(const void* w, qg_format fmt, int64_t N, int64_t K, const u
     return quant_gemm(w, fmt, N, K, 1, x, y, stream);
 }
 
-// Stream-K variant of quant_gemm: the workspace it needs (0 where the plain
-// schedule is as balanced or the call does not take the matrix-core tiles).
+// Workspace variant of quant_gemm: the workspace it needs (0 where quant_gemm's
+// schedule is kept).  Up to 16 rows: the direct path with one K segment per
+// workgroup where the plain launch would stage the activations in several K
+// phases; from 32 rows: stream-K tiles where the plain grid is under-filled.
 static size_t streamk_bytes(qg_format fmt, int64_t N, int64_t K, int64_t M) {
-    if (check_shape(fmt, 1, N, K, M) != QG_OK || M < kMfmaMinRows || M > ((int64_t)1 << 21) || N == 0) return 0;
+    if (check_shape(fmt, 1, N, K, M) != QG_OK || N == 0 || M < 2 || M > ((int64_t)1 << 21)) return 0;
+    if (M <= kMaxPassRows) return direct_xseg_bytes(fmt, N, (int)K, (int)M);
+    if (M < kMfmaMinRows) return 0;
     return mfma_streamk_bytes(fmt, (int)N, (int)K, (int)M);
 }
 
@@ -374,6 +378,16 @@ qg_status quant_gemm_streamk(const void* w, qg_format fmt, int64_t N, int64_t K,
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
     if (!workspace || workspace_bytes < need) return QG_EWORKSPACE;
     if (!aligned(workspace, 16)) return QG_EALIGN;
+    if (M <= kMaxPassRows) {
+        StreamArgs a = stream_args(w, fmt, 1, 0, N, K);
+        a.x = x;
+        a.ldx = K;
+        a.y = y;
+        a.ldy = N;
+        a.M = (int)M;
+        for (int i = 0; i < kMaxPassRows; ++i) a.xrow[i] = a.yrow[i] = i < M ? i : 0;
+        return launch_direct_xseg(fmt, a, workspace, (hipStream_t)stream) == hipSuccess ? QG_OK : QG_EHIP;
+    }
     const StreamArgs a = stream_args(w, fmt, 1, 0, N, K);
     const hipError_t e = launch_mfma_kquant_streamk(fmt, a.w0, a.w1, a.gbytes, (int)N, (int)K, x, K, (int)M, y, N,
                                                     workspace, workspace_bytes, (hipStream_t)stream);

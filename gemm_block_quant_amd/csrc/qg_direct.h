@@ -805,6 +805,10 @@ struct SegLds {
     lds_f32* total;
     QG_LDS int* progress;
     int mtmax;
+    // segments on different workgroups: sums [row group][segment][4][MT] and
+    // per-row-group counters in global memory
+    float* gpart;
+    int32_t* gcnt;
 };
 
 // The K range whose activations are staged in LDS: segments [s_lo, s_lo + ns)
@@ -826,7 +830,7 @@ struct Phase {
 // barrier inside, so every wave of the workgroup must call this function).
 // SEG false: the caller has one segment per row and one phase over all of K
 // (sg and ph are then ignored).
-template <int F, int MT, int SP, int PF, bool SEG, class Next, class Between>
+template <int F, int MT, int SP, int PF, bool SEG, bool XS = false, class Next, class Between>
 __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int K, const lds_u8* xl,
                                                    const lds_f32* xs, Next next_item, int rg_base, Segments sg,
                                                    Phase ph, SegLds sl, float* y, int64_t ldy, int64_t yrow,
@@ -952,7 +956,33 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
             float mine = slot_sum_rows<MT>(acc, slot);
 #pragma unroll
             for (int m = 0; m < MT; ++m) acc[m] = 0.f;
-            if (S > 1) {
+            bool store = s == S - 1;
+            if constexpr (XS) {
+                // The segments of a row group run on different workgroups: this
+                // segment's sums go to the workspace (agent-scope stores, complete
+                // before the count), and the last of the S segments to count in
+                // adds all of them in segment order, the order of the single-
+                // workgroup path below, so every output keeps its arithmetic.
+                const int rg = rg_base + rgl;
+                float* part = sl.gpart + (size_t)rg * S * (RW * MT) + grp * MT + (slot < MT ? slot : 0);
+                if (slot < MT)
+                    __hip_atomic_store(part + (size_t)s * (RW * MT), mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_s_waitcnt(0);
+                int before = 0;
+                if (lane == 0)
+                    before = __hip_atomic_fetch_add(sl.gcnt + rg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                before = __builtin_amdgcn_readfirstlane(before);
+                store = before == S - 1;
+                if (store) {
+                    float tot = 0.f;
+                    for (int q = 0; q < S; ++q) {
+                        const float v = __hip_atomic_load(part + (size_t)q * (RW * MT), __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+                        tot = q == 0 ? v : tot + v;
+                    }
+                    mine = tot;
+                }
+            } else if (S > 1) {
                 // add this segment after the ones before it, in segment order
                 // (the oldest unfinished item never waits, so this ends; the
                 // bound only guarantees that every wave exits)
@@ -975,7 +1005,7 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
                 }
                 __hip_atomic_store(prog, s + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
-            if (s == S - 1) {
+            if (store) {
                 if (F == QG_NVFP4) mine *= gscale;
                 if (slot < cnt && n < N) st_global_f32(y + yrow * ldy + n, mine);
             }

@@ -85,7 +85,10 @@ template <int F, int MT> constexpr bool direct_eager() {
 template <int F, int MT> constexpr int direct_xv() { return direct_eager<F, MT>() && MT < 16 ? 5 : 2; }
 
 // SEG false: one K segment and one phase (the launch guarantees it).
-template <int F, int MT, int SP, int PF, bool SEG>
+// XS: each workgroup takes one K segment (workgroup b: segment b % S, the
+// (b / S)-th share of the row groups), stages only that segment's activations
+// and adds its sums to the other segments' through a.xs_part / a.xs_cnt.
+template <int F, int MT, int SP, int PF, bool SEG, bool XS = false>
 __global__ __launch_bounds__((direct_waves<F, MT>() * 64)) void k_direct_gemm(const StreamArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8* smem = (lds_u8*)smem_generic;
@@ -94,8 +97,8 @@ __global__ __launch_bounds__((direct_waves<F, MT>() * 64)) void k_direct_gemm(co
     const int U = K / 64;
     const Segments sg = SEG ? Segments{a.seg_S > 0 ? a.seg_S : 1, a.seg_PS > 0 ? a.seg_PS : 1}
                             : Segments{1, (U + kDirectSlots - 1) / kDirectSlots};
-    const int nph = SEG && a.phases > 0 ? a.phases : 1;
-    const int seg_per_ph = (sg.S + nph - 1) / nph;
+    const int nph = XS ? 1 : SEG && a.phases > 0 ? a.phases : 1;
+    const int seg_per_ph = XS ? 1 : (sg.S + nph - 1) / nph;
     // LDS: one item counter per phase, then the activations of the longest
     // phase and their sums, then the segment sums
     const int KLmax = min(U, seg_per_ph * sg.PS * kDirectSlots) * 64;
@@ -105,16 +108,21 @@ __global__ __launch_bounds__((direct_waves<F, MT>() * 64)) void k_direct_gemm(co
     const int lane = threadIdx.x & 63;
     const int li = direct_out_slot(lane);
     const int groups = (a.N + RW - 1) / RW;
-    const int per = (groups + gridDim.x - 1) / gridDim.x;
-    const int g0 = blockIdx.x * per, g1 = min(groups, g0 + per);
+    // (XS: the grid is a whole number of workgroups per segment)
+    const int shares = XS ? (int)gridDim.x / sg.S : (int)gridDim.x;
+    const int share = XS ? (int)blockIdx.x / sg.S : (int)blockIdx.x;
+    const int per = (groups + shares - 1) / shares;
+    const int g0 = share * per, g1 = min(groups, g0 + per);
     const int rgs = g1 > g0 ? g1 - g0 : 0;
     // segment sums after the activations: progress[per], then total[per][4][MT]
     SegLds sl;
     sl.progress = (QG_LDS int*)(xl + direct_lds_bytes(F, MT, KLmax));
     sl.total = (lds_f32*)((lds_u8*)sl.progress + ((size_t)per * 4 + 15) / 16 * 16);
     sl.mtmax = MT;
+    sl.gpart = a.xs_part;
+    sl.gcnt = a.xs_cnt;
     if (threadIdx.x < kDirectCounterBytes / 4) counters[threadIdx.x] = 0;
-    if (SEG && sg.S > 1)
+    if (SEG && !XS && sg.S > 1)
         for (int i = threadIdx.x; i < per; i += blockDim.x) sl.progress[i] = 0;
     MatView mv = {a.w0, a.rb0, a.w1, a.rb1, a.gbytes};
     // activation and output rows of the pass: resolved once into registers for
@@ -140,7 +148,7 @@ __global__ __launch_bounds__((direct_waves<F, MT>() * 64)) void k_direct_gemm(co
     }
     for (int p = 0; p < nph; ++p) {
         Phase ph;
-        ph.s_lo = p * seg_per_ph;
+        ph.s_lo = XS ? (int)blockIdx.x % sg.S : p * seg_per_ph;
         ph.ns = min(sg.S, ph.s_lo + seg_per_ph) - ph.s_lo;
         ph.u0 = ph.s_lo * sg.PS * kDirectSlots;
         ph.KL = (min(U, (ph.s_lo + ph.ns) * sg.PS * kDirectSlots) - ph.u0) * 64;
@@ -159,8 +167,8 @@ __global__ __launch_bounds__((direct_waves<F, MT>() * 64)) void k_direct_gemm(co
         // the previous phase's activations, before any wave goes on
         __syncthreads();
         auto between = [&] { xst.commit(xl, xs, xp, a.ldx, a.M, ph.KL, row_of); };
-        wave_stream_direct<F, MT, SP, PF, SEG>(mv, a.N, K, xl, xs, next_item, g0, sg, ph, sl, a.y, a.ldy, yrow,
-                                               a.M, between);
+        wave_stream_direct<F, MT, SP, PF, SEG, XS>(mv, a.N, K, xl, xs, next_item, g0, sg, ph, sl, a.y, a.ldy, yrow,
+                                                   a.M, between);
     }
 }
 
@@ -232,6 +240,109 @@ static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
     if (lds > (size_t)kLdsBytes) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(direct_waves<F, MT>() * 64), lds, st, a);
     return hipGetLastError();
+}
+
+// Segment-per-workgroup launch (XS): taken where the plain launch would stage
+// the activations in several K phases (eight rows of K = 17,408), each phase
+// then giving a CU only its few row groups' items of one segment.  Workgroups
+// of one segment share the row groups in equal contiguous shares.
+constexpr int kXsegMT = 8;
+static int mt_for(int m);
+
+static size_t xseg_counter_bytes(int64_t groups) { return ((size_t)groups * 4 + 255) / 256 * 256; }
+
+template <int F, int MT>
+static bool xseg_plan(int64_t N, int K, Segments* sg_out, size_t* lds_out, long* grid_out, long* per_out) {
+    const Segments sg = direct_segments(F, N, K, num_cus());
+    if (sg.S < 2 || direct_phases(F, N, K, MT) < 2) return false;
+    constexpr int RW = kDirectRows;
+    const long groups = (N + RW - 1) / RW;
+    auto kern = k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF, true, true>;
+    size_t lds = direct_launch_lds(F, K, MT, sg, sg.S, 1);
+    long grid = 0, per = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+        int fit = 0;
+        if (kernel_residency((const void*)kern, lds, &fit, direct_waves<F, MT>() * 64) != hipSuccess) return false;
+        long shares = (long)num_cus() * fit / sg.S;
+        if (shares < 1) shares = 1;
+        if (shares > groups) shares = groups;
+        per = (groups + shares - 1) / shares;
+        grid = shares * sg.S;
+        lds = direct_launch_lds(F, K, MT, sg, sg.S, per);
+    }
+    if (lds > (size_t)kLdsBytes) return false;
+    *sg_out = sg;
+    *lds_out = lds;
+    *grid_out = grid;
+    *per_out = per;
+    return true;
+}
+
+__global__ void k_zero_counters(int32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+template <int F>
+static size_t xseg_bytes_fmt(int64_t N, int K) {
+    if constexpr (F == QG_Q4_K || F == QG_Q5_K || F == QG_Q6_K || F == QG_NVFP4 || F == QG_FP8) {
+        Segments sg;
+        size_t lds;
+        long grid, per;
+        if (!direct_eligible(F, K) || !xseg_plan<F, kXsegMT>(N, K, &sg, &lds, &grid, &per)) return 0;
+        const int64_t groups = (N + kDirectRows - 1) / kDirectRows;
+        return xseg_counter_bytes(groups) + (size_t)groups * sg.S * kDirectRows * kXsegMT * sizeof(float);
+    }
+    return 0;
+}
+
+size_t direct_xseg_bytes(int fmt, int64_t N, int K, int M) {
+    if (M < 2 || M > kMaxPassRows || mt_for(M) != kXsegMT) return 0;
+    switch (fmt) {
+        case QG_Q4_K: return xseg_bytes_fmt<QG_Q4_K>(N, K);
+        case QG_Q5_K: return xseg_bytes_fmt<QG_Q5_K>(N, K);
+        case QG_Q6_K: return xseg_bytes_fmt<QG_Q6_K>(N, K);
+        case QG_NVFP4: return xseg_bytes_fmt<QG_NVFP4>(N, K);
+        case QG_FP8: return xseg_bytes_fmt<QG_FP8>(N, K);
+        default: return 0;
+    }
+}
+
+template <int F>
+static hipError_t launch_xseg_fmt(StreamArgs a, void* ws, hipStream_t st) {
+    if constexpr (F == QG_Q4_K || F == QG_Q5_K || F == QG_Q6_K || F == QG_NVFP4 || F == QG_FP8) {
+        constexpr int MT = kXsegMT;
+        Segments sg;
+        size_t lds;
+        long grid, per;
+        if (!xseg_plan<F, MT>(a.N, a.K, &sg, &lds, &grid, &per)) return hipErrorInvalidValue;
+        const int64_t groups = (a.N + kDirectRows - 1) / kDirectRows;
+        a.seg_S = sg.S;
+        a.seg_PS = sg.PS;
+        a.phases = 1;
+        a.xs_cnt = (int32_t*)ws;
+        a.xs_part = (float*)((uint8_t*)ws + xseg_counter_bytes(groups));
+        // the counters start at zero in every call (a fill kernel, not a
+        // memset: the call may be captured into a graph)
+        hipLaunchKernelGGL(k_zero_counters, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, a.xs_cnt,
+                           (int)groups);
+        hipLaunchKernelGGL((k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF, true, true>),
+                           dim3((unsigned)grid), dim3(direct_waves<F, MT>() * 64), lds, st, a);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_direct_xseg(int fmt, StreamArgs a, void* ws, hipStream_t st) {
+    if (mt_for(a.M) != kXsegMT) return hipErrorInvalidValue;
+    switch (fmt) {
+        case QG_Q4_K: return launch_xseg_fmt<QG_Q4_K>(a, ws, st);
+        case QG_Q5_K: return launch_xseg_fmt<QG_Q5_K>(a, ws, st);
+        case QG_Q6_K: return launch_xseg_fmt<QG_Q6_K>(a, ws, st);
+        case QG_NVFP4: return launch_xseg_fmt<QG_NVFP4>(a, ws, st);
+        case QG_FP8: return launch_xseg_fmt<QG_FP8>(a, ws, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int F>

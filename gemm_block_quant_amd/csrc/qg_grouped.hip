@@ -387,7 +387,7 @@ __global__ __launch_bounds__(256) void k_grouped(const StreamArgs a, const int32
                 // workgroup's waves take its (row group, K segment) items round robin
                 const Segments sg{a.seg_S > 0 ? a.seg_S : 1, a.seg_PS > 0 ? a.seg_PS : 1};
                 const int rg0 = n_begin / RW, rgs = (n_end - n_begin + RW - 1) / RW;
-                SegLds sl;
+                SegLds sl{};
                 sl.progress = (QG_LDS int*)(xl + direct_lds_bytes(F, MTMAX, K));
                 sl.total = (lds_f32*)((lds_u8*)sl.progress + ((size_t)rgs * 4 + 15) / 16 * 16);
                 sl.mtmax = MT;

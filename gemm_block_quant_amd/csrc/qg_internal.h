@@ -28,9 +28,19 @@ struct StreamArgs {
     int xdiv;            // grouped product: row i of the call reads activation row i / xdiv (0 or 1: i)
     int xrow[kMaxPassRows];
     int yrow[kMaxPassRows];
+    // direct path with each workgroup on one K segment: per (row group,
+    // segment) sums and per-row-group counters (zero on entry); null otherwise
+    float* xs_part;
+    int32_t* xs_cnt;
 };
 
 hipError_t launch_stream_gemm(int fmt, StreamArgs a, hipStream_t st);
+// The direct path with each workgroup on one K segment, for passes whose
+// activations would otherwise be staged in several K phases: the workspace one
+// pass of M rows needs (0: the pass does not take it), and the launch (ws of
+// at least that many bytes, 16-byte aligned).
+size_t direct_xseg_bytes(int fmt, int64_t N, int K, int M);
+hipError_t launch_direct_xseg(int fmt, StreamArgs a, void* ws, hipStream_t st);
 int stream_rows_per_pass(int fmt, int64_t N, int K, int M);
 size_t stream_lds_bytes(int fmt, int K, int mt);
 

@@ -151,23 +151,29 @@ qg_status quant_gemv(const void* w, qg_format fmt, int64_t N, int64_t K, const u
 qg_status quant_gemm(const void* w, qg_format fmt, int64_t N, int64_t K, int64_t M, const uint16_t* x, float* y,
                      void* stream);
 
-/* Bytes of workspace quant_gemm_streamk needs for this call: per-tile
- * counters and two partial tiles per workgroup; 0 where the call does not
- * need one (then quant_gemm_streamk is quant_gemm and ignores the workspace).
- * Depends on the device's compute-unit count (the current device).  Host only;
- * 0 for invalid shapes. */
+/* Bytes of workspace quant_gemm_streamk needs for this call (0 where it
+ * needs none: quant_gemm_streamk is then quant_gemm and ignores the
+ * workspace).  Depends on the current device (its compute-unit count and
+ * the kernels' residency on it).  Host only; 0 for invalid shapes. */
 size_t quant_gemm_streamk_workspace_bytes(qg_format fmt, int64_t N, int64_t K, int64_t M);
 
 /* quant_gemm (same operation, arguments and limits: the product of the
- * passage cited there) with the matrix-core tiles scheduled evenly over the
- * GPU: where the tile count of a call with 32 <= M <= 2^21 rows is not a whole
- * number of rounds over the resident workgroups (two per compute unit), the
- * (tile, 64-value K step) iterations are dealt to them in equal contiguous
- * ranges, and a tile split between workgroups is finished by the last part to
- * arrive, which adds the parts' fp32 partial sums in a fixed order.  Results
- * are deterministic (one rounding order per shape and device) and within the
- * same error bound as quant_gemm, but not bit for bit quant_gemm's where a tile
- * is split.  Each weight block is still read once per tile.
+ * passage cited there) with a workspace that lets two schedules spread the
+ * work evenly over the GPU:
+ *  - 2..16 rows, where quant_gemm would stage the activations of 5..8 rows in
+ *    several K phases (rows of K = 17,408 cut into K segments, e.g. the
+ *    5120-row down projections): each workgroup takes one K segment and the
+ *    segments' fp32 sums meet in the workspace, added in segment order by
+ *    the last to finish.  The arithmetic is quant_gemm's: each row equals
+ *    the M = 1 result bit for bit.
+ *  - 32 <= M <= 2^21 rows, where the matrix-core tiles would leave resident
+ *    workgroups (two per compute unit) idle: the (tile, 64-value K step)
+ *    iterations are dealt to them in equal contiguous ranges, and a tile
+ *    split between workgroups is finished by the last part to arrive, which
+ *    adds the parts' fp32 partial sums in a fixed order.  Results are
+ *    deterministic and within quant_gemm's error bound, but not bit for bit
+ *    quant_gemm's where a tile is split.
+ * Each weight block is still read once per call (per tile of rows at M >= 32).
  * workspace: device scratch of at least
  * quant_gemm_streamk_workspace_bytes(fmt, N, K, M) bytes (16-byte aligned;
  * NULL allowed when that is 0), contents undefined between calls; calls
