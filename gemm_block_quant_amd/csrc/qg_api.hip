@@ -379,14 +379,19 @@ qg_status quant_gemm_streamk(const void* w, qg_format fmt, int64_t N, int64_t K,
     if (!workspace || workspace_bytes < need) return QG_EWORKSPACE;
     if (!aligned(workspace, 16)) return QG_EALIGN;
     if (M <= kMaxPassRows) {
+        // passes of up to 8 rows (every row keeps its arithmetic whatever the pass)
         StreamArgs a = stream_args(w, fmt, 1, 0, N, K);
         a.x = x;
         a.ldx = K;
         a.y = y;
         a.ldy = N;
-        a.M = (int)M;
-        for (int i = 0; i < kMaxPassRows; ++i) a.xrow[i] = a.yrow[i] = i < M ? i : 0;
-        return launch_direct_xseg(fmt, a, workspace, (hipStream_t)stream) == hipSuccess ? QG_OK : QG_EHIP;
+        for (int64_t m0 = 0; m0 < M; m0 += kXsegRows) {
+            const int cnt = (int)(M - m0 < kXsegRows ? M - m0 : kXsegRows);
+            a.M = cnt;
+            for (int i = 0; i < kMaxPassRows; ++i) a.xrow[i] = a.yrow[i] = (int)(m0 + (i < cnt ? i : 0));
+            if (launch_direct_xseg(fmt, a, workspace, (hipStream_t)stream) != hipSuccess) return QG_EHIP;
+        }
+        return QG_OK;
     }
     const StreamArgs a = stream_args(w, fmt, 1, 0, N, K);
     const hipError_t e = launch_mfma_kquant_streamk(fmt, a.w0, a.w1, a.gbytes, (int)N, (int)K, x, K, (int)M, y, N,

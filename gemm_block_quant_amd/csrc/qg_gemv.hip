@@ -246,8 +246,7 @@ static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
 // the activations in several K phases (eight rows of K = 17,408), each phase
 // then giving a CU only its few row groups' items of one segment.  Workgroups
 // of one segment share the row groups in equal contiguous shares.
-constexpr int kXsegMT = 8;
-static int mt_for(int m);
+constexpr int kXsegMT = kXsegRows;
 
 static size_t xseg_counter_bytes(int64_t groups) { return ((size_t)groups * 4 + 255) / 256 * 256; }
 
@@ -297,7 +296,8 @@ static size_t xseg_bytes_fmt(int64_t N, int K) {
 }
 
 size_t direct_xseg_bytes(int fmt, int64_t N, int K, int M) {
-    if (M < 2 || M > kMaxPassRows || mt_for(M) != kXsegMT) return 0;
+    // 5..16 rows, in passes of up to 8 (fewer rows fit one phase on the plain launch)
+    if (M < 5 || M > kMaxPassRows) return 0;
     switch (fmt) {
         case QG_Q4_K: return xseg_bytes_fmt<QG_Q4_K>(N, K);
         case QG_Q5_K: return xseg_bytes_fmt<QG_Q5_K>(N, K);
@@ -334,7 +334,7 @@ static hipError_t launch_xseg_fmt(StreamArgs a, void* ws, hipStream_t st) {
 }
 
 hipError_t launch_direct_xseg(int fmt, StreamArgs a, void* ws, hipStream_t st) {
-    if (mt_for(a.M) != kXsegMT) return hipErrorInvalidValue;
+    if (a.M < 1 || a.M > kXsegMT) return hipErrorInvalidValue;
     switch (fmt) {
         case QG_Q4_K: return launch_xseg_fmt<QG_Q4_K>(a, ws, st);
         case QG_Q5_K: return launch_xseg_fmt<QG_Q5_K>(a, ws, st);

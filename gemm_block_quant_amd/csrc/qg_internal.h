@@ -35,10 +35,11 @@ struct StreamArgs {
 };
 
 hipError_t launch_stream_gemm(int fmt, StreamArgs a, hipStream_t st);
-// The direct path with each workgroup on one K segment, for passes whose
-// activations would otherwise be staged in several K phases: the workspace one
-// pass of M rows needs (0: the pass does not take it), and the launch (ws of
-// at least that many bytes, 16-byte aligned).
+// The direct path with each workgroup on one K segment, for calls of 5..16
+// rows whose activations would otherwise be staged in several K phases: the
+// workspace it needs (0: not taken), and the launch of one pass of up to
+// kXsegRows rows (ws of at least that many bytes, 16-byte aligned).
+constexpr int kXsegRows = 8;
 size_t direct_xseg_bytes(int fmt, int64_t N, int K, int M);
 hipError_t launch_direct_xseg(int fmt, StreamArgs a, void* ws, hipStream_t st);
 int stream_rows_per_pass(int fmt, int64_t N, int K, int M);

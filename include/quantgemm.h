@@ -160,12 +160,12 @@ size_t quant_gemm_streamk_workspace_bytes(qg_format fmt, int64_t N, int64_t K, i
 /* quant_gemm (same operation, arguments and limits: the product of the
  * passage cited there) with a workspace that lets two schedules spread the
  * work evenly over the GPU:
- *  - 2..16 rows, where quant_gemm would stage the activations of 5..8 rows in
- *    several K phases (rows of K = 17,408 cut into K segments, e.g. the
- *    5120-row down projections): each workgroup takes one K segment and the
- *    segments' fp32 sums meet in the workspace, added in segment order by
- *    the last to finish.  The arithmetic is quant_gemm's: each row equals
- *    the M = 1 result bit for bit.
+ *  - 5..16 rows, where quant_gemm would stage the activations in several K
+ *    phases (rows of K = 17,408 cut into K segments, e.g. the 5120-row down
+ *    projections): passes of up to 8 rows in which each workgroup takes one
+ *    K segment and the segments' fp32 sums meet in the workspace, added in
+ *    segment order by the last to finish.  The arithmetic is quant_gemm's:
+ *    each row equals the M = 1 result bit for bit.
  *  - 32 <= M <= 2^21 rows, where the matrix-core tiles would leave resident
  *    workgroups (two per compute unit) idle: the (tile, 64-value K step)
  *    iterations are dealt to them in equal contiguous ranges, and a tile

@@ -21,12 +21,13 @@ DOWN = [(qg.Q6_K, 5120, 17408), (qg.NVFP4, 5120, 17408)]
 
 @pytest.mark.parametrize("fmt,N,K", DOWN)
 def test_xseg_rows_equal_decode_bitwise(fmt, N, K):
-    """Rows of 5..8-row calls equal the M = 1 result and quant_gemm's bit for bit."""
-    M = 8
+    """Rows of 5..16-row calls (16 and 9: passes of 8 rows, the last of 8 and of
+    1) equal the M = 1 result and quant_gemm's bit for bit."""
+    M = 16
     w, x = make_case(fmt, N, K, M, seed=700 + fmt)
     wd, xd = dev_bytes(w), dev_x(x)
     y1 = [qg.quant_gemv(wd, fmt, N, K, xd[m].contiguous()).cpu().numpy() for m in range(M)]
-    for m_rows in (8, 7, 5):
+    for m_rows in (8, 7, 5, 16, 11, 9):
         assert qg.quant_gemm_streamk_workspace_bytes(fmt, N, K, m_rows) > 0, m_rows
         xs = xd[:m_rows].contiguous()
         y = qg.quant_gemm_streamk(wd, fmt, N, K, m_rows, xs).cpu().numpy()
