@@ -520,7 +520,8 @@ template <> struct Direct<QG_Q6_K> {
     // 4-byte aligned loads shifted into place.  Measured: the LM head (whole
     // rows, 1 GB) 238 -> 210 us, its loads being address-unit bound; the
     // 5120-row down projections (K segments, latency-bound) 25.6 -> 28.0 us,
-    // so those keep the unaligned 16-byte loads.
+    // so those keep the unaligned 16-byte loads -- except with one segment
+    // per workgroup (8 rows), where they measured 34.4 -> 33.3 us.
     template <bool DW = false>
     __device__ static void load_at(uint32_t (&r)[REGS], const uint8_t* b0, const uint8_t*, const Offs& o) {
         const u32x4 qa = DW ? ld_global128_a2dw(b0 + o.a) : ld_global128_a2(b0 + o.a);
@@ -922,7 +923,7 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
             // no work: every lane loads the first bytes of the last row group
             // (one line; nothing streams for a dead slot)
             const typename D::Offs o = D::pick(live, D::pick(partial, cur_ol, cur_o), typename D::Offs{});
-            if constexpr (F == QG_Q6_K && !SEG)
+            if constexpr (F == QG_Q6_K && (!SEG || XS))
                 D::template load_at<true>(r[p], cur_b0 + (size_t)pass * D::PASS0, cur_b1 + (size_t)pass * D::PASS1, o);
             else
                 D::load_at(r[p], cur_b0 + (size_t)pass * D::PASS0, cur_b1 + (size_t)pass * D::PASS1, o);

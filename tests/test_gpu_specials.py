@@ -4,7 +4,8 @@ The dequantization export is bit-exact on special values (test_gpu_parity);
 here the same kind of values go through the decoders the products use: the
 register-direct streaming kernels (M = 1, 7, 8, 15, 16; K segments and K
 phases), the row-buffer kernels (Q8_0; NVFP4 with K % 64 = 32), 16-row passes
-(M = 17..31), the matrix-core tiles (M >= 32), the grouped product and the MoE
+(M = 17..31), the matrix-core tiles (M >= 32), the workspace entry's
+segment-per-workgroup and stream-K schedules, the grouped product and the MoE
 block.  Each case also carries zero-point rows (every code at the format's
 zero point, scales non-zero): their weights are exactly zero, so the band
 asks for y = 0 exactly there.  The pattern is the pages' kernel-versus-
@@ -63,6 +64,25 @@ def test_specials_and_zero_point_rows(fmt, N, K, M):
     else:
         y = qg.quant_gemm(wd, fmt, N, K, M, xd).cpu().numpy()
     _check(y, w, fmt, N, K, x, zrows, "specials fmt %d N %d K %d M %d" % (fmt, N, K, M))
+
+
+WORKSPACE_CASES = [
+    # one K segment per workgroup (quant_gemm_streamk, 5..16 rows on K-phased
+    # shapes): N = 300 cuts each row into 16 segments, N = 5120 into 3
+    (qg.Q6_K, 300, 17408, 8), (qg.NVFP4, 300, 17408, 8), (qg.Q4_K, 300, 17408, 16), (qg.FP8, 300, 17408, 8),
+    (qg.Q5_K, 300, 17408, 8), (qg.Q6_K, 5120, 17408, 8),
+    # stream-K tiles (260 tiles for 512 resident workgroups, 4 or 8 K steps)
+    (qg.Q4_K, 4160, 256, 512), (qg.Q6_K, 4160, 512, 512), (qg.NVFP4, 8320, 256, 512), (qg.FP8, 8320, 512, 512),
+]
+
+
+@pytest.mark.parametrize("fmt,N,K,M", WORKSPACE_CASES)
+def test_workspace_schedules_specials_and_zero_point_rows(fmt, N, K, M):
+    """The workspace entry's two schedules on the same edge values."""
+    assert qg.quant_gemm_streamk_workspace_bytes(fmt, N, K, M) > 0, "not on a workspace schedule"
+    w, x, zrows = special_case(fmt, N, K, M, seed=800 + fmt + M)
+    y = qg.quant_gemm_streamk(dev_bytes(w), fmt, N, K, M, dev_x(x)).cpu().numpy()
+    _check(y, w, fmt, N, K, x, zrows, "workspace specials fmt %d N %d K %d M %d" % (fmt, N, K, M))
 
 
 @pytest.mark.parametrize("fmt,K", [(qg.Q4_K, 1024), (qg.Q5_K, 1024), (qg.Q6_K, 1024), (qg.Q8_0, 1024),
