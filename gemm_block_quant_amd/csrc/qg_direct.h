@@ -516,18 +516,16 @@ template <> struct Direct<QG_Q6_K> {
     __device__ static Offs pick(bool c, const Offs& x, const Offs& y) {
         return Offs{c ? x.a : y.a, c ? x.b : y.b, c ? x.c : y.c, c ? x.d : y.d};
     }
-    // DW: the 16- and 8-byte fields (2-byte aligned: 210-byte blocks) read as
-    // 4-byte aligned loads shifted into place.  Measured: the LM head (whole
-    // rows, 1 GB) 238 -> 210 us, its loads being address-unit bound; the
-    // 5120-row down projections (K segments, latency-bound) 25.6 -> 28.0 us,
-    // so those keep the unaligned 16-byte loads -- except with one segment
-    // per workgroup (8 rows), where they measured 34.4 -> 33.3 us.
-    template <bool DW = false>
+    // The 16- and 8-byte fields (2-byte aligned: 210-byte blocks) are read as
+    // 4-byte aligned loads of the surrounding words shifted into place: the
+    // loads of the LM head (whole rows, 1 GB) were address-unit bound, 238 ->
+    // 210 us; the 5120-row down projections (K segments) 23.8 -> 22.3 us, and
+    // 34.4 -> 33.3 us at 8 rows with one segment per workgroup.
     __device__ static void load_at(uint32_t (&r)[REGS], const uint8_t* b0, const uint8_t*, const Offs& o) {
-        const u32x4 qa = DW ? ld_global128_a2dw(b0 + o.a) : ld_global128_a2(b0 + o.a);
-        const u32x4 qb = DW ? ld_global128_a2dw(b0 + o.a + 32) : ld_global128_a2(b0 + o.a + 32);
-        const u32x4 qh = DW ? ld_global128_a2dw(b0 + o.b) : ld_global128_a2(b0 + o.b);
-        const u32x2 sc = DW ? ld_global64_a2dw(b0 + o.c) : ld_global64_a2(b0 + o.c);
+        const u32x4 qa = ld_global128_a2dw(b0 + o.a);
+        const u32x4 qb = ld_global128_a2dw(b0 + o.a + 32);
+        const u32x4 qh = ld_global128_a2dw(b0 + o.b);
+        const u32x2 sc = ld_global64_a2dw(b0 + o.c);
         r[0] = qa.x; r[1] = qa.y; r[2] = qa.z; r[3] = qa.w;
         r[4] = qb.x; r[5] = qb.y; r[6] = qb.z; r[7] = qb.w;
         r[8] = qh.x; r[9] = qh.y; r[10] = qh.z; r[11] = qh.w;
@@ -923,10 +921,7 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
             // no work: every lane loads the first bytes of the last row group
             // (one line; nothing streams for a dead slot)
             const typename D::Offs o = D::pick(live, D::pick(partial, cur_ol, cur_o), typename D::Offs{});
-            if constexpr (F == QG_Q6_K && (!SEG || XS))
-                D::template load_at<true>(r[p], cur_b0 + (size_t)pass * D::PASS0, cur_b1 + (size_t)pass * D::PASS1, o);
-            else
-                D::load_at(r[p], cur_b0 + (size_t)pass * D::PASS0, cur_b1 + (size_t)pass * D::PASS1, o);
+            D::load_at(r[p], cur_b0 + (size_t)pass * D::PASS0, cur_b1 + (size_t)pass * D::PASS1, o);
         }
         slast = false;
         if (live) {
@@ -959,30 +954,13 @@ __device__ __forceinline__ void wave_stream_direct(const MatView& mv, int N, int
             for (int m = 0; m < MT; ++m) acc[m] = 0.f;
             bool store = s == S - 1;
             if constexpr (XS) {
-                // The segments of a row group run on different workgroups: this
-                // segment's sums go to the workspace (agent-scope stores, complete
-                // before the count), and the last of the S segments to count in
-                // adds all of them in segment order, the order of the single-
-                // workgroup path below, so every output keeps its arithmetic.
-                const int rg = rg_base + rgl;
-                float* part = sl.gpart + (size_t)rg * S * (RW * MT) + grp * MT + (slot < MT ? slot : 0);
-                if (slot < MT)
-                    __hip_atomic_store(part + (size_t)s * (RW * MT), mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __builtin_amdgcn_s_waitcnt(0);
-                int before = 0;
-                if (lane == 0)
-                    before = __hip_atomic_fetch_add(sl.gcnt + rg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                before = __builtin_amdgcn_readfirstlane(before);
-                store = before == S - 1;
-                if (store) {
-                    float tot = 0.f;
-                    for (int q = 0; q < S; ++q) {
-                        const float v = __hip_atomic_load(part + (size_t)q * (RW * MT), __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT);
-                        tot = q == 0 ? v : tot + v;
-                    }
-                    mine = tot;
-                }
+                // The segments of a row group run on different workgroups and a
+                // workgroup has one segment: this item's sums wait in LDS (one
+                // slot per row group) for the workgroup's end, where they go to
+                // the workspace together (no wait here on the wave's stores,
+                // which would drain its load ring)
+                store = false;
+                if (slot < MT) sl.total[(size_t)(rgl * RW + grp) * MT + slot] = mine;
             } else if (S > 1) {
                 // add this segment after the ones before it, in segment order
                 // (the oldest unfinished item never waits, so this ends; the

@@ -170,6 +170,45 @@ __global__ __launch_bounds__((direct_waves<F, MT>() * 64)) void k_direct_gemm(co
         wave_stream_direct<F, MT, SP, PF, SEG, XS>(mv, a.N, K, xl, xs, next_item, g0, sg, ph, sl, a.y, a.ldy, yrow,
                                                    a.M, between);
     }
+    if constexpr (XS) {
+        // This workgroup's segment sums (LDS, [row group][4][MT]) to the
+        // workspace, every store complete before any row group counts in; the
+        // last of a row group's S segments to count in adds the S sums in
+        // segment order -- the running sum of the single-workgroup path -- and
+        // writes the row group's outputs.  Nothing waits on another workgroup.
+        const int S = sg.S, s = (int)blockIdx.x % S;
+        constexpr int V = RW * MT;  // values per row group and segment
+        __syncthreads();
+        for (int i = threadIdx.x; i < rgs * V; i += blockDim.x)
+            __hip_atomic_store(a.xs_part + ((size_t)(g0 + i / V) * S + s) * V + i % V, sl.total[i],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        float gscale = 1.f;
+        if (F == QG_NVFP4) {
+            const uint8_t* gb = a.gbytes;
+            gscale = __builtin_bit_cast(float, (uint32_t)gb[0] | ((uint32_t)gb[1] << 8) | ((uint32_t)gb[2] << 16) |
+                                                   ((uint32_t)gb[3] << 24));
+        }
+        // row groups whose last segment this is, then one output per thread
+        QG_LDS int* last = sl.progress;
+        for (int t = threadIdx.x; t < rgs; t += blockDim.x)
+            last[t] = __hip_atomic_fetch_add(a.xs_cnt + g0 + t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+        __syncthreads();
+        for (int i = threadIdx.x; i < rgs * V; i += blockDim.x) {
+            const int t = i / V, e = i % V, gi = e / MT, m = e % MT;
+            const int n = RW * (g0 + t) + gi;
+            if (!last[t] || m >= a.M || n >= a.N) continue;
+            const float* part = a.xs_part + (size_t)(g0 + t) * S * V + e;
+            float tot = 0.f;
+            for (int q = 0; q < S; ++q) {
+                const float v = __hip_atomic_load(part + (size_t)q * V, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                tot = q == 0 ? v : tot + v;
+            }
+            if (F == QG_NVFP4) tot *= gscale;
+            st_global_f32(a.y + (int64_t)a.yrow[m] * a.ldy + n, tot);
+        }
+    }
 }
 
 // Persistent grid: as many 4-wave workgroups as can be resident at once (by
