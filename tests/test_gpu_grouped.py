@@ -161,10 +161,13 @@ def test_grouped_e1_is_dense_bitwise_on_tiles(fmt, K):
 
 
 @pytest.mark.parametrize("E,M,mode", [(20000, 300, "random"), (5000, 200, "random"), (7, 200, "invalid"),
-                                      (1, 129, "null"), (64, 129, "one"), (3, 4096, "random")])
+                                      (1, 129, "null"), (64, 129, "one"), (3, 4096, "random"),
+                                      # small calls: counting sort, and the one-wave bitonic sort (E > 16384)
+                                      (288, 128, "random"), (4, 31, "invalid"), (9, 1, "random"),
+                                      (20000, 100, "random")])
 def test_grouped_bucketing_paths(E, M, mode):
-    """Calls of more than 128 rows bucket by counting sort (E <= 16384) or by
-    a bitonic sort of (id, row) keys (larger E): every output against the
+    """Calls bucket by counting sort (E <= 16384) or by a bitonic sort of
+    (id, row) keys (larger E): every output against the
     oracle for many experts, all ids invalid, ids = NULL, one expert, and a
     large call over few experts."""
     fmt, N, K = qg.Q4_K, 8, 256
