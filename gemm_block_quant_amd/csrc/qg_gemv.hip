@@ -66,8 +66,14 @@ __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
 // change any row's arithmetic.
 // 16 waves per workgroup; 8 where the accumulators of many activation rows
 // need more registers than 4 waves per SIMD allow, and for one activation row
-// (two workgroups per CU then: measured 5 % faster on the Q6_K LM head and
-// down projection, 1-2 % on Q4_K and FP8, 1 % slower on NVFP4, which keeps 16).
+// (measured 5 % faster than 16 on the Q6_K LM head and down projection, 1-2 %
+// on Q4_K and FP8, 1 % slower on NVFP4, which keeps 16).  The registers then
+// decide how many workgroups share a CU: two for Q4_K and FP8 (88-96 VGPRs),
+// one for the Q6_K kernels (132-176).  More waves did not help: Q6_K capped
+// at 128 VGPRs to fit two workgroups spilled and ran 6 % (LM head) and 59 %
+// (down projection) slower, 4-wave workgroups (five waves per SIMD) 6 %
+// slower on Q4_K and 2 % on FP8, 8-wave NVFP4 workgroups 25 % slower on the
+// down projection.
 template <int F, int MT> constexpr int direct_waves() {
     return MT >= 16 || ((F == QG_Q6_K || F == QG_Q5_K) && MT >= 8) || (MT == 1 && F != QG_NVFP4) ? 8 : 16;
 }
