@@ -447,15 +447,18 @@ def clocks_under_load(p, seconds: float = 0.3):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: HBM-traffic figures taken from counters are only
-    reported while the kernels they were taken on are unchanged."""
+    """Hash of the HIP sources' code (comments and blank space left out): HBM-
+    traffic figures taken from counters are only reported while the kernels
+    they were taken on are unchanged."""
     import glob
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "gemm_block_quant_amd", "csrc", "*"))):
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, "r", encoding="utf-8") as fh:
+            code = re.sub(r"/\*.*?\*/|//[^\n]*", " ", fh.read(), flags=re.S)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
