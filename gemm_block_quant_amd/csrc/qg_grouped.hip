@@ -562,10 +562,12 @@ hipError_t launch_grouped(int fmt, const StreamArgs& a, const int32_t* ids, int6
         if (e != hipSuccess) return e;
     }
     // 3. rows per pass of the streaming kernel: room for the expected rows per
-    // distinct expert (twice the mean, at least 1, below the tiles' threshold),
-    // as LDS allows
+    // distinct expert (twice the mean, at least 4, below the tiles' threshold),
+    // as LDS allows.  At least 4: a decode batch (128 rows over 288 experts)
+    // has a few experts with 3 or 4 rows, each read twice in passes of 2 (the
+    // MoE layer 328 -> 318 us with passes of up to 4)
     int64_t want = 2 * ((M + S - 1) / S);
-    int mtmax = want <= 1 ? 1 : want <= 2 ? 2 : want <= 4 ? 4 : want <= 8 ? 8 : 16;
+    int mtmax = want <= 4 ? 4 : want <= 8 ? 8 : 16;
     while (mtmax > 1 && stream_lds_bytes(fmt, a.K, mtmax) > (size_t)kLdsBytes) mtmax >>= 1;
     switch (fmt) {
         case QG_Q8_0: return grouped_mt<QG_Q8_0>(a, mtmax, ws, E, M, estride0, estride1, tm, st);
