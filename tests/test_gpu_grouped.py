@@ -89,6 +89,27 @@ def test_grouped_moe_layer(N, K):
     assert_band(y, y_ref, bound, "moe N %d K %d" % (N, K))
 
 
+@pytest.mark.parametrize("fmt", [qg.Q4_K, qg.Q5_K, qg.Q6_K, qg.NVFP4, qg.FP8])
+def test_grouped_decode_batch_rows_bitwise(fmt):
+    """A decode-like batch (fewer rows than experts, a few experts with 3 to 5
+    rows, streamed in passes of up to 4 rows): every row equals the same row
+    computed alone (a one-row grouped call) bit for bit, and the band."""
+    E, N, K = 40, 256, 1024
+    sizes = [5, 4, 4, 3, 3, 2, 2, 2] + [1] * 15
+    ids = np.concatenate([np.full(c, e * 3 % E, np.int32) for e, c in enumerate(sizes)])
+    ids = ids[np.random.default_rng(31).permutation(len(ids))]
+    M = len(ids)
+    w = synth.weights(fmt, synth.rng(30, 0), E * N, K, E=E)
+    x = synth.x_bf16(synth.rng(30, 1), M, K)
+    wd, xd = dev_bytes(w), dev_x(x)
+    y = qg.quant_grouped_gemm(wd, fmt, E, N, K, M, xd, _ids_dev(ids)).cpu().numpy()
+    for i in range(M):
+        y1 = qg.quant_grouped_gemm(wd, fmt, E, N, K, 1, xd[i:i + 1].contiguous(), _ids_dev(ids[i:i + 1]))
+        assert same_bits(y[i], y1.cpu().numpy()[0]), i
+    y_ref, bound = oracle.gemm(fmt, w, N, K, x, E=E, ids=ids)
+    assert_band(y, y_ref, bound, "decode batch fmt %d" % fmt)
+
+
 def _slot_ids(sizes, E, seed, invalid=2):
     """ids giving expert e sizes[e] rows (shuffled), plus `invalid` rows with bad ids."""
     ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(sizes)] +
