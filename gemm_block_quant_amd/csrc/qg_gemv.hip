@@ -67,13 +67,13 @@ __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
 // 16 waves per workgroup; 8 where the accumulators of many activation rows
 // need more registers than 4 waves per SIMD allow, and for one activation row
 // (measured 5 % faster than 16 on the Q6_K LM head and down projection, 1-2 %
-// on Q4_K and FP8, 1 % slower on NVFP4, which keeps 16).  The registers then
-// decide how many workgroups share a CU: two for Q4_K and FP8 (88-96 VGPRs),
-// one for the Q6_K kernels (132-176).  More waves did not help: Q6_K capped
-// at 128 VGPRs to fit two workgroups spilled and ran 6 % (LM head) and 59 %
-// (down projection) slower, 4-wave workgroups (five waves per SIMD) 6 %
-// slower on Q4_K and 2 % on FP8, 8-wave NVFP4 workgroups 25 % slower on the
-// down projection.
+// on Q4_K and FP8, 1 % slower on NVFP4, which keeps 16).  At one row the
+// unsegmented launch then puts one 8-wave workgroup on each CU (see
+// dispatch_direct); the Q6_K kernels (132-176 VGPRs) fit only one anyway.
+// More waves per CU were slower: Q6_K capped at 128 VGPRs to fit two
+// workgroups spilled and ran 6 % (LM head) and 59 % (down projection)
+// slower, 4-wave workgroups at five waves per SIMD 6 % slower on Q4_K and 2 %
+// on FP8, 8-wave NVFP4 workgroups 25 % slower on the down projection.
 template <int F, int MT> constexpr int direct_waves() {
     return MT >= 16 || ((F == QG_Q6_K || F == QG_Q5_K) && MT >= 8) || (MT == 1 && F != QG_NVFP4) ? 8 : 16;
 }
@@ -268,8 +268,15 @@ static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
     // one ring slot for NVFP4's K-segmented rows at one activation row (2 %
     // faster on the 5120-row down projection; Q6_K 5 % slower that way)
     constexpr int PFS = F == QG_NVFP4 && MT == 1 ? 1 : DirectTune<F, MT>::PF;
-    auto kern = sg.S > 1 || a.phases > 1 ? k_direct_gemm<F, MT, DirectTune<F, MT>::SP, PFS, true>
-                                         : k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF, false>;
+    const bool seg = sg.S > 1 || a.phases > 1;
+    auto kern = seg ? k_direct_gemm<F, MT, DirectTune<F, MT>::SP, PFS, true>
+                    : k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF, false>;
+    // One activation row on the unsegmented kernel: one 8-wave workgroup per
+    // CU even where the registers fit two (measured 1.5-2 % faster on the
+    // Q4_K gate+up matrix, 2-5 % on Q5_K, 0.4 % on FP8; 4 or 12 waves per CU
+    // were slower).  The K-segmented kernels keep the residency their
+    // segment count is cut for.
+    const bool one_per_cu = !seg && MT == 1 && direct_waves<F, MT>() == 8;
     constexpr int RW = kDirectRows;
     const long groups = (a.N + RW - 1) / RW;
     // grid from the residency, then the LDS for the resulting share of row
@@ -280,7 +287,7 @@ static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
         int fit = 0;
         hipError_t e = kernel_residency((const void*)kern, lds, &fit, direct_waves<F, MT>() * 64);
         if (e != hipSuccess) return e;
-        grid = (long)num_cus() * fit;
+        grid = (long)num_cus() * (one_per_cu ? 1 : fit);
         if (grid > groups) grid = groups;
         const long per = (groups + grid - 1) / grid;
         lds = direct_launch_lds(F, a.K, MT, sg, a.phases, per);
