@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
 // need more registers than 4 waves per SIMD allow, and for one activation row
 // (measured 5 % faster than 16 on the Q6_K LM head and down projection, 1-2 %
 // on Q4_K and FP8, 1 % slower on NVFP4, which keeps 16).  At one row the
-// unsegmented launch then puts one 8-wave workgroup on each CU (see
+// unsegmented launch puts one workgroup of direct_row1_waves on each CU (see
 // dispatch_direct); the Q6_K kernels (132-176 VGPRs) fit only one anyway.
 // More waves per CU were slower: Q6_K capped at 128 VGPRs to fit two
 // workgroups spilled and ran 6 % (LM head) and 59 % (down projection)
@@ -76,6 +76,19 @@ __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
 // on FP8, 8-wave NVFP4 workgroups 25 % slower on the down projection.
 template <int F, int MT> constexpr int direct_waves() {
     return MT >= 16 || ((F == QG_Q6_K || F == QG_Q5_K) && MT >= 8) || (MT == 1 && F != QG_NVFP4) ? 8 : 16;
+}
+// Waves of the one workgroup per CU that the unsegmented kernel runs at one
+// activation row.  Swept per format (waves per CU, Q4_K gate+up matrix:
+// 6 22.3, 7 21.9, 8 21.3, 9 20.9, 10 20.7, 12 21.8 us; NVFP4 17408 rows: 7-9
+// 12.5, 10 12.3, 12-16 12.4-12.6 us; FP8 gate+up: 4 33.7, 5 32.1, 6 33.1,
+// 7 32.3, 8 36.2, 9-10 32.3 us, and its LM head 5-6 214 us against 237 at
+// 8; Q5_K and Q6_K keep 8: 6 to 10 were slower).
+template <int F> constexpr int direct_row1_waves() {
+    return F == QG_Q4_K || F == QG_NVFP4 ? 10 : F == QG_FP8 ? 5 : 8;
+}
+// The kernel's block-size bound covers both launches.
+template <int F, int MT> constexpr int direct_bound() {
+    return MT == 1 && direct_row1_waves<F>() > direct_waves<F, MT>() ? direct_row1_waves<F>() : direct_waves<F, MT>();
 }
 
 // Eager activation staging (see XStage) for the 8-wave Q5_K and Q6_K kernels,
@@ -95,7 +108,7 @@ template <int F, int MT> constexpr int direct_xv() { return direct_eager<F, MT>(
 // (b / S)-th share of the row groups), stages only that segment's activations
 // and adds its sums to the other segments' through a.xs_part / a.xs_cnt.
 template <int F, int MT, int SP, int PF, bool SEG, bool XS = false>
-__global__ __launch_bounds__((direct_waves<F, MT>() * 64)) void k_direct_gemm(const StreamArgs a) {
+__global__ __launch_bounds__((direct_bound<F, MT>() * 64)) void k_direct_gemm(const StreamArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8* smem = (lds_u8*)smem_generic;
     constexpr int RW = kDirectRows;
@@ -271,12 +284,12 @@ static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
     const bool seg = sg.S > 1 || a.phases > 1;
     auto kern = seg ? k_direct_gemm<F, MT, DirectTune<F, MT>::SP, PFS, true>
                     : k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF, false>;
-    // One activation row on the unsegmented kernel: one 8-wave workgroup per
-    // CU even where the registers fit two (measured 1.5-2 % faster on the
-    // Q4_K gate+up matrix, 2-5 % on Q5_K, 0.4 % on FP8; 4 or 12 waves per CU
-    // were slower).  The K-segmented kernels keep the residency their
-    // segment count is cut for.
-    const bool one_per_cu = !seg && MT == 1 && direct_waves<F, MT>() == 8;
+    // One activation row on the unsegmented kernel: one workgroup of
+    // direct_row1_waves per CU, even where the registers fit more (two 8-wave
+    // workgroups per CU measured 1.5-2 % slower on Q4_K, 2-5 % on Q5_K).  The
+    // K-segmented kernels keep the residency their segment count is cut for.
+    const bool one_per_cu = !seg && MT == 1;
+    const int waves = one_per_cu ? direct_row1_waves<F>() : direct_waves<F, MT>();
     constexpr int RW = kDirectRows;
     const long groups = (a.N + RW - 1) / RW;
     // grid from the residency, then the LDS for the resulting share of row
@@ -285,7 +298,7 @@ static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
     long grid = 0;
     for (int pass = 0; pass < 2; ++pass) {
         int fit = 0;
-        hipError_t e = kernel_residency((const void*)kern, lds, &fit, direct_waves<F, MT>() * 64);
+        hipError_t e = kernel_residency((const void*)kern, lds, &fit, waves * 64);
         if (e != hipSuccess) return e;
         grid = (long)num_cus() * (one_per_cu ? 1 : fit);
         if (grid > groups) grid = groups;
@@ -293,7 +306,7 @@ static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
         lds = direct_launch_lds(F, a.K, MT, sg, a.phases, per);
     }
     if (lds > (size_t)kLdsBytes) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(direct_waves<F, MT>() * 64), lds, st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(waves * 64), lds, st, a);
     return hipGetLastError();
 }
 
