@@ -82,13 +82,17 @@ template <int F, int MT> constexpr int direct_waves() {
 // 6 22.3, 7 21.9, 8 21.3, 9 20.9, 10 20.7, 12 21.8 us; NVFP4 17408 rows: 7-9
 // 12.5, 10 12.3, 12-16 12.4-12.6 us; FP8 gate+up: 4 33.7, 5 32.1, 6 33.1,
 // 7 32.3, 8 36.2, 9-10 32.3 us, and its LM head 5-6 214 us against 237 at
-// 8; Q5_K and Q6_K keep 8: 6 to 10 were slower).
+// 8; Q6_K LM head: 6 227, 8 201, 10 194.5, 12 195 us; Q5_K keeps 8: 6, 7, 9
+// and 10 were slower).
 template <int F> constexpr int direct_row1_waves() {
-    return F == QG_Q4_K || F == QG_NVFP4 ? 10 : F == QG_FP8 ? 5 : 8;
+    return F == QG_Q4_K || F == QG_NVFP4 || F == QG_Q6_K ? 10 : F == QG_FP8 ? 5 : 8;
 }
-// The kernel's block-size bound covers both launches.
-template <int F, int MT> constexpr int direct_bound() {
-    return MT == 1 && direct_row1_waves<F>() > direct_waves<F, MT>() ? direct_row1_waves<F>() : direct_waves<F, MT>();
+// The kernel's block-size bound covers the launches of its instantiation
+// (the segmented one keeps direct_waves: a larger bound would cap its
+// registers below what the Q6_K segmented kernel holds).
+template <int F, int MT, bool SEG> constexpr int direct_bound() {
+    return !SEG && MT == 1 && direct_row1_waves<F>() > direct_waves<F, MT>() ? direct_row1_waves<F>()
+                                                                             : direct_waves<F, MT>();
 }
 
 // Eager activation staging (see XStage) for the 8-wave Q5_K and Q6_K kernels,
@@ -108,7 +112,7 @@ template <int F, int MT> constexpr int direct_xv() { return direct_eager<F, MT>(
 // (b / S)-th share of the row groups), stages only that segment's activations
 // and adds its sums to the other segments' through a.xs_part / a.xs_cnt.
 template <int F, int MT, int SP, int PF, bool SEG, bool XS = false>
-__global__ __launch_bounds__((direct_bound<F, MT>() * 64)) void k_direct_gemm(const StreamArgs a) {
+__global__ __launch_bounds__((direct_bound<F, MT, SEG>() * 64)) void k_direct_gemm(const StreamArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8* smem = (lds_u8*)smem_generic;
     constexpr int RW = kDirectRows;
