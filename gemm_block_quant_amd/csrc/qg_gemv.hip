@@ -87,12 +87,19 @@ template <int F, int MT> constexpr int direct_waves() {
 template <int F> constexpr int direct_row1_waves() {
     return F == QG_Q4_K || F == QG_NVFP4 || F == QG_Q6_K ? 10 : F == QG_FP8 ? 5 : 8;
 }
+// Waves per workgroup of the unsegmented launch: the one-row table above;
+// 12 for the 8-row Q6_K kernel, whose 165 registers allow three waves per
+// SIMD (LM head at eight rows 256 -> 242 us; 10 waves 249 us); otherwise
+// direct_waves.
+template <int F, int MT> constexpr int direct_plain_waves() {
+    return MT == 1 ? direct_row1_waves<F>() : F == QG_Q6_K && MT == 8 ? 12 : direct_waves<F, MT>();
+}
 // The kernel's block-size bound covers the launches of its instantiation
 // (the segmented one keeps direct_waves: a larger bound would cap its
-// registers below what the Q6_K segmented kernel holds).
+// registers below what the Q6_K segmented kernels hold).
 template <int F, int MT, bool SEG> constexpr int direct_bound() {
-    return !SEG && MT == 1 && direct_row1_waves<F>() > direct_waves<F, MT>() ? direct_row1_waves<F>()
-                                                                             : direct_waves<F, MT>();
+    return !SEG && direct_plain_waves<F, MT>() > direct_waves<F, MT>() ? direct_plain_waves<F, MT>()
+                                                                       : direct_waves<F, MT>();
 }
 
 // Eager activation staging (see XStage) for the 8-wave Q5_K and Q6_K kernels,
@@ -293,7 +300,7 @@ static hipError_t dispatch_direct(StreamArgs a, hipStream_t st) {
     // workgroups per CU measured 1.5-2 % slower on Q4_K, 2-5 % on Q5_K).  The
     // K-segmented kernels keep the residency their segment count is cut for.
     const bool one_per_cu = !seg && MT == 1;
-    const int waves = one_per_cu ? direct_row1_waves<F>() : direct_waves<F, MT>();
+    const int waves = seg ? direct_waves<F, MT>() : direct_plain_waves<F, MT>();
     constexpr int RW = kDirectRows;
     const long groups = (a.N + RW - 1) / RW;
     // grid from the residency, then the LDS for the resulting share of row
