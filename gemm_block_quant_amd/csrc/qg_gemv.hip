@@ -88,11 +88,11 @@ template <int F> constexpr int direct_row1_waves() {
     return F == QG_Q4_K || F == QG_NVFP4 || F == QG_Q6_K ? 10 : F == QG_FP8 ? 5 : 8;
 }
 // Waves per workgroup of the unsegmented launch: the one-row table above;
-// 12 for the 8-row Q6_K kernel, whose 165 registers allow three waves per
-// SIMD (LM head at eight rows 256 -> 242 us; 10 waves 249 us); otherwise
-// direct_waves.
+// 12 for the 8-row Q6_K and Q5_K kernels, whose 146-165 registers allow
+// three waves per SIMD (Q6_K LM head at eight rows 256 -> 242 us, 10 waves
+// 249 us; Q5_K gate+up 41.2 -> 39.9 us); otherwise direct_waves.
 template <int F, int MT> constexpr int direct_plain_waves() {
-    return MT == 1 ? direct_row1_waves<F>() : F == QG_Q6_K && MT == 8 ? 12 : direct_waves<F, MT>();
+    return MT == 1 ? direct_row1_waves<F>() : (F == QG_Q6_K || F == QG_Q5_K) && MT == 8 ? 12 : direct_waves<F, MT>();
 }
 // The kernel's block-size bound covers the launches of its instantiation
 // (the segmented one keeps direct_waves: a larger bound would cap its
