@@ -83,7 +83,8 @@ template <int F, int MT> constexpr int direct_waves() {
 // 12.5, 10 12.3, 12-16 12.4-12.6 us; FP8 gate+up: 4 33.7, 5 32.1, 6 33.1,
 // 7 32.3, 8 36.2, 9-10 32.3 us, and its LM head 5-6 214 us against 237 at
 // 8; Q6_K LM head: 6 227, 8 201, 10 194.5, 12 195 us; Q5_K keeps 8: 6, 7, 9
-// and 10 were slower).
+// and 10 were slower; on another box 9 and 11 waves against 10: Q4_K +2 %
+// and +4 %, NVFP4 +2 % and +1 %, the Q6_K LM head +1.5 % and -0.6 %).
 template <int F> constexpr int direct_row1_waves() {
     return F == QG_Q4_K || F == QG_NVFP4 || F == QG_Q6_K ? 10 : F == QG_FP8 ? 5 : 8;
 }
