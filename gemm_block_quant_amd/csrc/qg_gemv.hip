@@ -110,6 +110,11 @@ template <int F, int MT, bool SEG> constexpr int direct_bound() {
 // on the Q6_K LM head and on Q5_K.  The other kernels keep two vectors and the waiting form
 // (eager staging measured 1 % slower on Q4_K, 8 % on FP8 and up to 17 % on
 // NVFP4 at eight rows).
+// Waves per workgroup of the segment-per-workgroup launch (XS, eight rows):
+// 12 for Q6_K, whose 165 registers allow three waves per SIMD (the down
+// projection at eight rows 31.0 -> 29.1 us); direct_waves otherwise.
+template <int F, int MT> constexpr int direct_xs_waves() { return F == QG_Q6_K ? 12 : direct_waves<F, MT>(); }
+
 template <int F, int MT> constexpr bool direct_eager() {
     return direct_waves<F, MT>() == 8 && (F == QG_Q5_K || F == QG_Q6_K);
 }
@@ -120,7 +125,8 @@ template <int F, int MT> constexpr int direct_xv() { return direct_eager<F, MT>(
 // (b / S)-th share of the row groups), stages only that segment's activations
 // and adds its sums to the other segments' through a.xs_part / a.xs_cnt.
 template <int F, int MT, int SP, int PF, bool SEG, bool XS = false>
-__global__ __launch_bounds__((direct_bound<F, MT, SEG>() * 64)) void k_direct_gemm(const StreamArgs a) {
+__global__ __launch_bounds__(((XS ? direct_xs_waves<F, MT>() : direct_bound<F, MT, SEG>()) * 64)) void k_direct_gemm(
+    const StreamArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_generic[];
     lds_u8* smem = (lds_u8*)smem_generic;
     constexpr int RW = kDirectRows;
@@ -341,7 +347,7 @@ static bool xseg_plan(int64_t N, int K, Segments* sg_out, size_t* lds_out, long*
     long grid = 0, per = 0;
     for (int pass = 0; pass < 2; ++pass) {
         int fit = 0;
-        if (kernel_residency((const void*)kern, lds, &fit, direct_waves<F, MT>() * 64) != hipSuccess) return false;
+        if (kernel_residency((const void*)kern, lds, &fit, direct_xs_waves<F, MT>() * 64) != hipSuccess) return false;
         long shares = (long)num_cus() * fit / sg.S;
         if (shares < 1) shares = 1;
         if (shares > groups) shares = groups;
@@ -407,7 +413,7 @@ static hipError_t launch_xseg_fmt(StreamArgs a, void* ws, hipStream_t st) {
         hipLaunchKernelGGL(k_zero_counters, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, a.xs_cnt,
                            (int)groups);
         hipLaunchKernelGGL((k_direct_gemm<F, MT, DirectTune<F, MT>::SP, DirectTune<F, MT>::PF, true, true>),
-                           dim3((unsigned)grid), dim3(direct_waves<F, MT>() * 64), lds, st, a);
+                           dim3((unsigned)grid), dim3(direct_xs_waves<F, MT>() * 64), lds, st, a);
         return hipGetLastError();
     }
     return hipErrorInvalidValue;
