@@ -59,7 +59,8 @@ __global__ __launch_bounds__(256) void k_stream_gemm(const StreamArgs a) {
                                       yrow, a.M, stage);
 }
 
-// Direct path: one 16-wave workgroup per CU.  Workgroup b owns an equal
+// Direct path: workgroups of the wave counts below, as many per CU as the
+// registers allow (one at one activation row).  Workgroup b owns an equal
 // contiguous share of the row groups; its waves take (row group, K segment)
 // items one at a time from a counter in LDS, so every CU finishes within
 // about one item of the others.  The order in which waves take items does not
